@@ -1,0 +1,451 @@
+"""Pins of the CPU oracle against mathematics that does not depend on it.
+
+The pages print no worked example and no reference values, so the oracle is
+pinned by closed forms (dense softmax attention, linear attention), by a
+token-level brute force written independently of the block factorisation, by
+finite differences and by a second autograd formulation, by invariants and by
+a hand-worked example.  Each pin is chosen so that a plausible slip in the
+oracle (a dropped term, a transposed operand, a wrong index or sign) breaks it.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+from sparse_linear_attention_mean_amd.inputs import make_inputs, random_bf16
+
+B = orc.BLOCK
+
+
+def _rand(shape, seed, std=1.0):
+    return orc.decode_bf16(random_bf16(shape, seed, std=std))
+
+
+def _random_mask(bsz, nh, t, seed, p=(0.3, 0.5, 0.2)):
+    rng = np.random.default_rng(seed)
+    return rng.choice(np.array([1, 0, -1], np.int8), size=(bsz, nh, t, t), p=p)
+
+
+# ---------------------------------------------------------------------------
+# token-level brute force (independent of block states and of the oracle)
+# ---------------------------------------------------------------------------
+def brute_force_head(q, k, v, w, mask, valid_len, scale):
+    n, d = q.shape
+    o_s = np.zeros((n, d))
+    y = np.zeros((n, d))
+    lse = np.full(n, -np.inf)
+    den = np.zeros(n)
+    fq = np.where(q > 0, q + 1, np.exp(np.minimum(q, 0)))
+    fk = np.where(k > 0, k + 1, np.exp(np.minimum(k, 0)))
+    for r in range(valid_len):
+        cls = np.array([mask[r // B, t // B] for t in range(valid_len)])
+        crit = np.flatnonzero(cls == 1)
+        marg = np.flatnonzero(cls == 0)
+        if crit.size:
+            s = np.array([scale * float(np.dot(q[r], k[t])) for t in crit])
+            e = np.exp(s - s.max())
+            o_s[r] = (e[:, None] * v[crit]).sum(0) / e.sum()
+            lse[r] = s.max() + math.log(e.sum())
+        if marg.size:
+            a = np.array([float(np.dot(fq[r], fk[t])) for t in marg])
+            den[r] = a.sum()
+            y[r] = (a[:, None] * v[marg]).sum(0) / a.sum()
+    o = o_s + y @ w.T
+    return o, o_s, y, lse, den
+
+
+def test_worked_example_two_blocks():
+    """Hand-worked case: two blocks, k_c = 1, k_n = 0.  Keys of a block are
+    identical, so the softmax over the critical block returns that block's
+    value row, and the linear branch over the other block returns the mean of
+    its value rows.  Query block 0 prefers key block 0, query block 1 key
+    block 1 (pooled scores by construction)."""
+    d = 4
+    n = 2 * B
+    q = np.zeros((n, d))
+    q[:B] = [1.0, 0.0, 0.0, 0.0]
+    q[B:] = [0.0, 1.0, 0.0, 0.0]
+    k = np.zeros((n, d))
+    k[:B] = [2.0, 0.0, 0.0, 0.0]
+    k[B:] = [0.0, 2.0, 0.0, 0.0]
+    v = np.zeros((n, d))
+    v[:B] = [1.0, 2.0, 3.0, 4.0]
+    v[B:] = np.arange(B * d, dtype=np.float64).reshape(B, d) / 100.0
+    w = np.diag([1.0, -1.0, 0.5, 2.0])
+    out = orc.forward(q[None, None], k[None, None], v[None, None], w, 0.5, 0.0)
+    mask = out["mask"][0, 0]
+    assert mask.tolist() == [[1, 0], [0, 1]]
+    o = out["o"][0, 0]
+    mean_v1 = v[B:].mean(0)
+    mean_v0 = v[:B].mean(0)
+    # query block 0: softmax over block 0 gives v0; linear over block 1
+    np.testing.assert_allclose(o[:B], np.broadcast_to(v[0] + w @ mean_v1, (B, d)), atol=1e-12)
+    # query block 1: softmax over block 1 is uniform (identical keys) -> mean
+    np.testing.assert_allclose(o[B:], np.broadcast_to(mean_v1 + w @ mean_v0, (B, d)), atol=1e-12)
+    # lse of a uniform softmax over 64 identical logits: logit + ln 64
+    scale = 0.5
+    np.testing.assert_allclose(out["lse"][0, 0, :B], scale * 2.0 + math.log(B), atol=1e-12)
+
+
+@pytest.mark.parametrize("valid_len", [256, 250])
+def test_all_critical_is_dense_softmax_attention(valid_len):
+    bsz, nh, n, d = 1, 2, 256, 16
+    q, k, v = (_rand((bsz, nh, n, d), s) for s in (1, 2, 3))
+    for x in (q, k, v):
+        x[:, :, valid_len:] = 0.0
+    w = _rand((d, d), 4, std=0.25)
+    scale = 1 / math.sqrt(d)
+    out = orc.forward(q, k, v, w, 1.0, 0.0, valid_len=valid_len)
+    assert (out["mask"] == 1).all()
+    assert np.all(out["den"] == 0) and np.all(out["y"] == 0)
+    np.testing.assert_array_equal(out["o"], out["o_sparse"])
+    # textbook dense attention over the valid keys
+    s = scale * np.einsum("bhnd,bhmd->bhnm", q, k)
+    s[..., valid_len:] = -np.inf
+    p = np.exp(s - s.max(-1, keepdims=True))
+    p /= p.sum(-1, keepdims=True)
+    ref = p @ v
+    ref[:, :, valid_len:] = 0.0
+    np.testing.assert_allclose(out["o"], ref, atol=1e-12, rtol=0)
+    # library routine: torch SDPA on the CPU in fp64
+    am = torch.zeros(n, n, dtype=torch.bool)
+    am[:, :valid_len] = True
+    ref_t = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v), attn_mask=am).numpy()
+    np.testing.assert_allclose(out["o"][:, :, :valid_len], ref_t[:, :, :valid_len], atol=1e-12)
+    lse_ref = np.log(np.exp(s[..., :valid_len]).sum(-1))
+    np.testing.assert_allclose(out["lse"][:, :, :valid_len], lse_ref[:, :, :valid_len], atol=1e-10)
+
+
+@pytest.mark.parametrize("valid_len", [256, 200])
+def test_all_marginal_is_linear_attention(valid_len):
+    bsz, nh, n, d = 2, 1, 256, 16
+    q, k, v = (_rand((bsz, nh, n, d), s) for s in (5, 6, 7))
+    for x in (q, k, v):
+        x[:, :, valid_len:] = 0.0
+    w = _rand((d, d), 8, std=0.25)
+    out = orc.forward(q, k, v, w, 0.0, 0.0, valid_len=valid_len)
+    assert (out["mask"] == 0).all()
+    assert np.all(out["o_sparse"] == 0) and np.all(np.isneginf(out["lse"]))
+    fq = np.where(q > 0, q + 1, np.exp(q))
+    fk = np.where(k > 0, k + 1, np.exp(k))[:, :, :valid_len]
+    kv = np.einsum("bhna,bhnc->bhac", fk, v[:, :, :valid_len])
+    ks = fk.sum(2)
+    num = np.einsum("bhna,bhac->bhnc", fq, kv)
+    den = np.einsum("bhna,bha->bhn", fq, ks)
+    y = num / den[..., None]
+    y[:, :, valid_len:] = 0.0
+    np.testing.assert_allclose(out["y"], y, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(out["o"], y @ w.T, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("valid_len,seed", [(192, 0), (170, 1), (129, 2)])
+def test_block_factorisation_matches_token_brute_force(valid_len, seed):
+    nh, n, d = 2, 192, 8
+    q, k, v = (_rand((1, nh, n, d), seed * 10 + s) for s in (1, 2, 3))
+    for x in (q, k, v):
+        x[:, :, valid_len:] = 0.0
+    w = _rand((d, d), seed * 10 + 4, std=0.3)
+    t = n // B
+    mask = _random_mask(1, nh, t, seed)
+    mask[0, 0, 0] = [0, 0, 0]       # a row with no critical block
+    mask[0, 1, 1] = [1, 1, -1]      # a row with no marginal block
+    scale = 0.37
+    out = orc.forward(q, k, v, w, 0.0, 0.0, valid_len=valid_len, scale=scale, mask=mask)
+    for h in range(nh):
+        o, o_s, y, lse, den = brute_force_head(q[0, h], k[0, h], v[0, h], w, mask[0, h],
+                                               valid_len, scale)
+        np.testing.assert_allclose(out["o"][0, h], o, atol=1e-12)
+        np.testing.assert_allclose(out["o_sparse"][0, h], o_s, atol=1e-12)
+        np.testing.assert_allclose(out["y"][0, h], y, atol=1e-12)
+        np.testing.assert_allclose(out["den"][0, h], den, rtol=1e-12)
+        np.testing.assert_allclose(out["lse"][0, h], lse, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# classifier
+# ---------------------------------------------------------------------------
+def _sorted_classify(row, k_c, k_n):
+    t = len(row)
+    order = sorted(range(t), key=lambda j: (-float(row[j]), j))
+    out = [0] * t
+    for j in order[:k_c]:
+        out[j] = 1
+    for j in order[t - k_n:] if k_n else []:
+        out[j] = -1
+    return out
+
+
+@pytest.mark.parametrize("kind", ["random", "constant", "integers", "signed_zeros"])
+def test_classifier_matches_sorted_brute_force(kind):
+    rng = np.random.default_rng(11)
+    t = 37
+    if kind == "random":
+        s = rng.standard_normal((20, t)).astype(np.float32)
+    elif kind == "constant":
+        s = np.full((4, t), 0.75, np.float32)
+    elif kind == "integers":
+        s = rng.integers(-3, 4, size=(20, t)).astype(np.float32)
+    else:
+        s = np.where(rng.random((20, t)) < 0.5, np.float32(0.0), np.float32(-0.0))
+        s[:, ::7] = 1.0
+    for k_c, k_n in [(0, 0), (3, 5), (1, 0), (0, 4), (10, 27), (37, 0), (0, 37)]:
+        got = orc.classify(s, k_c, k_n)
+        for r in range(s.shape[0]):
+            assert got[r].tolist() == _sorted_classify(s[r], k_c, k_n)
+            assert (got[r] == 1).sum() == k_c and (got[r] == -1).sum() == k_n
+            crit, marg, negl = (s[r][got[r] == c] for c in (1, 0, -1))
+            if crit.size and marg.size:
+                assert crit.min() >= marg.max()
+            if marg.size and negl.size:
+                assert marg.min() >= negl.max()
+
+
+def test_classifier_rejects_nan():
+    s = np.zeros(8, np.float32)
+    s[3] = np.nan
+    with pytest.raises(ValueError):
+        orc.classify_row(s, 2, 2)
+
+
+def test_block_counts_reading():
+    # (T, f_c, f_n) -> (k_c, k_n, k_m): critical rounds up, negligible down
+    table = {
+        (16, 0.125, 0.25): (2, 4, 10),
+        (128, 0.05, 0.10): (7, 12, 109),
+        (512, 0.05, 0.10): (26, 51, 435),
+        (1024, 0.02, 0.20): (21, 204, 799),
+        (256, 0.05, 0.10): (13, 25, 218),
+        (4, 1.0, 0.0): (4, 0, 0),
+        (4, 0.0, 0.0): (0, 0, 4),
+        (10, 0.5, 0.5): (5, 5, 0),
+    }
+    for (t, fc, fn), want in table.items():
+        assert orc.block_counts(t, fc, fn) == want
+    with pytest.raises(ValueError):
+        orc.block_counts(10, 0.61, 0.5)
+
+
+def test_pooled_means_on_linear_inputs():
+    n, d, valid_len = 256, 3, 230
+    c = np.array([1.0, -2.0, 0.5])
+    x = np.arange(n, dtype=np.float64)[:, None] * c[None, :]
+    m = orc.block_means(x, valid_len)
+    for i in range(4):
+        lo, hi = i * B, min((i + 1) * B, valid_len)
+        np.testing.assert_allclose(m[i], (lo + hi - 1) / 2.0 * c, rtol=1e-15)
+    # the score map is the fp32 rounding of scale * qbar . kbar
+    s = orc.compressed_scores(x, 2 * x, valid_len, 0.25)
+    ref = 0.25 * np.array([[(m[i] * 2 * m[j]).sum() for j in range(4)] for i in range(4)])
+    np.testing.assert_array_equal(s, ref.astype(np.float32))
+
+
+# ---------------------------------------------------------------------------
+# identities and invariants
+# ---------------------------------------------------------------------------
+def _problem(seed, n=192, d=8, nh=2, valid_len=None):
+    q, k, v = (_rand((1, nh, n, d), seed + s) for s in (1, 2, 3))
+    valid_len = n if valid_len is None else valid_len
+    for x in (q, k, v):
+        x[:, :, valid_len:] = 0.0
+    w = _rand((d, d), seed + 4, std=0.3)
+    mask = _random_mask(1, nh, n // B, seed)
+    return q, k, v, w, mask, valid_len
+
+
+def test_projection_identities_and_linearity_in_v():
+    q, k, v, w, mask, vl = _problem(20, valid_len=180)
+    d = w.shape[0]
+    base = orc.forward(q, k, v, w, 0, 0, valid_len=vl, mask=mask)
+    zero = orc.forward(q, k, v, np.zeros((d, d)), 0, 0, valid_len=vl, mask=mask)
+    np.testing.assert_allclose(zero["o"], base["o_sparse"], atol=1e-14)
+    ident = orc.forward(q, k, v, np.eye(d), 0, 0, valid_len=vl, mask=mask)
+    np.testing.assert_allclose(ident["o"], base["o_sparse"] + base["y"], atol=1e-13)
+    v2 = _rand(v.shape, 99)
+    v2[:, :, vl:] = 0.0
+    a = orc.forward(q, k, v2, w, 0, 0, valid_len=vl, mask=mask)
+    ab = orc.forward(q, k, v + 2.0 * v2, w, 0, 0, valid_len=vl, mask=mask)
+    np.testing.assert_allclose(ab["o"], base["o"] + 2.0 * a["o"], atol=1e-12)
+
+
+def test_outputs_are_convex_combinations_of_values():
+    q, k, v, w, mask, vl = _problem(30, valid_len=150)
+    out = orc.forward(q, k, v, w, 0, 0, valid_len=vl, mask=mask)
+    for h in range(q.shape[1]):
+        for r in range(vl):
+            i = r // B
+            cls = np.array([mask[0, h, i, t // B] for t in range(vl)])
+            for c, name in ((1, "o_sparse"), (0, "y")):
+                sel = np.flatnonzero(cls == c)
+                if sel.size == 0:
+                    continue
+                vals = v[0, h, sel]
+                o = out[name][0, h, r]
+                assert np.all(o <= vals.max(0) + 1e-12) and np.all(o >= vals.min(0) - 1e-12)
+
+
+def test_permutation_inside_blocks():
+    q, k, v, w, mask, vl = _problem(40)
+    rng = np.random.default_rng(3)
+    n = q.shape[2]
+    perm = np.concatenate([j * B + rng.permutation(B) for j in range(n // B)])
+    base = orc.forward(q, k, v, w, 0.34, 0.2, valid_len=vl)
+    pk = orc.forward(q, k[:, :, perm], v[:, :, perm], w, 0.34, 0.2, valid_len=vl)
+    np.testing.assert_array_equal(pk["mask"], base["mask"])
+    np.testing.assert_allclose(pk["o"], base["o"], atol=1e-12)
+    pq = orc.forward(q[:, :, perm], k, v, w, 0.34, 0.2, valid_len=vl)
+    np.testing.assert_array_equal(pq["mask"], base["mask"])
+    np.testing.assert_allclose(pq["o"], base["o"][:, :, perm], atol=1e-12)
+
+
+def test_padding_equals_ragged_unpadded_problem():
+    """A padded run equals a brute force on the unpadded problem whose last
+    block is ragged (its own pooling, scores and sorted classification)."""
+    nh, n, d, vl = 1, 256, 8, 200
+    q, k, v = (_rand((1, nh, n, d), 50 + s) for s in (1, 2, 3))
+    for x in (q, k, v):
+        x[:, :, vl:] = 0.0
+    w = _rand((d, d), 54, std=0.3)
+    fc, fn = 0.25, 0.25
+    out = orc.forward(q, k, v, w, fc, fn, valid_len=vl)
+    qs, ks, vs = q[0, 0, :vl], k[0, 0, :vl], v[0, 0, :vl]
+    t = math.ceil(vl / B)
+    qb = np.array([qs[i * B:(i + 1) * B].mean(0) for i in range(t)])
+    kb = np.array([ks[i * B:(i + 1) * B].mean(0) for i in range(t)])
+    scale = 1 / math.sqrt(d)
+    scores = (scale * qb @ kb.T).astype(np.float32)
+    k_c, k_n = math.ceil(fc * t), math.floor(fn * t)
+    mask = np.array([_sorted_classify(scores[i], k_c, k_n) for i in range(t)])
+    np.testing.assert_array_equal(out["mask"][0, 0], mask)
+    o, *_ = brute_force_head(qs, ks, vs, w, mask, vl, scale)
+    np.testing.assert_allclose(out["o"][0, 0, :vl], o, atol=1e-12)
+    assert np.all(out["o"][0, 0, vl:] == 0)
+
+
+# ---------------------------------------------------------------------------
+# backward
+# ---------------------------------------------------------------------------
+def _loss(q, k, v, w, do, mask, vl, scale):
+    out = orc.forward(q, k, v, w, 0, 0, valid_len=vl, scale=scale, mask=mask)
+    return float((out["o"] * do).sum())
+
+
+def test_backward_matches_central_differences():
+    nh, n, d, vl = 1, 128, 4, 120
+    q, k, v = (_rand((1, nh, n, d), 60 + s) for s in (1, 2, 3))
+    for x in (q, k, v):
+        x[:, :, vl:] = 0.0
+    w = _rand((d, d), 64, std=0.4)
+    do = _rand((1, nh, n, d), 65)
+    mask = np.array([[[[1, 0], [-1, 1]]]], np.int8)
+    scale = 0.6
+    g = orc.backward(q, k, v, w, do, mask, valid_len=vl, scale=scale)
+    eps = 1e-6
+    rng = np.random.default_rng(0)
+    for name, arr in (("dq", q), ("dk", k), ("dv", v)):
+        for _ in range(40):
+            idx = (0, 0, int(rng.integers(0, vl)), int(rng.integers(0, d)))
+            plus, minus = arr.copy(), arr.copy()
+            plus[idx] += eps
+            minus[idx] -= eps
+            args = {"q": q, "k": k, "v": v}
+            key = name[1]
+            fp = _loss(**{**args, key: plus}, w=w, do=do, mask=mask, vl=vl, scale=scale)
+            fm = _loss(**{**args, key: minus}, w=w, do=do, mask=mask, vl=vl, scale=scale)
+            assert abs((fp - fm) / (2 * eps) - g[name][idx]) < 1e-6 * max(1.0, abs(g[name][idx]))
+    for _ in range(10):
+        a, b = (int(x) for x in rng.integers(0, d, 2))
+        wp, wm = w.copy(), w.copy()
+        wp[a, b] += eps
+        wm[a, b] -= eps
+        fd = (_loss(q, k, v, wp, do, mask, vl, scale) - _loss(q, k, v, wm, do, mask, vl, scale)) / (2 * eps)
+        assert abs(fd - g["dw"][a, b]) < 1e-6 * max(1.0, abs(fd))
+    for name in ("dq", "dk", "dv"):
+        assert np.all(g[name][0, 0, vl:] == 0)
+
+
+def _torch_brute_force(q, k, v, w, mask, vl, scale):
+    """Differentiable token-level formulation (torch fp64 on the CPU)."""
+    n = q.shape[0]
+    tok = torch.arange(n)
+    cls = torch.from_numpy(mask.astype(np.int64))[tok[:, None] // B, tok[None, :] // B]
+    valid = (tok[:, None] < vl) & (tok[None, :] < vl)
+    crit = (cls == 1) & valid
+    marg = (cls == 0) & valid
+    s = scale * q @ k.T
+    s = torch.where(crit, s, torch.full_like(s, -torch.inf))
+    has = crit.any(1, keepdim=True)
+    p = torch.softmax(torch.where(has, s, torch.zeros_like(s)), dim=1) * crit
+    o_s = p @ v
+    fq = torch.nn.functional.elu(q) + 1
+    fk = torch.nn.functional.elu(k) + 1
+    a = (fq @ fk.T) * marg
+    den = a.sum(1, keepdim=True)
+    y = torch.where(den > 0, (a @ v) / torch.where(den > 0, den, torch.ones_like(den)),
+                    torch.zeros_like(o_s))
+    o = o_s + y @ w.T
+    return o * (tok[:, None] < vl)
+
+
+@pytest.mark.parametrize("vl", [192, 161])
+def test_backward_matches_autograd_of_token_formulation(vl):
+    nh, n, d = 2, 192, 8
+    q, k, v = (_rand((1, nh, n, d), 70 + s) for s in (1, 2, 3))
+    for x in (q, k, v):
+        x[:, :, vl:] = 0.0
+    w = _rand((d, d), 74, std=0.3)
+    do = _rand((1, nh, n, d), 75)
+    mask = _random_mask(1, nh, n // B, 5)
+    mask[0, 0, 2] = [0, 0, -1]
+    scale = 0.41
+    g = orc.backward(q, k, v, w, do, mask, valid_len=vl, scale=scale)
+    wt = torch.from_numpy(w).requires_grad_(True)
+    dw = torch.zeros_like(wt)
+    for h in range(nh):
+        qt, kt, vt = (torch.from_numpy(x[0, h].copy()).requires_grad_(True) for x in (q, k, v))
+        o = _torch_brute_force(qt, kt, vt, wt, mask[0, h], vl, scale)
+        gq, gk, gv, gw = torch.autograd.grad((o * torch.from_numpy(do[0, h])).sum(), (qt, kt, vt, wt))
+        np.testing.assert_allclose(g["dq"][0, h], gq.numpy(), atol=1e-11)
+        np.testing.assert_allclose(g["dk"][0, h], gk.numpy(), atol=1e-11)
+        np.testing.assert_allclose(g["dv"][0, h], gv.numpy(), atol=1e-11)
+        dw += gw
+    np.testing.assert_allclose(g["dw"], dw.numpy(), atol=1e-11)
+
+
+def test_backward_identities():
+    # all critical: the key gradient of a softmax sums to zero over the keys
+    q, k, v, w, _, vl = _problem(80, valid_len=170)
+    do = _rand(q.shape, 85)
+    t = q.shape[2] // B
+    crit = np.ones((1, q.shape[1], t, t), np.int8)
+    g = orc.backward(q, k, v, w, do, crit, valid_len=vl)
+    np.testing.assert_allclose(g["dk"].sum(axis=2), 0.0, atol=1e-11)
+    # dw = dO^T Y summed over heads and valid rows
+    mask = _random_mask(1, q.shape[1], t, 9)
+    f = orc.forward(q, k, v, w, 0, 0, valid_len=vl, mask=mask)
+    g = orc.backward(q, k, v, w, do, mask, valid_len=vl)
+    dov = do.copy()
+    dov[:, :, vl:] = 0
+    np.testing.assert_allclose(g["dw"], np.einsum("bhno,bhnc->oc", dov, f["y"]), atol=1e-11)
+    # all marginal: Y is invariant to scaling phi(q), so dphi(q) . phi(q) = 0
+    marg = np.zeros((1, q.shape[1], t, t), np.int8)
+    g = orc.backward(q, k, v, w, do, marg, valid_len=vl)
+    fq = orc.phi(q)
+    dphi = g["dq"] / orc.phi_prime(q)
+    np.testing.assert_allclose((dphi * fq).sum(-1)[:, :, :vl], 0.0, atol=1e-11)
+
+
+def test_generator_is_seeded_and_grid_structured():
+    a = make_inputs(1, 2, 512, 32, (2, 16, 16), 500, seed=3)
+    b = make_inputs(1, 2, 512, 32, (2, 16, 16), 500, seed=3)
+    for name in ("q", "k", "v", "w", "do"):
+        np.testing.assert_array_equal(a[name], b[name])
+    assert np.all(a["q"][:, :, 500:] == 0) and np.all(a["do"][:, :, 500:] == 0)
+    q = orc.decode_bf16(a["q"])[0, 0, :500]
+    k = orc.decode_bf16(a["k"])[0, 0, :500]
+    # nearby tokens score higher than far-away ones on average
+    near = np.mean([q[i] @ k[i + 1] for i in range(0, 400)])
+    far = np.mean([q[i] @ k[(i + 250) % 500] for i in range(0, 400)])
+    assert near > far
