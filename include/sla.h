@@ -1,0 +1,170 @@
+/*
+ * sla.h -- C ABI of the MI355X (gfx950) Sparse-Linear Attention library.
+ *
+ * The operation is the one described by "SLA: Beyond Sparsity in Diffusion
+ * Transformers via Fine-Tunable Sparse-Linear Attention" (English abstract and
+ * the method section of the paper card): for every query block the key blocks
+ * are classified as critical, marginal or negligible; critical blocks get exact
+ * O(N^2) softmax attention, marginal blocks O(N) linear attention, negligible
+ * blocks are skipped, and the two results are fused into one output; forward
+ * and backward are both provided.  The classifier ranks key blocks on a
+ * compressed (block mean-pooled) score map, the selection family described in
+ * the abstract of "Trainable Log-linear Sparse Attention for Efficient
+ * Diffusion Transformers".
+ *
+ * Concretely, per (batch b, head h), with blocks of 64 tokens, T = N / 64,
+ * L = valid_len, scale s, phi(x) = elu(x) + 1:
+ *
+ *   qbar_i, kbar_j   mean of the valid rows of Q / K block i / j
+ *   S_ij             s * qbar_i . kbar_j                       (fp32)
+ *   mask[i, j]       per row i, under the order (S_ij descending, j ascending):
+ *                    first k_c -> +1 critical, last k_n -> -1 negligible,
+ *                    the rest -> 0 marginal
+ *   O_s[r]           softmax attention of row r over the valid tokens of the
+ *                    critical blocks of its query block (0 when there are none)
+ *   h_j, z_j         sum over valid t in block j of phi(k_t) v_t^T and phi(k_t)
+ *   H_i, Z_i         sums of h_j, z_j over the marginal blocks of row i
+ *   Y[r]             (phi(q_r) H_i) / (phi(q_r) . Z_i)   (0 if the denominator is 0)
+ *   O[r]             O_s[r] + Y[r] W^T       (W: d x d, nn.Linear layout, no bias)
+ *   rows r >= L      output zero and receive zero gradients
+ *
+ * with k_c = ceil(frac_critical * T - 1e-6) and k_n = floor(frac_negligible *
+ * T + 1e-6) (computed in double from the float fractions).  The backward holds
+ * the mask fixed (no gradient through the classifier).
+ *
+ * Conventions for every entry point below:
+ *  - Tensors are contiguous, row-major.  Q, K, V, O, dO are bf16 [B, H, N, d]
+ *    ("BHND"); W is bf16 [d, d]; dQ, dK, dV, dW are fp32.  Device pointers must
+ *    be 16-byte aligned.
+ *  - The caller owns every buffer.  The library allocates no device memory,
+ *    copies nothing between host and device and never synchronises the stream.
+ *    Scratch memory is the caller's ``workspace`` (size from
+ *    sla_workspace_size); state handed from forward to backward is the
+ *    caller's ``saved`` buffer (size from sla_saved_size).
+ *  - SLA_OK means "all work enqueued on ``stream``" (a hipStream_t; NULL is the
+ *    default stream).  Arguments are validated on the host before anything is
+ *    enqueued; on an error nothing is enqueued and no output is touched, and
+ *    sla_last_error() returns a thread-local description.  A failed launch
+ *    returns SLA_ERR_DEVICE; device faults surface at the caller's next
+ *    synchronisation.
+ *  - Outputs are overwritten, never accumulated; inputs are never written.
+ *  - Calls are reentrant: no mutable global state.  Two calls that share a
+ *    workspace or saved buffer must be ordered on one stream.
+ */
+#ifndef SLA_H_
+#define SLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum sla_status {
+  SLA_OK = 0,
+  SLA_ERR_INVALID_ARGUMENT = 1, /* bad shape, fraction, pointer or alignment */
+  SLA_ERR_UNSUPPORTED = 2,      /* valid but not implemented (e.g. head_dim 96) */
+  SLA_ERR_WORKSPACE = 3,        /* workspace smaller than sla_workspace_size() */
+  SLA_ERR_DEVICE = 4            /* a HIP launch or runtime call failed */
+} sla_status;
+
+/* mask_mode */
+enum {
+  SLA_MASK_COMPUTE = 0, /* forward classifies and writes ``mask`` */
+  SLA_MASK_GIVEN = 1    /* forward reads a caller-supplied ``mask`` (fixed mask) */
+};
+
+/* Number of timed stages in stage_events (see sla_config). */
+#define SLA_NUM_STAGES 8
+enum {
+  SLA_STAGE_KV_STATE = 0,   /* forward: per-key-block states and pooled K   */
+  SLA_STAGE_POOL_Q = 1,     /* forward: pooled Q                            */
+  SLA_STAGE_CLASSIFY = 2,   /* forward: compressed scores + classification  */
+  SLA_STAGE_AGGREGATE = 3,  /* forward: marginal sums H_i, Z_i              */
+  SLA_STAGE_ATTENTION = 4,  /* forward: fused sparse + linear + projection  */
+  SLA_STAGE_BWD_PRE = 5,    /* backward: mask lists, D, dY, linear dQ, dH   */
+  SLA_STAGE_BWD_KV = 6,     /* backward: transposed sums, dK and dV         */
+  SLA_STAGE_BWD_Q = 7       /* backward: sparse dQ and dW                   */
+};
+
+typedef struct sla_config {
+  int32_t batch;           /* B >= 1 */
+  int32_t heads;           /* H >= 1 */
+  int32_t seq_len;         /* N: a positive multiple of 64 */
+  int32_t head_dim;        /* d: 64 or 128 */
+  int32_t valid_len;       /* L: 0 means N; otherwise N - 64 < L <= N */
+  int32_t block;           /* 64 (the only supported block size) */
+  float frac_critical;     /* in [0, 1] */
+  float frac_negligible;   /* in [0, 1]; k_c + k_n <= T */
+  float softmax_scale;     /* <= 0 means 1 / sqrt(d) */
+  int32_t mask_mode;       /* SLA_MASK_COMPUTE or SLA_MASK_GIVEN (forward only) */
+  /* Optional per-stage timing: NULL, or an array of 2 * SLA_NUM_STAGES
+     hipEvent_t created by the caller with timing enabled.  When set, the
+     library records event [2 s] before and [2 s + 1] after stage s on
+     ``stream`` (stages a call does not run are left unrecorded). */
+  void* stage_events;
+} sla_config;
+
+/* k_c, k_n, k_m (= T - k_c - k_n) for the configuration.  Host only. */
+sla_status sla_block_counts(const sla_config* cfg, int32_t* k_c, int32_t* k_n, int32_t* k_m);
+
+/* Bytes of scratch needed by sla_forward, sla_backward and sla_pool_scores
+   for this configuration (one size serves all three); 0 if cfg is invalid. */
+size_t sla_workspace_size(const sla_config* cfg);
+
+/* Bytes of the forward-to-backward state written by sla_forward; 0 if invalid.
+   Layout (each region 256-byte aligned, offsets from sla_saved_offsets):
+     lse  fp32 [B,H,N]     log-sum-exp of the critical logits (-inf if none)
+     den  fp32 [B,H,N]     linear denominator phi(q) . Z_i
+     y    bf16 [B,H,N,d]   normalised linear output Y (before W)
+     hst  bf16 [B,H,T,d,d] H_i stored transposed: element (c, a) at c*d + a
+     zst  fp32 [B,H,T,2,d] Z_i as two fp32 parts whose sum is Z_i           */
+size_t sla_saved_size(const sla_config* cfg);
+sla_status sla_saved_offsets(const sla_config* cfg, size_t* lse, size_t* den, size_t* y,
+                             size_t* hst, size_t* zst);
+
+/*
+ * Forward.  q, k, v: bf16 [B,H,N,d]; w: bf16 [d,d]; o: bf16 [B,H,N,d] (out).
+ * mask: int8 [B,H,T,T]; written when mask_mode is SLA_MASK_COMPUTE, read when
+ * SLA_MASK_GIVEN (values must be -1, 0 or +1; a given mask need not have the
+ * k_c / k_n row counts).  saved: sla_saved_size() bytes (out), needed by
+ * sla_backward.  With frac_critical = 1 and frac_negligible = 0 the call is
+ * plain dense softmax attention (linear branch empty).
+ */
+sla_status sla_forward(const sla_config* cfg, const void* q, const void* k, const void* v,
+                       const void* w, void* o, int8_t* mask, void* saved, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/*
+ * Backward of sum(dO * O) with the mask held fixed.  q, k, v, w, o, d_o as in
+ * the forward (o is the forward's output, d_o bf16 [B,H,N,d]); mask and saved
+ * exactly as the forward wrote or read them for the same inputs.  dq, dk, dv:
+ * fp32 [B,H,N,d] (out); dw: fp32 [d,d] (out), summed over batch, heads and
+ * valid rows.  Deterministic: no atomics in any reduction.
+ */
+sla_status sla_backward(const sla_config* cfg, const void* q, const void* k, const void* v,
+                        const void* w, const void* o, const void* d_o, const int8_t* mask,
+                        const void* saved, float* dq, float* dk, float* dv, float* dw,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* The compressed score map alone: scores fp32 [B,H,T,T] (out), bit-identical
+   to the map sla_forward classifies in SLA_MASK_COMPUTE mode. */
+sla_status sla_pool_scores(const sla_config* cfg, const void* q, const void* k, float* scores,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Classification alone: scores fp32 [B,H,T,T] (in, finite) -> mask int8
+   [B,H,T,T] (out), by the rule above.  Uses cfg's sizes and fractions only. */
+sla_status sla_classify(const sla_config* cfg, const float* scores, int8_t* mask, void* stream);
+
+/* Static description of a status code. */
+const char* sla_status_string(sla_status status);
+
+/* Thread-local description of the last failure in this thread ("" if none). */
+const char* sla_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SLA_H_ */

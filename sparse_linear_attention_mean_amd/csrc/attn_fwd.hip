@@ -1,0 +1,368 @@
+// Fused SLA forward for gfx950: one workgroup per (batch, head, query block).
+//
+// "SLA: Beyond Sparsity in Diffusion Transformers via Fine-Tunable
+// Sparse-Linear Attention" (English abstract; method section, steps 2-5):
+// exact softmax attention over the critical key blocks, linear attention over
+// the marginal ones, negligible blocks skipped, all in one kernel.  Per query
+// block i of 64 rows:
+//   sparse:  for every critical key block j: S = Q_i K_j^T (bf16 MFMA, fp32),
+//            online softmax in base 2 with lazy rescaling, O += P V_j (P in bf16)
+//   linear:  Y = (phi(Q_i) H_i) / (phi(Q_i) . Z_i)   (H_i, Z_i from the
+//            aggregation kernel; bf16 MFMA, fp32)
+//   fusion:  O = O_s + Y W^T
+//
+// Layout of the work: 4 waves, wave (kh, qh) owns key half kh (32 of the 64
+// keys of every critical block) and query half qh (32 rows).  Everything is
+// computed transposed (S^T = K Q^T, O^T = V^T P^T) with v_mfma_f32_32x32x16:
+// then the S^T result tile, converted to bf16, is directly the B operand of
+// the P V product (k index permuted identically in the V^T operand), each
+// lane owns one query row, and row statistics need a single xor-32 exchange.
+// K_j is staged to LDS row-major, V_j transposed; both double-buffered with
+// the next block's global loads in flight during the current block's MFMAs.
+// The two key halves are merged at the end like split-K partial softmaxes.
+#include "sla_device.h"
+#include "sla_internal.h"
+
+namespace sla {
+
+struct AttnArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* w;
+  const int32_t* lut;
+  const int32_t* lut_cnt;
+  const uint16_t* hst;
+  const float* zst;
+  uint16_t* o;
+  float* lse;
+  float* den;
+  uint16_t* y;
+  int N, L, T;
+  float scale_log2;
+};
+
+template <int D>
+struct AttnCfg {
+  static constexpr int KP = D + 8;                 // K row pitch in LDS (bf16)
+  static constexpr int VP = 72;                    // V^T row pitch (64 keys + pad)
+  static constexpr int kBuf = 64 * KP + D * VP;    // one K + V^T buffer (bf16 elements)
+  static constexpr int kLds = 2 * kBuf * 2;        // bytes, double buffered
+  static constexpr int KCH = D / 32;               // 16-byte K chunks per thread
+  static constexpr int TPT = D / 32;               // tokens per thread in the V transpose
+  static constexpr int NCT = D / 32;               // 32-row tiles of O^T per wave
+  static constexpr int NCC = D / 16;               // 16-wide k chunks over the head dim
+};
+
+template <int D, bool DENSE, bool LINEAR>
+__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs args) {
+  using C = AttnCfg<D>;
+  constexpr int KP = C::KP, VP = C::VP;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[C::kLds / 2];
+
+  const int T = args.T, N = args.N, L = args.L;
+  const uint32_t wg = xcd_remap(blockIdx.x, gridDim.x);
+  const int i = wg % T;
+  const long long bh = wg / T;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int kh = wave & 1, qh = wave >> 1;
+  const int n32 = lane & 31, hl = lane >> 5;
+  const size_t head = static_cast<size_t>(bh) * N * D;
+  const int row = i * kBlock + 32 * qh + n32;   // this lane's query row
+  const float sl2 = args.scale_log2;
+
+  // Q fragments: B operand of S^T = K Q^T (k = head-dim index 16 cc + 8 hl + s)
+  bf16x8 qf[C::NCC];
+  {
+    const uint16_t* qrow = args.q + head + static_cast<size_t>(row) * D + 8 * hl;
+#pragma unroll
+    for (int cc = 0; cc < C::NCC; ++cc) qf[cc] = as_bf16x8(ld16(qrow + 16 * cc));
+  }
+
+  const int cnt = DENSE ? T : args.lut_cnt[bh * T + i];
+  const int32_t* lrow = DENSE ? nullptr : args.lut + (bh * T + i) * static_cast<long long>(T);
+
+  // staging roles
+  u32x4 rk[C::KCH], rv[C::TPT];
+  const int vgrp = tid / (D / 8), vc8 = tid % (D / 8);
+#define SLA_LOAD_BLOCK(jblk)                                                                      \
+  do {                                                                                            \
+    const int j_ = (jblk);                                                                        \
+    const uint16_t* kb = args.k + head + static_cast<size_t>(j_) * kBlock * D;                    \
+    const uint16_t* vb = args.v + head + static_cast<size_t>(j_) * kBlock * D;                    \
+    _Pragma("unroll") for (int u = 0; u < C::KCH; ++u) {                                          \
+      const int c = tid + 256 * u;                                                                \
+      rk[u] = ld16(kb + static_cast<size_t>(c / (D / 8)) * D + 8 * (c % (D / 8)));                \
+    }                                                                                             \
+    _Pragma("unroll") for (int u = 0; u < C::TPT; ++u) {                                          \
+      const int t = C::TPT * vgrp + u;                                                            \
+      const u32x4 val = ld16(vb + static_cast<size_t>(t) * D + 8 * vc8);                          \
+      rv[u] = (j_ * kBlock + t < L) ? val : u32x4{0u, 0u, 0u, 0u};                                \
+    }                                                                                             \
+  } while (0)
+#define SLA_STORE_BLOCK(bufidx)                                                                   \
+  do {                                                                                            \
+    uint16_t* ks_ = smem + (bufidx) * C::kBuf;                                                    \
+    uint16_t* vt_ = ks_ + 64 * KP;                                                                \
+    _Pragma("unroll") for (int u = 0; u < C::KCH; ++u) {                                          \
+      const int c = tid + 256 * u;                                                                \
+      st16(ks_ + (c / (D / 8)) * KP + 8 * (c % (D / 8)), rk[u]);                                  \
+    }                                                                                             \
+    _Pragma("unroll") for (int s = 0; s < 8; ++s) {                                               \
+      uint16_t* dst = vt_ + (8 * vc8 + s) * VP + C::TPT * vgrp;                                   \
+      if constexpr (C::TPT == 4) {                                                                \
+        st8(dst, u32x2{u4_elem(rv[0], s) | (u4_elem(rv[1], s) << 16),                             \
+                       u4_elem(rv[2], s) | (u4_elem(rv[3], s) << 16)});                           \
+      } else {                                                                                    \
+        *reinterpret_cast<uint32_t*>(dst) = u4_elem(rv[0], s) | (u4_elem(rv[1], s) << 16);        \
+      }                                                                                           \
+    }                                                                                             \
+  } while (0)
+
+  f32x16 acc[C::NCT];
+#pragma unroll
+  for (int ct = 0; ct < C::NCT; ++ct) acc[ct] = f32x16{};
+  float m_run = -INFINITY;   // running max (log2 units) of this lane's query
+  float l_run = 0.f;         // partial row sum over this lane's keys
+
+  if (cnt > 0) {
+    SLA_LOAD_BLOCK(DENSE ? 0 : lrow[0]);
+    SLA_STORE_BLOCK(0);
+    __syncthreads();
+  }
+  for (int n = 0; n < cnt; ++n) {
+    const int j = DENSE ? n : lrow[n];
+    const int buf = n & 1;
+    if (n + 1 < cnt) SLA_LOAD_BLOCK(DENSE ? n + 1 : lrow[n + 1]);
+    const uint16_t* ks = smem + buf * C::kBuf;
+    const uint16_t* vt = ks + 64 * KP;
+
+    // S^T tile: 32 keys (32 kh ..) x 32 queries
+    f32x16 st = {};
+#pragma unroll
+    for (int cc = 0; cc < C::NCC; ++cc) {
+      st = mfma32(as_bf16x8(ld16(ks + (32 * kh + n32) * KP + 16 * cc + 8 * hl)), qf[cc], st);
+    }
+    const bool tail = (j + 1) * kBlock > L;
+    float mloc = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      float x = st[e] * sl2;
+      if (tail) {
+        const int key = j * kBlock + 32 * kh + 8 * (e / 4) + 4 * hl + (e % 4);
+        if (key >= L) x = -INFINITY;
+      }
+      st[e] = x;
+      mloc = fmaxf(mloc, x);
+    }
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+    const float m_new = fmaxf(m_run, mloc);
+    const bool need = m_new > m_run + 8.0f;
+    if (__any(need)) {
+      const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+      if (need) m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int ct = 0; ct < C::NCT; ++ct)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[ct][e] *= alpha;
+    }
+    const float mu = (m_run == -INFINITY) ? 0.f : m_run;
+    float p[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      p[e] = __builtin_amdgcn_exp2f(st[e] - mu);
+      l_run += p[e];
+    }
+    bf16x8 pb[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int s = 0; s < 8; ++s) pb[h][s] = static_cast<__bf16>(p[8 * h + s]);
+
+    // O^T += V^T P^T; k index of chunk h: keys 16 h + {4 hl .. 4 hl + 3, 8 + 4 hl .. 8 + 4 hl + 3}
+#pragma unroll
+    for (int ct = 0; ct < C::NCT; ++ct) {
+      const uint16_t* vrow = vt + (32 * ct + n32) * VP + 32 * kh + 4 * hl;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        acc[ct] = mfma32(as_bf16x8(ld8(vrow + 16 * h), ld8(vrow + 16 * h + 8)), pb[h], acc[ct]);
+      }
+    }
+    if (n + 1 < cnt) SLA_STORE_BLOCK(buf ^ 1);
+    __syncthreads();
+  }
+  l_run += __shfl_xor(l_run, 32);
+#undef SLA_LOAD_BLOCK
+#undef SLA_STORE_BLOCK
+
+  // ---- merge the two key halves (split-K style) ----
+  constexpr int NACC = C::NCT * 16;
+  float* ex = reinterpret_cast<float*>(smem);              // [qh][NACC][64]
+  float* exm = ex + 2 * NACC * 64;                         // [qh][64]
+  float* exl = exm + 128;                                  // [qh][64]
+  float* osl = exl + 128;                                  // [D][64] fp32 O_s^T (linear path)
+  __syncthreads();
+  if (kh == 1) {
+#pragma unroll
+    for (int ct = 0; ct < C::NCT; ++ct)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) ex[(qh * NACC + ct * 16 + e) * 64 + lane] = acc[ct][e];
+    exm[qh * 64 + lane] = m_run;
+    exl[qh * 64 + lane] = l_run;
+  }
+  __syncthreads();
+  const bool valid_row = row < L;
+  if (kh == 0) {
+    const float m2 = exm[qh * 64 + lane], l2 = exl[qh * 64 + lane];
+    const float ms = fmaxf(m_run, m2);
+    float a1 = 0.f, a2 = 0.f, inv = 0.f, lse_v = -INFINITY;
+    if (ms != -INFINITY) {
+      a1 = __builtin_amdgcn_exp2f(m_run - ms);
+      a2 = __builtin_amdgcn_exp2f(m2 - ms);
+      const float ls = a1 * l_run + a2 * l2;
+      if (ls > 0.f) {
+        inv = 1.0f / ls;
+        lse_v = (ms + __log2f(ls)) * kLn2;
+      }
+    }
+#pragma unroll
+    for (int ct = 0; ct < C::NCT; ++ct)
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        acc[ct][e] = (a1 * acc[ct][e] + a2 * ex[(qh * NACC + ct * 16 + e) * 64 + lane]) * inv;
+    if (hl == 0) args.lse[bh * N + row] = valid_row ? lse_v : -INFINITY;
+    if constexpr (!LINEAR) {
+      // O = O_s; lane holds O^T[c = 32 ct + 8 (e/4) + 4 hl + e%4][row]
+      uint16_t* orow = args.o + head + static_cast<size_t>(row) * D;
+#pragma unroll
+      for (int ct = 0; ct < C::NCT; ++ct)
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+          const int c = 32 * ct + 8 * e4 + 4 * hl;
+          u32x2 v = {0u, 0u};
+          if (valid_row)
+            v = u32x2{pack_bf16x2(acc[ct][4 * e4], acc[ct][4 * e4 + 1]),
+                      pack_bf16x2(acc[ct][4 * e4 + 2], acc[ct][4 * e4 + 3])};
+          st8(orow + c, v);
+        }
+    } else {
+#pragma unroll
+      for (int ct = 0; ct < C::NCT; ++ct)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int c = 32 * ct + 8 * (e / 4) + 4 * hl + (e % 4);
+          osl[c * 64 + 32 * qh + n32] = acc[ct][e];
+        }
+    }
+  }
+
+  if constexpr (!LINEAR) {
+    // no marginal blocks: Y = 0, den = 0
+    if (kh == 1) {
+      uint16_t* yrow = args.y + head + static_cast<size_t>(row) * D;
+#pragma unroll
+      for (int c = 8 * hl; c < D; c += 16) st16(yrow + c, u32x4{0u, 0u, 0u, 0u});
+      if (hl == 0) args.den[bh * N + row] = 0.f;
+    }
+    return;
+  } else {
+    // ---- linear branch: Y^T = (H_i^T phi(Q)^T) / den ----
+    const uint16_t* hrow = args.hst + (static_cast<size_t>(bh) * T + i) * D * D;
+    const float* zrow = args.zst + (static_cast<size_t>(bh) * T + i) * 2 * D;
+    bf16x8 pq[C::NCC];
+    float dpart = 0.f;
+#pragma unroll
+    for (int cc = 0; cc < C::NCC; ++cc) {
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const __bf16 r = static_cast<__bf16>(phi(static_cast<float>(qf[cc][s])));
+        pq[cc][s] = r;
+        const int a = 16 * cc + 8 * hl + s;
+        dpart += static_cast<float>(r) * (zrow[a] + zrow[D + a]);
+      }
+    }
+    const float den_v = dpart + __shfl_xor(dpart, 32);
+    const float rden = den_v > 0.f ? 1.0f / den_v : 0.f;
+    constexpr int NCL = D / 64;   // 32-row tiles of Y^T per wave (c half kh)
+    f32x16 lin[NCL];
+#pragma unroll
+    for (int ct = 0; ct < NCL; ++ct) {
+      lin[ct] = f32x16{};
+      const uint16_t* hr = hrow + static_cast<size_t>((D / 2) * kh + 32 * ct + n32) * D + 8 * hl;
+#pragma unroll
+      for (int cc = 0; cc < C::NCC; ++cc)
+        lin[ct] = mfma32(as_bf16x8(ld16(hr + 16 * cc)), pq[cc], lin[ct]);
+    }
+    if (kh == 0 && hl == 0) args.den[bh * N + row] = valid_row ? den_v : 0.f;
+    __syncthreads();   // exchange area free again: reuse it for Y (bf16 [64][D + 8])
+    constexpr int YP = D + 8;
+    uint16_t* ysl = smem;
+    uint16_t* yrow = args.y + head + static_cast<size_t>(row) * D;
+#pragma unroll
+    for (int ct = 0; ct < NCL; ++ct)
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const int c = (D / 2) * kh + 32 * ct + 8 * e4 + 4 * hl;
+        const uint32_t w0 = pack_bf16x2(lin[ct][4 * e4] * rden, lin[ct][4 * e4 + 1] * rden);
+        const uint32_t w1 = pack_bf16x2(lin[ct][4 * e4 + 2] * rden, lin[ct][4 * e4 + 3] * rden);
+        st8(ysl + (32 * qh + n32) * YP + c, u32x2{w0, w1});
+        st8(yrow + c, valid_row ? u32x2{w0, w1} : u32x2{0u, 0u});
+      }
+    __syncthreads();
+    // ---- fusion: O^T = O_s^T + W Y^T, wave (kh = o half, qh) ----
+    const uint16_t* ys = ysl + (32 * qh + n32) * YP + 8 * hl;
+    uint16_t* orow = args.o + head + static_cast<size_t>(row) * D;
+#pragma unroll
+    for (int ot = 0; ot < NCL; ++ot) {
+      const int obase = (D / 2) * kh + 32 * ot;
+      const uint16_t* wr = args.w + static_cast<size_t>(obase + n32) * D + 8 * hl;
+      f32x16 out = {};
+#pragma unroll
+      for (int cc = 0; cc < C::NCC; ++cc)
+        out = mfma32(as_bf16x8(ld16(wr + 16 * cc)), as_bf16x8(ld16(ys + 16 * cc)), out);
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const int o0 = obase + 8 * e4 + 4 * hl;
+        float r[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) r[x] = out[4 * e4 + x] + osl[(o0 + x) * 64 + 32 * qh + n32];
+        st8(orow + o0, valid_row ? u32x2{pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3])}
+                                 : u32x2{0u, 0u});
+      }
+    }
+  }
+}
+
+template <int D>
+static hipError_t launch_attn_t(const AttnArgs& a, unsigned grid, bool dense, bool linear,
+                                hipStream_t s) {
+  if (dense) {
+    if (linear)
+      hipLaunchKernelGGL((attn_fwd_kernel<D, true, true>), dim3(grid), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((attn_fwd_kernel<D, true, false>), dim3(grid), dim3(256), 0, s, a);
+  } else {
+    if (linear)
+      hipLaunchKernelGGL((attn_fwd_kernel<D, false, true>), dim3(grid), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((attn_fwd_kernel<D, false, false>), dim3(grid), dim3(256), 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_fwd(const Dims& d, const uint16_t* q, const uint16_t* k,
+                           const uint16_t* v, const uint16_t* w, const int32_t* lut,
+                           const int32_t* lut_cnt, bool dense, bool linear,
+                           const uint16_t* hst, const float* zst, uint16_t* o, float* lse,
+                           float* den, uint16_t* y, hipStream_t s) {
+  AttnArgs a{q, k, v, w, lut, lut_cnt, hst, zst, o, lse, den, y, d.N, d.L, d.T,
+             d.scale * kLog2e};
+  const unsigned grid = static_cast<unsigned>(d.BH() * d.T);
+  if (d.D == 128) return launch_attn_t<128>(a, grid, dense, linear, s);
+  return launch_attn_t<64>(a, grid, dense, linear, s);
+}
+
+}  // namespace sla

@@ -1,0 +1,437 @@
+// Forward preparation kernels for gfx950: per-key-block linear-attention
+// states, block mean pooling, the compressed score map and the three-way
+// classifier (critical / marginal / negligible per query block), plus the
+// list builders that turn a block mask into the index lists the attention
+// kernels consume.
+//
+// Method: "SLA: Beyond Sparsity in Diffusion Transformers via Fine-Tunable
+// Sparse-Linear Attention" (English abstract; method section, steps 1-4 of the
+// technical framework).  Classification ranks key blocks on a mean-pooled
+// (block-compressed) score map, the selection family described in the
+// abstract of "Trainable Log-linear Sparse Attention for Efficient Diffusion
+// Transformers".
+#include "sla_device.h"
+#include "sla_internal.h"
+
+namespace sla {
+
+// ---------------------------------------------------------------------------
+// kv_state: for key block j of head bh
+//   h_j^T[c][a] = sum_t v_t[c] * phi(k_t)[a],  z_j[a] = sum_t phi(k_t)[a],
+//   kbar_j[a]   = mean_t k_t[a]            (valid tokens t only)
+// h^T and z are written as bf16 in the "K-tiled" layout the aggregation GEMM
+// reads as its A operand: states[bh][j / 8][n][j % 8], n = c*D + a for h^T,
+// n = D*D + a for bf16(z), n = D*D + D + a for bf16(z - bf16(z)).  One
+// workgroup handles 8 consecutive key blocks so that every lane can write the
+// 8 block values of one state entry as a single 16-byte store.
+// phi(k) is rounded to bf16 once and the same rounded values feed h and z.
+// kbar sums column a in token order 0..63 in fp32, exactly as pool_kernel
+// does, so the pooled K is bit-identical in both paths.
+// ---------------------------------------------------------------------------
+template <int D>
+struct KvCfg {
+  static constexpr int kThreads = D * 4;               // one (row pair, 8 columns) unit each
+  static constexpr int kWaves = kThreads / 64;
+  static constexpr int kTiles = (D / 32) * (D / 32);   // 32x32 tiles of h^T
+  static constexpr int kTilesPerWave = kTiles / kWaves;
+  static constexpr int kPitch = 72;                    // LDS row pitch (bf16): 64 tokens + pad
+};
+
+template <int D>
+__global__ __launch_bounds__(KvCfg<D>::kThreads) void kv_state_kernel(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, float* __restrict__ kbar,
+    uint16_t* __restrict__ states, int N, int L, int T, int Tp) {
+  using C = KvCfg<D>;
+  constexpr int P = C::kPitch;
+  constexpr int TPW = C::kTilesPerWave;
+  constexpr int NB = D * D + 2 * D;
+  __shared__ uint16_t pk[D * P];   // phi(K)^T, bf16
+  __shared__ uint16_t vt[D * P];   // V^T
+  __shared__ uint16_t kt[D * P];   // K^T (raw, for the pooled mean)
+  __shared__ uint16_t zst[2 * D * 8];
+
+  const int groups = Tp / 8;
+  const uint32_t wg = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = wg / groups;
+  const int g = wg % groups;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int n32 = lane & 31;
+  const int hl = lane >> 5;
+
+  // staging unit of this thread: rows 2*rp, 2*rp+1; columns 8*c8 .. 8*c8+7
+  const int rp = tid / (D / 8);
+  const int c8 = tid % (D / 8);
+  const size_t head = static_cast<size_t>(bh) * N * D;
+
+  u32x4 rk[2], rv[2];
+  auto load = [&](int j) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int tok = j * kBlock + 2 * rp + r;
+      if (j < T && tok < L) {
+        const size_t off = head + static_cast<size_t>(tok) * D + 8 * c8;
+        rk[r] = ld16(k + off);
+        rv[r] = ld16(v + off);
+      } else {
+        rk[r] = u32x4{0u, 0u, 0u, 0u};
+        rv[r] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+
+  uint32_t stash[TPW][16][4];   // bf16 pairs of (block 2p, block 2p+1) per result entry
+  load(g * 8);
+#pragma unroll
+  for (int jj = 0; jj < 8; ++jj) {
+    const int j = g * 8 + jj;
+    // transpose the staged rows into LDS; invalid tokens are zero in K^T, V^T and phi(K)^T
+    {
+      const int tok0 = j * kBlock + 2 * rp;
+      const bool ok0 = j < T && tok0 < L, ok1 = j < T && tok0 + 1 < L;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const int row = (8 * c8 + s) * P + 2 * rp;
+        const uint32_t k0 = u4_elem(rk[0], s), k1 = u4_elem(rk[1], s);
+        *reinterpret_cast<uint32_t*>(&kt[row]) = k0 | (k1 << 16);
+        *reinterpret_cast<uint32_t*>(&vt[row]) = u4_elem(rv[0], s) | (u4_elem(rv[1], s) << 16);
+        const float p0 = ok0 ? phi(bf16_to_f32(static_cast<uint16_t>(k0))) : 0.f;
+        const float p1 = ok1 ? phi(bf16_to_f32(static_cast<uint16_t>(k1))) : 0.f;
+        *reinterpret_cast<uint32_t*>(&pk[row]) = pack_bf16x2(p0, p1);
+      }
+    }
+    __syncthreads();
+    if (jj < 7) load(j + 1);
+
+#pragma unroll
+    for (int x = 0; x < TPW; ++x) {
+      const int tt = wave * TPW + x;
+      const int ct = tt / (D / 32), at = tt % (D / 32);
+      f32x16 acc = {};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        acc = mfma32(as_bf16x8(ld16(&vt[(32 * ct + n32) * P + 16 * kk + 8 * hl])),
+                     as_bf16x8(ld16(&pk[(32 * at + n32) * P + 16 * kk + 8 * hl])), acc);
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const uint32_t hb = f32_to_bf16(acc[i]);
+        if (jj & 1)
+          stash[x][i][jj >> 1] |= hb << 16;
+        else
+          stash[x][i][jj >> 1] = hb;
+      }
+    }
+    if (tid < D) {
+      const int a = tid;
+      float zs = 0.f, ks = 0.f;
+      for (int t = 0; t < kBlock; ++t) {
+        zs += bf16_to_f32(pk[a * P + t]);
+        ks += bf16_to_f32(kt[a * P + t]);
+      }
+      const uint16_t zh = f32_to_bf16(zs);
+      zst[a * 8 + jj] = zh;
+      zst[(D + a) * 8 + jj] = f32_to_bf16(zs - bf16_to_f32(zh));
+      if (j < T) {
+        const int nvalid = min(kBlock, L - j * kBlock);
+        kbar[(static_cast<size_t>(bh) * T + j) * D + a] = ks / static_cast<float>(nvalid);
+      }
+    }
+    __syncthreads();
+  }
+
+  uint16_t* out = states + (static_cast<size_t>(bh) * groups + g) * NB * 8;
+#pragma unroll
+  for (int x = 0; x < TPW; ++x) {
+    const int tt = wave * TPW + x;
+    const int ct = tt / (D / 32), at = tt % (D / 32);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int c = 32 * ct + 8 * (i / 4) + 4 * hl + (i % 4);
+      const int a = 32 * at + n32;
+      st16(out + (static_cast<size_t>(c) * D + a) * 8,
+           u32x4{stash[x][i][0], stash[x][i][1], stash[x][i][2], stash[x][i][3]});
+    }
+  }
+  for (int e = tid; e < 2 * D; e += C::kThreads)
+    st16(out + (static_cast<size_t>(D) * D + e) * 8, ld16(&zst[e * 8]));
+}
+
+// ---------------------------------------------------------------------------
+// pool: xbar[bh][i][a] = mean of the valid rows of block i, summed in token
+// order 0..63 in fp32 (same order as kv_state_kernel's pooled K).
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void pool_kernel(const uint16_t* __restrict__ x,
+                                                   float* __restrict__ xbar, int N, int L,
+                                                   int T, long long rows) {
+  const long long r = static_cast<long long>(blockIdx.x) * (256 / D) + threadIdx.x / D;
+  const int a = threadIdx.x % D;
+  if (r >= rows) return;
+  const long long bh = r / T;
+  const int i = static_cast<int>(r % T);
+  const uint16_t* src = x + (static_cast<size_t>(bh) * N + static_cast<size_t>(i) * kBlock) * D + a;
+  const int nvalid = min(kBlock, L - i * kBlock);
+  float s = 0.f;
+  for (int t = 0; t < kBlock; ++t) {
+    const float val = t < nvalid ? bf16_to_f32(src[static_cast<size_t>(t) * D]) : 0.f;
+    s += val;
+  }
+  xbar[static_cast<size_t>(r) * D + a] = s / static_cast<float>(nvalid);
+}
+
+// ---------------------------------------------------------------------------
+// scores[bh][i][j] = (sum_a qbar_i[a] * kbar_j[a]) * scale: fp32 fused
+// multiply-adds in order a = 0..D-1, then one multiply by the scale.
+// 64 x 64 tile per workgroup.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void scores_kernel(const float* __restrict__ qbar,
+                                                     const float* __restrict__ kbar,
+                                                     float* __restrict__ scores, int T,
+                                                     float scale) {
+  __shared__ float qs[64][D + 1];
+  __shared__ float ks[64][D + 1];
+  const int tiles = (T + 63) / 64;
+  const int bh = blockIdx.z;
+  const int i0 = blockIdx.y * 64, j0 = blockIdx.x * 64;
+  (void)tiles;
+  const float* qh = qbar + static_cast<size_t>(bh) * T * D;
+  const float* kh = kbar + static_cast<size_t>(bh) * T * D;
+  for (int e = threadIdx.x; e < 64 * D; e += 256) {
+    const int r = e / D, a = e % D;
+    qs[r][a] = (i0 + r < T) ? qh[static_cast<size_t>(i0 + r) * D + a] : 0.f;
+    ks[r][a] = (j0 + r < T) ? kh[static_cast<size_t>(j0 + r) * D + a] : 0.f;
+  }
+  __syncthreads();
+  const int ty = threadIdx.x / 16, tx = threadIdx.x % 16;
+  float acc[4][4] = {};
+  for (int a = 0; a < D; ++a) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[r][c] = __fmaf_rn(qs[ty + 16 * r][a], ks[tx + 16 * c][a], acc[r][c]);
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int i = i0 + ty + 16 * r, j = j0 + tx + 16 * c;
+      if (i < T && j < T) scores[(static_cast<size_t>(bh) * T + i) * T + j] = __fmul_rn(acc[r][c], scale);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// classify: one workgroup per row (bh, i).  Keys are 64-bit: the fp32 score
+// mapped to an unsigned code that increases as the score decreases (-0 folded
+// onto +0), in the high word, and the block index in the low word; a bitonic
+// sort in LDS then gives the total order (score descending, index ascending).
+// Positions 0..k_c-1 are critical, T-k_n..T-1 negligible, the rest marginal.
+// Writes the mask row; optionally the ascending critical list and the
+// marginal bit row.  Rows i in [T, Tp) only clear their bit row.
+// ---------------------------------------------------------------------------
+constexpr int kMaxT = 2048;
+
+__device__ __forceinline__ uint32_t descending_code(float s) {
+  uint32_t u = __float_as_uint(s + 0.0f);   // -0 -> +0
+  const uint32_t asc = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ~asc;
+}
+
+__global__ __launch_bounds__(256) void classify_kernel(const float* __restrict__ scores,
+                                                       int8_t* __restrict__ mask,
+                                                       int32_t* __restrict__ lut,
+                                                       int32_t* __restrict__ lut_cnt,
+                                                       uint32_t* __restrict__ rbits, int T,
+                                                       int Tp, int kc, int kn) {
+  __shared__ unsigned long long keys[kMaxT];
+  __shared__ int8_t cls[kMaxT];
+  const int i = blockIdx.x;
+  const long long bh = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int words = Tp / 32;
+  if (i >= T) {
+    if (rbits)
+      for (int w = tid; w < words; w += 256) rbits[(bh * Tp + i) * words + w] = 0u;
+    return;
+  }
+  int n2 = 1;
+  while (n2 < T) n2 <<= 1;
+  const float* row = scores + (bh * T + i) * T;
+  for (int j = tid; j < n2; j += 256)
+    keys[j] = (j < T) ? ((static_cast<unsigned long long>(descending_code(row[j])) << 32) |
+                         static_cast<unsigned long long>(j))
+                      : ~0ull;
+  __syncthreads();
+  for (int size = 2; size <= n2; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int t = tid; t < n2 / 2; t += 256) {
+        const int lo = 2 * t - (t & (stride - 1));
+        const int hi = lo + stride;
+        const bool up = ((lo & size) == 0);
+        const unsigned long long a = keys[lo], b = keys[hi];
+        if ((a > b) == up) {
+          keys[lo] = b;
+          keys[hi] = a;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int p = tid; p < T; p += 256) {
+    const int j = static_cast<int>(keys[p] & 0xffffffffull);
+    cls[j] = p < kc ? 1 : (p >= T - kn ? -1 : 0);
+  }
+  __syncthreads();
+  int8_t* mrow = mask + (bh * T + i) * T;
+  for (int j = tid; j < T; j += 256) mrow[j] = cls[j];
+  if (tid < 64) {
+    const int lane = tid;
+    if (lut) {
+      int cnt = 0;
+      int32_t* lrow = lut + (bh * T + i) * T;
+      for (int base = 0; base < T; base += 64) {
+        const int j = base + lane;
+        const bool f = j < T && cls[j] == 1;
+        const unsigned long long bal = __ballot(f);
+        if (f) lrow[cnt + __popcll(bal & ((1ull << lane) - 1ull))] = j;
+        cnt += __popcll(bal);
+      }
+      if (lane == 0) lut_cnt[bh * T + i] = cnt;
+    }
+    if (rbits) {
+      uint32_t* brow = rbits + (bh * Tp + i) * words;
+      for (int base = 0; base < Tp; base += 64) {
+        const int j = base + lane;
+        const bool f = j < T && cls[j] == 0;
+        const unsigned long long bal = __ballot(f);
+        if (lane == 0) {
+          brow[base / 32] = static_cast<uint32_t>(bal);
+          if (base / 32 + 1 < words) brow[base / 32 + 1] = static_cast<uint32_t>(bal >> 32);
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// mask_lists: from a three-valued mask build, per row, the ascending list of
+// critical key blocks and the marginal bit row; per column, the ascending
+// list of query blocks for which the key block is critical and the marginal
+// bit column.  Values other than +1 and 0 count as negligible.
+// blockIdx.z = 0: rows, 1: columns.  Index Tp-T tail rows/columns clear bits.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void mask_lists_kernel(const int8_t* __restrict__ mask,
+                                                        int32_t* __restrict__ lut,
+                                                        int32_t* __restrict__ lut_cnt,
+                                                        uint32_t* __restrict__ rbits,
+                                                        int32_t* __restrict__ col,
+                                                        int32_t* __restrict__ col_cnt,
+                                                        uint32_t* __restrict__ cbits, int T,
+                                                        int Tp) {
+  const int x = blockIdx.x;
+  const long long bh = blockIdx.y;
+  const bool by_col = blockIdx.z == 1;
+  const int lane = threadIdx.x;
+  const int words = Tp / 32;
+  int32_t* list = by_col ? col : lut;
+  int32_t* cnts = by_col ? col_cnt : lut_cnt;
+  uint32_t* bits = by_col ? cbits : rbits;
+  if (list == nullptr) return;
+  uint32_t* brow = bits ? bits + (bh * Tp + x) * words : nullptr;
+  if (x >= T) {
+    if (brow)
+      for (int w = lane; w < words; w += 64) brow[w] = 0u;
+    return;
+  }
+  const int8_t* m = mask + bh * T * T;
+  int cnt = 0;
+  int32_t* lrow = list + (bh * T + x) * T;
+  for (int base = 0; base < Tp; base += 64) {
+    const int y = base + lane;
+    int8_t val = -1;
+    if (y < T) val = by_col ? m[static_cast<long long>(y) * T + x] : m[static_cast<long long>(x) * T + y];
+    const bool crit = y < T && val == 1;
+    const bool marg = y < T && val == 0;
+    const unsigned long long bc = __ballot(crit);
+    if (crit) lrow[cnt + __popcll(bc & ((1ull << lane) - 1ull))] = y;
+    cnt += __popcll(bc);
+    const unsigned long long bm = __ballot(marg);
+    if (brow && lane == 0) {
+      brow[base / 32] = static_cast<uint32_t>(bm);
+      if (base / 32 + 1 < words) brow[base / 32 + 1] = static_cast<uint32_t>(bm >> 32);
+    }
+  }
+  if (lane == 0) cnts[bh * T + x] = cnt;
+}
+
+__global__ void fill_mask_kernel(int8_t* __restrict__ mask, long long n, int8_t value) {
+  for (long long e = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x; e < n;
+       e += static_cast<long long>(gridDim.x) * blockDim.x)
+    mask[e] = value;
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+hipError_t launch_kv_state(const Dims& d, const uint16_t* k, const uint16_t* v, float* kbar,
+                           uint16_t* states, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(d.BH() * (d.Tp / 8)));
+  if (d.D == 128)
+    hipLaunchKernelGGL(kv_state_kernel<128>, grid, dim3(KvCfg<128>::kThreads), 0, s, k, v, kbar,
+                       states, d.N, d.L, d.T, d.Tp);
+  else
+    hipLaunchKernelGGL(kv_state_kernel<64>, grid, dim3(KvCfg<64>::kThreads), 0, s, k, v, kbar,
+                       states, d.N, d.L, d.T, d.Tp);
+  return hipGetLastError();
+}
+
+hipError_t launch_pool(const Dims& d, const uint16_t* x, float* xbar, hipStream_t s) {
+  const long long rows = d.BH() * d.T;
+  const int per = 256 / d.D;
+  const dim3 grid(static_cast<unsigned>((rows + per - 1) / per));
+  if (d.D == 128)
+    hipLaunchKernelGGL(pool_kernel<128>, grid, dim3(256), 0, s, x, xbar, d.N, d.L, d.T, rows);
+  else
+    hipLaunchKernelGGL(pool_kernel<64>, grid, dim3(256), 0, s, x, xbar, d.N, d.L, d.T, rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_scores(const Dims& d, const float* qbar, const float* kbar, float* scores,
+                         hipStream_t s) {
+  const int tiles = (d.T + 63) / 64;
+  const dim3 grid(tiles, tiles, static_cast<unsigned>(d.BH()));
+  if (d.D == 128)
+    hipLaunchKernelGGL(scores_kernel<128>, grid, dim3(256), 0, s, qbar, kbar, scores, d.T, d.scale);
+  else
+    hipLaunchKernelGGL(scores_kernel<64>, grid, dim3(256), 0, s, qbar, kbar, scores, d.T, d.scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_classify(const Dims& d, const float* scores, int8_t* mask, int32_t* lut,
+                           int32_t* lut_cnt, uint32_t* rbits, hipStream_t s) {
+  const int rows = rbits ? d.Tp : d.T;
+  hipLaunchKernelGGL(classify_kernel, dim3(rows, static_cast<unsigned>(d.BH())), dim3(256), 0, s,
+                     scores, mask, lut, lut_cnt, rbits, d.T, d.Tp, d.kc, d.kn);
+  return hipGetLastError();
+}
+
+hipError_t launch_mask_lists(const Dims& d, const int8_t* mask, int32_t* lut, int32_t* lut_cnt,
+                             uint32_t* rbits, int32_t* col, int32_t* col_cnt, uint32_t* cbits,
+                             hipStream_t s) {
+  const unsigned z = col ? 2u : 1u;
+  hipLaunchKernelGGL(mask_lists_kernel, dim3(d.Tp, static_cast<unsigned>(d.BH()), z), dim3(64), 0,
+                     s, mask, lut, lut_cnt, rbits, col, col_cnt, cbits, d.T, d.Tp);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_mask(const Dims& d, int8_t* mask, int8_t value, hipStream_t s) {
+  const long long n = d.BH() * d.T * d.T;
+  const long long blocks = std::min<long long>((n + 255) / 256, 4096);
+  hipLaunchKernelGGL(fill_mask_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, mask,
+                     n, value);
+  return hipGetLastError();
+}
+
+}  // namespace sla

@@ -1,0 +1,363 @@
+// Host side of the C ABI declared in include/sla.h: argument validation,
+// block counts, workspace / saved-state layout and launch sequencing.
+// Nothing here allocates device memory or synchronises the caller's stream.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "sla_device.h"
+#include "sla_internal.h"
+
+namespace sla {
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+sla_status fail(sla_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+// Counts per row: critical rounds up, negligible rounds down (1e-6 slack for
+// float noise), both in double from the float fractions.
+sla_status counts(int T, float fc, float fn, int* kc, int* kn) {
+  if (!(fc >= 0.f && fc <= 1.f) || !(fn >= 0.f && fn <= 1.f))
+    return fail(SLA_ERR_INVALID_ARGUMENT, "fractions must lie in [0, 1] (got %g, %g)", fc, fn);
+  long long c = static_cast<long long>(ceil(static_cast<double>(fc) * T - 1e-6));
+  long long n = static_cast<long long>(floor(static_cast<double>(fn) * T + 1e-6));
+  c = std::max(0LL, std::min<long long>(c, T));
+  n = std::max(0LL, std::min<long long>(n, T));
+  if (c + n > T)
+    return fail(SLA_ERR_INVALID_ARGUMENT, "critical (%lld) + negligible (%lld) blocks exceed %d", c,
+                n, T);
+  *kc = static_cast<int>(c);
+  *kn = static_cast<int>(n);
+  return SLA_OK;
+}
+
+sla_status make_dims(const sla_config* cfg, Dims* d) {
+  if (cfg == nullptr) return fail(SLA_ERR_INVALID_ARGUMENT, "config is NULL");
+  if (cfg->batch < 1 || cfg->heads < 1)
+    return fail(SLA_ERR_INVALID_ARGUMENT, "batch and heads must be >= 1");
+  if (cfg->block != kBlock) return fail(SLA_ERR_UNSUPPORTED, "block must be 64 (got %d)", cfg->block);
+  if (cfg->seq_len < kBlock || cfg->seq_len % kBlock != 0)
+    return fail(SLA_ERR_INVALID_ARGUMENT, "seq_len must be a positive multiple of 64 (got %d)",
+                cfg->seq_len);
+  if (cfg->head_dim != 64 && cfg->head_dim != 128)
+    return fail(SLA_ERR_UNSUPPORTED, "head_dim must be 64 or 128 (got %d)", cfg->head_dim);
+  const int N = cfg->seq_len;
+  const int L = cfg->valid_len == 0 ? N : cfg->valid_len;
+  if (L <= N - kBlock || L > N)
+    return fail(SLA_ERR_INVALID_ARGUMENT, "valid_len must satisfy seq_len-64 < valid_len <= seq_len");
+  const int T = N / kBlock;
+  if (T > 2048) return fail(SLA_ERR_UNSUPPORTED, "seq_len above 131072 is not supported");
+  if (cfg->mask_mode != SLA_MASK_COMPUTE && cfg->mask_mode != SLA_MASK_GIVEN)
+    return fail(SLA_ERR_INVALID_ARGUMENT, "unknown mask_mode %d", cfg->mask_mode);
+  if (!isfinite(cfg->softmax_scale))
+    return fail(SLA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite");
+  const long long elems = static_cast<long long>(cfg->batch) * cfg->heads * N;
+  if (elems > (1LL << 40)) return fail(SLA_ERR_UNSUPPORTED, "problem too large");
+  int kc = 0, kn = 0;
+  sla_status st = counts(T, cfg->frac_critical, cfg->frac_negligible, &kc, &kn);
+  if (st != SLA_OK) return st;
+  d->B = cfg->batch;
+  d->H = cfg->heads;
+  d->N = N;
+  d->D = cfg->head_dim;
+  d->L = L;
+  d->T = T;
+  d->Tp = (T + 31) / 32 * 32;
+  d->NB = d->D * d->D + 2 * d->D;
+  d->kc = kc;
+  d->kn = kn;
+  d->km = T - kc - kn;
+  d->scale = cfg->softmax_scale > 0.f ? cfg->softmax_scale : 1.0f / sqrtf(static_cast<float>(d->D));
+  d->mask_mode = cfg->mask_mode;
+  return SLA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+sla_status check_ptr(const void* p, const char* name) {
+  if (p == nullptr) return fail(SLA_ERR_INVALID_ARGUMENT, "%s is NULL", name);
+  if (!aligned16(p)) return fail(SLA_ERR_INVALID_ARGUMENT, "%s is not 16-byte aligned", name);
+  return SLA_OK;
+}
+
+#define SLA_CHECK(expr)              \
+  do {                               \
+    sla_status st_ = (expr);         \
+    if (st_ != SLA_OK) return st_;   \
+  } while (0)
+
+sla_status launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(SLA_ERR_DEVICE, "%s: %s", what, hipGetErrorString(e));
+  return SLA_OK;
+}
+
+// Optional per-stage event recording.
+struct Stages {
+  hipEvent_t* ev;
+  hipStream_t s;
+  sla_status begin(int stage) {
+    if (ev && hipEventRecord(ev[2 * stage], s) != hipSuccess)
+      return fail(SLA_ERR_DEVICE, "hipEventRecord failed");
+    return SLA_OK;
+  }
+  sla_status end(int stage) {
+    if (ev && hipEventRecord(ev[2 * stage + 1], s) != hipSuccess)
+      return fail(SLA_ERR_DEVICE, "hipEventRecord failed");
+    return SLA_OK;
+  }
+};
+
+}  // namespace
+
+WorkspaceLayout workspace_layout(const Dims& d) {
+  WorkspaceLayout w{};
+  const size_t BH = static_cast<size_t>(d.BH());
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  w.qbar = take(BH * d.T * d.D * 4);
+  w.kbar = take(BH * d.T * d.D * 4);
+  w.scores = take(BH * d.T * d.T * 4);
+  w.lut = take(BH * d.T * d.T * 4);
+  w.lut_cnt = take(BH * d.T * 4);
+  w.col = take(BH * d.T * d.T * 4);
+  w.col_cnt = take(BH * d.T * 4);
+  w.rbits = take(BH * d.Tp * (d.Tp / 32) * 4);
+  w.cbits = take(BH * d.Tp * (d.Tp / 32) * 4);
+  w.states = take(BH * (d.Tp / 8) * d.NB * 8 * 2);
+  w.dstate = take(BH * d.T * d.D * d.D * 2);
+  w.dstate_z = take(BH * d.T * 2 * d.D * 4);
+  w.dsum = take(BH * d.N * 4);
+  w.dw_part = take(static_cast<size_t>(kDwParts) * d.D * d.D * 4);
+  w.total = off;
+  return w;
+}
+
+SavedLayout saved_layout(const Dims& d) {
+  SavedLayout s{};
+  const size_t BH = static_cast<size_t>(d.BH());
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  s.lse = take(BH * d.N * 4);
+  s.den = take(BH * d.N * 4);
+  s.y = take(BH * d.N * d.D * 2);
+  s.hst = take(BH * d.T * d.D * d.D * 2);
+  s.zst = take(BH * d.T * 2 * d.D * 4);
+  s.total = off;
+  return s;
+}
+
+}  // namespace sla
+
+using namespace sla;
+
+extern "C" {
+
+sla_status sla_block_counts(const sla_config* cfg, int32_t* k_c, int32_t* k_n, int32_t* k_m) {
+  Dims d;
+  SLA_CHECK(make_dims(cfg, &d));
+  if (k_c) *k_c = d.kc;
+  if (k_n) *k_n = d.kn;
+  if (k_m) *k_m = d.km;
+  return SLA_OK;
+}
+
+size_t sla_workspace_size(const sla_config* cfg) {
+  Dims d;
+  if (make_dims(cfg, &d) != SLA_OK) return 0;
+  return workspace_layout(d).total;
+}
+
+size_t sla_saved_size(const sla_config* cfg) {
+  Dims d;
+  if (make_dims(cfg, &d) != SLA_OK) return 0;
+  return saved_layout(d).total;
+}
+
+sla_status sla_saved_offsets(const sla_config* cfg, size_t* lse, size_t* den, size_t* y,
+                             size_t* hst, size_t* zst) {
+  Dims d;
+  SLA_CHECK(make_dims(cfg, &d));
+  const SavedLayout s = saved_layout(d);
+  if (lse) *lse = s.lse;
+  if (den) *den = s.den;
+  if (y) *y = s.y;
+  if (hst) *hst = s.hst;
+  if (zst) *zst = s.zst;
+  return SLA_OK;
+}
+
+sla_status sla_forward(const sla_config* cfg, const void* q, const void* k, const void* v,
+                       const void* w, void* o, int8_t* mask, void* saved, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  Dims d;
+  SLA_CHECK(make_dims(cfg, &d));
+  SLA_CHECK(check_ptr(q, "q"));
+  SLA_CHECK(check_ptr(k, "k"));
+  SLA_CHECK(check_ptr(v, "v"));
+  SLA_CHECK(check_ptr(w, "w"));
+  SLA_CHECK(check_ptr(o, "o"));
+  SLA_CHECK(check_ptr(mask, "mask"));
+  SLA_CHECK(check_ptr(saved, "saved"));
+  SLA_CHECK(check_ptr(workspace, "workspace"));
+  const WorkspaceLayout wl = workspace_layout(d);
+  if (workspace_bytes < wl.total)
+    return fail(SLA_ERR_WORKSPACE, "workspace of %zu bytes is below the required %zu",
+                workspace_bytes, wl.total);
+  const SavedLayout sl = saved_layout(d);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Stages stg{static_cast<hipEvent_t*>(cfg->stage_events), s};
+  char* ws = static_cast<char*>(workspace);
+  char* sv = static_cast<char*>(saved);
+  auto* lut = reinterpret_cast<int32_t*>(ws + wl.lut);
+  auto* lut_cnt = reinterpret_cast<int32_t*>(ws + wl.lut_cnt);
+  auto* rbits = reinterpret_cast<uint32_t*>(ws + wl.rbits);
+  auto* states = reinterpret_cast<uint16_t*>(ws + wl.states);
+  auto* hst = reinterpret_cast<uint16_t*>(sv + sl.hst);
+  auto* zst = reinterpret_cast<float*>(sv + sl.zst);
+  const auto* q16 = static_cast<const uint16_t*>(q);
+  const auto* k16 = static_cast<const uint16_t*>(k);
+  const auto* v16 = static_cast<const uint16_t*>(v);
+
+  const bool given = d.mask_mode == SLA_MASK_GIVEN;
+  // all blocks critical: plain dense attention, no classification, no linear branch
+  const bool dense = !given && d.kc == d.T;
+  const bool linear = given || d.km > 0;
+
+  if (dense) {
+    SLA_CHECK(launched(launch_fill_mask(d, mask, 1, s), "fill_mask"));
+  } else {
+    if (linear || !given) {
+      SLA_CHECK(stg.begin(SLA_STAGE_KV_STATE));
+      SLA_CHECK(launched(launch_kv_state(d, k16, v16, reinterpret_cast<float*>(ws + wl.kbar), states, s),
+                         "kv_state"));
+      SLA_CHECK(stg.end(SLA_STAGE_KV_STATE));
+    }
+    if (!given) {
+      SLA_CHECK(stg.begin(SLA_STAGE_POOL_Q));
+      SLA_CHECK(launched(launch_pool(d, q16, reinterpret_cast<float*>(ws + wl.qbar), s), "pool_q"));
+      SLA_CHECK(stg.end(SLA_STAGE_POOL_Q));
+      SLA_CHECK(stg.begin(SLA_STAGE_CLASSIFY));
+      SLA_CHECK(launched(launch_scores(d, reinterpret_cast<float*>(ws + wl.qbar),
+                                       reinterpret_cast<float*>(ws + wl.kbar),
+                                       reinterpret_cast<float*>(ws + wl.scores), s),
+                         "scores"));
+      SLA_CHECK(launched(launch_classify(d, reinterpret_cast<float*>(ws + wl.scores), mask, lut,
+                                         lut_cnt, rbits, s),
+                         "classify"));
+      SLA_CHECK(stg.end(SLA_STAGE_CLASSIFY));
+    } else {
+      SLA_CHECK(stg.begin(SLA_STAGE_CLASSIFY));
+      SLA_CHECK(launched(launch_mask_lists(d, mask, lut, lut_cnt, rbits, nullptr, nullptr, nullptr, s),
+                         "mask_lists"));
+      SLA_CHECK(stg.end(SLA_STAGE_CLASSIFY));
+    }
+    if (linear) {
+      SLA_CHECK(stg.begin(SLA_STAGE_AGGREGATE));
+      SLA_CHECK(launched(launch_aggregate(d, rbits, states, hst, zst, s), "aggregate"));
+      SLA_CHECK(stg.end(SLA_STAGE_AGGREGATE));
+    }
+  }
+  SLA_CHECK(stg.begin(SLA_STAGE_ATTENTION));
+  SLA_CHECK(launched(launch_attn_fwd(d, q16, k16, v16, static_cast<const uint16_t*>(w), lut, lut_cnt,
+                                     dense, linear, hst, zst, static_cast<uint16_t*>(o),
+                                     reinterpret_cast<float*>(sv + sl.lse),
+                                     reinterpret_cast<float*>(sv + sl.den),
+                                     reinterpret_cast<uint16_t*>(sv + sl.y), s),
+                     "attention"));
+  SLA_CHECK(stg.end(SLA_STAGE_ATTENTION));
+  return SLA_OK;
+}
+
+sla_status sla_backward(const sla_config* cfg, const void* q, const void* k, const void* v,
+                        const void* w, const void* o, const void* d_o, const int8_t* mask,
+                        const void* saved, float* dq, float* dk, float* dv, float* dw,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  Dims d;
+  SLA_CHECK(make_dims(cfg, &d));
+  SLA_CHECK(check_ptr(q, "q"));
+  SLA_CHECK(check_ptr(k, "k"));
+  SLA_CHECK(check_ptr(v, "v"));
+  SLA_CHECK(check_ptr(w, "w"));
+  SLA_CHECK(check_ptr(o, "o"));
+  SLA_CHECK(check_ptr(d_o, "d_o"));
+  SLA_CHECK(check_ptr(mask, "mask"));
+  SLA_CHECK(check_ptr(saved, "saved"));
+  SLA_CHECK(check_ptr(dq, "dq"));
+  SLA_CHECK(check_ptr(dk, "dk"));
+  SLA_CHECK(check_ptr(dv, "dv"));
+  SLA_CHECK(check_ptr(dw, "dw"));
+  SLA_CHECK(check_ptr(workspace, "workspace"));
+  const WorkspaceLayout wl = workspace_layout(d);
+  if (workspace_bytes < wl.total)
+    return fail(SLA_ERR_WORKSPACE, "workspace of %zu bytes is below the required %zu",
+                workspace_bytes, wl.total);
+  (void)stream;
+  return fail(SLA_ERR_UNSUPPORTED, "backward not built yet");
+}
+
+sla_status sla_pool_scores(const sla_config* cfg, const void* q, const void* k, float* scores,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  Dims d;
+  SLA_CHECK(make_dims(cfg, &d));
+  SLA_CHECK(check_ptr(q, "q"));
+  SLA_CHECK(check_ptr(k, "k"));
+  SLA_CHECK(check_ptr(scores, "scores"));
+  SLA_CHECK(check_ptr(workspace, "workspace"));
+  const WorkspaceLayout wl = workspace_layout(d);
+  if (workspace_bytes < wl.total)
+    return fail(SLA_ERR_WORKSPACE, "workspace of %zu bytes is below the required %zu",
+                workspace_bytes, wl.total);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  auto* qbar = reinterpret_cast<float*>(ws + wl.qbar);
+  auto* kbar = reinterpret_cast<float*>(ws + wl.kbar);
+  SLA_CHECK(launched(launch_pool(d, static_cast<const uint16_t*>(q), qbar, s), "pool_q"));
+  SLA_CHECK(launched(launch_pool(d, static_cast<const uint16_t*>(k), kbar, s), "pool_k"));
+  SLA_CHECK(launched(launch_scores(d, qbar, kbar, scores, s), "scores"));
+  return SLA_OK;
+}
+
+sla_status sla_classify(const sla_config* cfg, const float* scores, int8_t* mask, void* stream) {
+  Dims d;
+  SLA_CHECK(make_dims(cfg, &d));
+  SLA_CHECK(check_ptr(scores, "scores"));
+  SLA_CHECK(check_ptr(mask, "mask"));
+  return launched(launch_classify(d, scores, mask, nullptr, nullptr, nullptr,
+                                  static_cast<hipStream_t>(stream)),
+                  "classify");
+}
+
+const char* sla_status_string(sla_status status) {
+  switch (status) {
+    case SLA_OK: return "ok";
+    case SLA_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case SLA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case SLA_ERR_WORKSPACE: return "workspace too small";
+    case SLA_ERR_DEVICE: return "device error";
+  }
+  return "unknown status";
+}
+
+const char* sla_last_error(void) { return g_last_error; }
+
+}  // extern "C"

@@ -1,0 +1,98 @@
+// Device-side helpers shared by the gfx950 kernels of the SLA library.
+//
+// MFMA operand layouts used throughout (wave64, bf16 inputs, fp32 accumulate):
+//   v_mfma_f32_32x32x16_bf16: lane l holds A[m = l % 32][k = 8 (l / 32) + s] and
+//     B[k = 8 (l / 32) + s][n = l % 32] for s = 0..7; result register i holds
+//     C[m = 8 (i / 4) + 4 (l / 32) + i % 4][n = l % 32], i = 0..15.
+//   v_mfma_f32_16x16x32_bf16: lane l holds A[m = l % 16][k = 8 (l / 16) + s],
+//     B[k = 8 (l / 16) + s][n = l % 16]; result register i holds
+//     C[m = 4 (l / 16) + i][n = l % 16], i = 0..3.
+// Because an MFMA sums over k, any permutation of the k index that A and B
+// share leaves the product unchanged; kernels use that to feed a 32x32 result
+// tile straight back in as the B operand of the next product.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sla {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+// Native vector types for register staging (HIP's uint4 class defeats
+// scalar replacement of register arrays).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kBlock = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round-to-nearest-even fp32 -> bf16 (finite inputs; NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float x) {
+  uint32_t u = __float_as_uint(x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+// elu(x) + 1
+__device__ __forceinline__ float phi(float x) { return x > 0.f ? x + 1.f : __expf(x); }
+__device__ __forceinline__ float phi_prime(float x) { return x > 0.f ? 1.f : __expf(x); }
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const uint4& v) {
+  bf16x8 r;
+  __builtin_memcpy(&r, &v, 16);
+  return r;
+}
+__device__ __forceinline__ bf16x8 as_bf16x8(const uint2& lo, const uint2& hi) {
+  uint4 v = make_uint4(lo.x, lo.y, hi.x, hi.y);
+  return as_bf16x8(v);
+}
+__device__ __forceinline__ uint4 as_uint4(const bf16x8& v) {
+  uint4 r;
+  __builtin_memcpy(&r, &v, 16);
+  return r;
+}
+
+// 16-bit element s (0..7) of a 16-byte register vector.
+__device__ __forceinline__ uint32_t u4_elem(const u32x4& v, int s) {
+  const uint32_t w = v[s >> 1];
+  return (s & 1) ? (w >> 16) : (w & 0xffffu);
+}
+__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ bf16x8 as_bf16x8(const u32x2& lo, const u32x2& hi) {
+  return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+}
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ u32x2 ld8(const void* p) { return *reinterpret_cast<const u32x2*>(p); }
+__device__ __forceinline__ void st16(void* p, const u32x4& v) { *reinterpret_cast<u32x4*>(p) = v; }
+__device__ __forceinline__ void st8(void* p, const u32x2& v) { *reinterpret_cast<u32x2*>(p) = v; }
+
+// Workgroup id remapped so that consecutive logical ids share an XCD: the
+// hardware deals workgroups round-robin over the 8 XCDs, each with its own L2.
+__device__ __forceinline__ uint32_t xcd_remap(uint32_t bid, uint32_t total) {
+  if (total % 8u != 0u) return bid;
+  return (bid % 8u) * (total / 8u) + bid / 8u;
+}
+
+}  // namespace sla

@@ -1,0 +1,83 @@
+// Internal layout of the workspace / saved buffers and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/sla.h"
+
+namespace sla {
+
+// Shapes derived from a validated sla_config.
+struct Dims {
+  int B, H, N, D, L;   // batch, heads, seq_len, head_dim, valid_len
+  int T;               // number of 64-token blocks
+  int Tp;              // T rounded up to a multiple of 32 (K-dimension of the aggregation)
+  int NB;              // per-block state row: D*D entries of h^T then 2*D of z (hi, lo)
+  int kc, kn, km;      // per-row counts (compute mode)
+  float scale;         // softmax scale
+  int mask_mode;
+  long long BH() const { return static_cast<long long>(B) * H; }
+};
+
+// Byte offsets inside the caller's workspace.
+struct WorkspaceLayout {
+  size_t qbar, kbar;        // fp32 [BH, T, D]
+  size_t scores;            // fp32 [BH, T, T]
+  size_t lut, lut_cnt;      // int32 [BH, T, T] critical key blocks per row (ascending), int32 [BH, T]
+  size_t col, col_cnt;      // int32 [BH, T, T] critical query blocks per column, int32 [BH, T]
+  size_t rbits, cbits;      // uint32 [BH, Tp, Tp/32] marginal bits by row / by column
+  size_t states;            // bf16 [BH, Tp/8, NB, 8]  (forward h/z states; backward dH/dZ)
+  size_t dstate;            // bf16 [BH, T, D*D] + fp32 [BH, T, 2, D] aggregated backward states
+  size_t dstate_z;
+  size_t dsum;              // fp32 [BH, N]  D_r of the backward
+  size_t dw_part;           // fp32 [P, D, D] dW partial sums
+  size_t total;
+};
+
+struct SavedLayout {
+  size_t lse, den, y, hst, zst, total;
+};
+
+constexpr int kDwParts = 256;
+
+WorkspaceLayout workspace_layout(const Dims& d);
+SavedLayout saved_layout(const Dims& d);
+
+// ---- launchers (return hipSuccess or the launch error) ----
+hipError_t launch_kv_state(const Dims& d, const uint16_t* k, const uint16_t* v, float* kbar,
+                           uint16_t* states, hipStream_t s);
+hipError_t launch_pool(const Dims& d, const uint16_t* x, float* xbar, hipStream_t s);
+hipError_t launch_scores(const Dims& d, const float* qbar, const float* kbar, float* scores,
+                         hipStream_t s);
+hipError_t launch_classify(const Dims& d, const float* scores, int8_t* mask, int32_t* lut,
+                           int32_t* lut_cnt, uint32_t* rbits, hipStream_t s);
+hipError_t launch_mask_lists(const Dims& d, const int8_t* mask, int32_t* lut, int32_t* lut_cnt,
+                             uint32_t* rbits, int32_t* col, int32_t* col_cnt, uint32_t* cbits,
+                             hipStream_t s);
+hipError_t launch_fill_mask(const Dims& d, int8_t* mask, int8_t value, hipStream_t s);
+hipError_t launch_aggregate(const Dims& d, const uint32_t* bits, const uint16_t* states,
+                            uint16_t* hout, float* zout, hipStream_t s);
+hipError_t launch_attn_fwd(const Dims& d, const uint16_t* q, const uint16_t* k,
+                           const uint16_t* v, const uint16_t* w, const int32_t* lut,
+                           const int32_t* lut_cnt, bool dense, bool linear,
+                           const uint16_t* hst, const float* zst, uint16_t* o, float* lse,
+                           float* den, uint16_t* y, hipStream_t s);
+
+// backward
+hipError_t launch_bwd_q_lin(const Dims& d, const uint16_t* q, const uint16_t* o,
+                            const uint16_t* dO, const uint16_t* w, const float* den,
+                            const uint16_t* y, const uint16_t* hst, const float* zst,
+                            float* dsum, float* dq, uint16_t* dstates, hipStream_t s);
+hipError_t launch_dw(const Dims& d, const uint16_t* dO, const uint16_t* y, float* part, float* dw,
+                     hipStream_t s);
+hipError_t launch_bwd_kv(const Dims& d, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                         const uint16_t* dO, const float* lse, const float* dsum,
+                         const int32_t* col, const int32_t* col_cnt, const uint16_t* dh,
+                         const float* dz, float* dk, float* dv, hipStream_t s);
+hipError_t launch_bwd_q(const Dims& d, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                        const uint16_t* dO, const float* lse, const float* dsum,
+                        const int32_t* lut, const int32_t* lut_cnt, float* dq, hipStream_t s);
+
+}  // namespace sla
