@@ -1,0 +1,267 @@
+#!/usr/bin/env python3
+"""Benchmark of the SLA hot path on one MI355X.
+
+One step = one ``sla_forward`` plus one ``sla_backward`` (every stage of the
+method: states, pooling, classification, aggregation, fused attention, and the
+backward) on one batch of seeded synthetic input already resident in HBM.
+Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--mode fwd|fwdbwd] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+DEFAULT_WORKLOAD = "video_dit_b2_h12_n32768_d128"
+DOMINANT = {"fwd": "attention", "fwdbwd": "attention"}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--mode", choices=("fwd", "fwdbwd"), default="fwdbwd")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--dense", action="store_true",
+                    help="time the same library as dense attention (all blocks critical)")
+    return ap.parse_args()
+
+
+class HipEvents:
+    """hipEvent_t arrays created through the HIP runtime torch already loaded."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventQuery.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def array(self, n):
+        arr = (ctypes.c_void_p * n)()
+        for i in range(n):
+            ev = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(ev)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            arr[i] = ev
+        return arr
+
+    def elapsed_ms(self, a, b):
+        out = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(out), a, b) != 0:
+            return None
+        return out.value
+
+
+def kernel_sources_digest(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "sparse_linear_attention_mean_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(kernel, workload, digest):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_digest") != digest:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(inp, wl, k_c, k_n):
+    """The oracle as it stands, on a bounded sample of the same workload:
+    states of one head, the forward of half of its query blocks and the
+    backward of one head of the same structure at half the length."""
+    import oracle as orc
+
+    scale = orc.default_scale(wl.head_dim)
+    q = orc.decode_bf16(inp["q"][0, 0])
+    k = orc.decode_bf16(inp["k"][0, 0])
+    v = orc.decode_bf16(inp["v"][0, 0])
+    w = orc.decode_bf16(inp["w"])
+    t = wl.num_blocks
+    t0 = time.perf_counter()
+    scores = orc.compressed_scores(q, k, wl.valid_len, scale)
+    mask = orc.classify(scores, k_c, k_n)
+    blocks = list(range(0, t, 2))
+    orc.forward_head(q, k, v, w, mask, wl.valid_len, scale, blocks=blocks)
+    t_fwd = time.perf_counter() - t0
+    flops_fwd = 4.0 * 64 * 64 * wl.head_dim * k_c * len(blocks)
+    # backward on the first half of the head (same block size and fractions)
+    nq = max(64, (wl.seq_len // 2) // 64 * 64)
+    tq = nq // 64
+    kc_q, kn_q, _ = orc.block_counts(tq, wl.frac_critical, wl.frac_negligible)
+    mq = orc.classify(orc.compressed_scores(q[:nq], k[:nq], nq, scale), kc_q, kn_q)
+    do = orc.decode_bf16(inp["do"][0, 0])[:nq] if "do" in inp else np.ones((nq, wl.head_dim))
+    t1 = time.perf_counter()
+    orc.backward_head(q[:nq], k[:nq], v[:nq], w, do, mq, nq, scale)
+    t_bwd = time.perf_counter() - t1
+    flops_bwd = 10.0 * 64 * 64 * wl.head_dim * kc_q * tq
+    tflops = (flops_fwd + flops_bwd) / (t_fwd + t_bwd) / 1e12
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count()
+    threads = int(os.environ.get("OMP_NUM_THREADS", cores))
+    return {
+        "value": tflops,
+        "unit": "TFLOP/s (critical-block FLOPs, fp64 oracle)",
+        "cores": min(cores, threads),
+        "kind": "oracle",
+        "sample": (f"head (0,0): scores+classify, states, forward of {len(blocks)} of {t} query "
+                   f"blocks ({t_fwd:.1f} s); backward of its first {nq} tokens ({t_bwd:.1f} s)"),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; multi-GPU runs are not part of it",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+
+    from sparse_linear_attention_mean_amd import _binding as B
+    from sparse_linear_attention_mean_amd.attention import SlaProblem, bf16_from_bits
+    from sparse_linear_attention_mean_amd.inputs import WORKLOADS, make_workload_inputs
+
+    wl = WORKLOADS[args.workload]
+    fc, fn = (1.0, 0.0) if args.dense else (wl.frac_critical, wl.frac_negligible)
+    with_bwd = args.mode == "fwdbwd"
+    inp = make_workload_inputs(wl.name, seed=args.seed, with_grad=with_bwd)
+    dev = torch.device("cuda:0")
+    q, k, v, w = (bf16_from_bits(inp[x], dev) for x in ("q", "k", "v", "w"))
+    do = bf16_from_bits(inp["do"], dev) if with_bwd else None
+    prob = SlaProblem.create(wl.batch, wl.heads, wl.seq_len, wl.head_dim, fc, fn,
+                             valid_len=wl.valid_len, device=dev)
+    k_c, k_n, k_m = B.sla_block_counts(prob.cfg)
+    o = torch.empty(prob.shape(), dtype=torch.bfloat16, device=dev)
+    mask = prob.new_mask()
+    shp = prob.shape()
+    grads = None
+    if with_bwd:
+        grads = tuple(torch.empty(shp, dtype=torch.float32, device=dev) for _ in range(3)) + (
+            torch.empty((wl.head_dim, wl.head_dim), dtype=torch.float32, device=dev),)
+
+    hip = HipEvents()
+    nstage = B.SLA_NUM_STAGES
+    ev_sets = [hip.array(2 * nstage) for _ in range(args.steps)]
+    warm_ev = hip.array(2 * nstage)
+
+    def step(ev):
+        prob.cfg.stage_events = ctypes.cast(ev, ctypes.c_void_p).value
+        prob.forward(q, k, v, w, o=o, mask=mask)
+        if with_bwd:
+            prob.backward(q, k, v, w, o, do, mask, grads=grads)
+
+    for _ in range(args.warmup):
+        step(warm_ev)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for s in range(args.steps):
+        step(ev_sets[s])
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+
+    stage_ms = {}
+    for si, name in enumerate(B.STAGES):
+        vals = [hip.elapsed_ms(ev_sets[s][2 * si], ev_sets[s][2 * si + 1]) for s in range(args.steps)]
+        vals = [x for x in vals if x is not None]
+        if vals:
+            stage_ms[name] = sum(vals) / len(vals)
+
+    bh = wl.batch * wl.heads
+    t = wl.num_blocks
+    d = wl.head_dim
+    pairs = bh * t * k_c
+    flops_fwd_crit = 4.0 * 64 * 64 * d * pairs
+    flops_bwd_crit = 10.0 * 64 * 64 * d * pairs if with_bwd else 0.0
+    flops = flops_fwd_crit + flops_bwd_crit
+    dense_flops = (4.0 + (10.0 if with_bwd else 0.0)) * bh * wl.seq_len ** 2 * d
+    value = flops / (ms * 1e-3) / 1e12
+
+    # dominant kernel: the fused forward attention (MFMA-bound)
+    dom = DOMINANT[args.mode]
+    dom_ms = stage_ms.get(dom)
+    linear_flops = (2 * 2.0 * 64 * d * d * bh * t) if k_m > 0 else 0.0
+    dom_flops = flops_fwd_crit + linear_flops
+    achieved = dom_flops / (dom_ms * 1e-3) / 1e12 if dom_ms else None
+    digest = kernel_sources_digest(["attn_fwd.hip", "sla_device.h"])
+    traffic = traffic_from_profile("attn_fwd", wl.name, digest)
+
+    rec = {
+        "metric": "SLA fwd/bwd effective TFLOPS + % bf16 MFMA peak at N=32768,H=12,d=128",
+        "value": round(value, 2),
+        "unit": "TFLOP/s (critical-block FLOPs)",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded grid-structured Q/K, Gaussian V and dO)",
+        "config": {
+            "workload": wl.name,
+            "batch": wl.batch, "heads": wl.heads, "seq_len": wl.seq_len,
+            "valid_len": wl.valid_len, "head_dim": d, "block": 64,
+            "frac_critical": fc, "frac_negligible": fn,
+            "k_c": k_c, "k_n": k_n, "k_m": k_m, "mode": args.mode,
+        },
+        "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "tflops_dense_equivalent": round(dense_flops / (ms * 1e-3) / 1e12, 1),
+        "stages_ms": {kk: round(vv, 4) for kk, vv in stage_ms.items()},
+        "roofline": {
+            "kernel": "attn_fwd_kernel (fused sparse + linear + projection)",
+            "bound": "mfma",
+            "achieved": round(achieved, 2) if achieved else None,
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4) if achieved else None,
+            "traffic": traffic,
+        },
+    }
+    if with_bwd:
+        fwd_ms = sum(stage_ms.get(s, 0.0) for s in B.STAGES[:5])
+        bwd_ms = sum(stage_ms.get(s, 0.0) for s in B.STAGES[5:])
+        if fwd_ms > 0:
+            rec["fwd_tflops"] = round(flops_fwd_crit / (fwd_ms * 1e-3) / 1e12, 2)
+        if bwd_ms > 0:
+            rec["bwd_tflops"] = round(flops_bwd_crit / (bwd_ms * 1e-3) / 1e12, 2)
+    if not args.no_cpu_baseline:
+        sys.path.insert(0, ROOT)
+        rec["cpu_baseline"] = cpu_baseline(inp, wl, k_c, k_n)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

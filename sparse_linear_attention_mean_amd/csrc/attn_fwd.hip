@@ -17,8 +17,11 @@
 // then the S^T result tile, converted to bf16, is directly the B operand of
 // the P V product (k index permuted identically in the V^T operand), each
 // lane owns one query row, and row statistics need a single xor-32 exchange.
-// K_j is staged to LDS row-major, V_j transposed; both double-buffered with
-// the next block's global loads in flight during the current block's MFMAs.
+// K_j is staged to LDS row-major and V_j^T (written once per key block by the
+// state builder) row-major too, so staging is a plain 16-byte copy; both are
+// double-buffered with the next block's global loads in flight during the
+// current block's MFMAs.  Row pitches (D + 8 and 68 bf16) keep the MFMA
+// operand reads free of LDS bank conflicts.
 // The two key halves are merged at the end like split-K partial softmaxes.
 #include "sla_device.h"
 #include "sla_internal.h"
@@ -28,7 +31,7 @@ namespace sla {
 struct AttnArgs {
   const uint16_t* q;
   const uint16_t* k;
-  const uint16_t* v;
+  const uint16_t* vT;
   const uint16_t* w;
   const int32_t* lut;
   const int32_t* lut_cnt;
@@ -45,11 +48,10 @@ struct AttnArgs {
 template <int D>
 struct AttnCfg {
   static constexpr int KP = D + 8;                 // K row pitch in LDS (bf16)
-  static constexpr int VP = 72;                    // V^T row pitch (64 keys + pad)
+  static constexpr int VP = 68;                    // V^T row pitch (64 keys + pad)
   static constexpr int kBuf = 64 * KP + D * VP;    // one K + V^T buffer (bf16 elements)
   static constexpr int kLds = 2 * kBuf * 2;        // bytes, double buffered
   static constexpr int KCH = D / 32;               // 16-byte K chunks per thread
-  static constexpr int TPT = D / 32;               // tokens per thread in the V transpose
   static constexpr int NCT = D / 32;               // 32-row tiles of O^T per wave
   static constexpr int NCC = D / 16;               // 16-wide k chunks over the head dim
 };
@@ -84,41 +86,31 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs args) {
   const int cnt = DENSE ? T : args.lut_cnt[bh * T + i];
   const int32_t* lrow = DENSE ? nullptr : args.lut + (bh * T + i) * static_cast<long long>(T);
 
-  // staging roles
-  u32x4 rk[C::KCH], rv[C::TPT];
-  const int vgrp = tid / (D / 8), vc8 = tid % (D / 8);
-#define SLA_LOAD_BLOCK(jblk)                                                                      \
-  do {                                                                                            \
-    const int j_ = (jblk);                                                                        \
-    const uint16_t* kb = args.k + head + static_cast<size_t>(j_) * kBlock * D;                    \
-    const uint16_t* vb = args.v + head + static_cast<size_t>(j_) * kBlock * D;                    \
-    _Pragma("unroll") for (int u = 0; u < C::KCH; ++u) {                                          \
-      const int c = tid + 256 * u;                                                                \
-      rk[u] = ld16(kb + static_cast<size_t>(c / (D / 8)) * D + 8 * (c % (D / 8)));                \
-    }                                                                                             \
-    _Pragma("unroll") for (int u = 0; u < C::TPT; ++u) {                                          \
-      const int t = C::TPT * vgrp + u;                                                            \
-      const u32x4 val = ld16(vb + static_cast<size_t>(t) * D + 8 * vc8);                          \
-      rv[u] = (j_ * kBlock + t < L) ? val : u32x4{0u, 0u, 0u, 0u};                                \
-    }                                                                                             \
+  // staging: 8 D chunks of 16 bytes for K (row t, 8 columns) and as many for
+  // V^T (row c, 8 tokens); chunk e = tid + 256 u
+  u32x4 rk[C::KCH], rv[C::KCH];
+#define SLA_LOAD_BLOCK(jblk)                                                                  \
+  do {                                                                                        \
+    const int j_ = (jblk);                                                                    \
+    const uint16_t* kb = args.k + head + static_cast<size_t>(j_) * kBlock * D;                \
+    const uint16_t* vb = args.vT + head + static_cast<size_t>(j_) * kBlock * D;               \
+    _Pragma("unroll") for (int u = 0; u < C::KCH; ++u) {                                      \
+      const int e = tid + 256 * u;                                                            \
+      rk[u] = ld16(kb + 8 * e);                                                               \
+      rv[u] = ld16(vb + 8 * e);                                                               \
+    }                                                                                         \
   } while (0)
-#define SLA_STORE_BLOCK(bufidx)                                                                   \
-  do {                                                                                            \
-    uint16_t* ks_ = smem + (bufidx) * C::kBuf;                                                    \
-    uint16_t* vt_ = ks_ + 64 * KP;                                                                \
-    _Pragma("unroll") for (int u = 0; u < C::KCH; ++u) {                                          \
-      const int c = tid + 256 * u;                                                                \
-      st16(ks_ + (c / (D / 8)) * KP + 8 * (c % (D / 8)), rk[u]);                                  \
-    }                                                                                             \
-    _Pragma("unroll") for (int s = 0; s < 8; ++s) {                                               \
-      uint16_t* dst = vt_ + (8 * vc8 + s) * VP + C::TPT * vgrp;                                   \
-      if constexpr (C::TPT == 4) {                                                                \
-        st8(dst, u32x2{u4_elem(rv[0], s) | (u4_elem(rv[1], s) << 16),                             \
-                       u4_elem(rv[2], s) | (u4_elem(rv[3], s) << 16)});                           \
-      } else {                                                                                    \
-        *reinterpret_cast<uint32_t*>(dst) = u4_elem(rv[0], s) | (u4_elem(rv[1], s) << 16);        \
-      }                                                                                           \
-    }                                                                                             \
+#define SLA_STORE_BLOCK(bufidx)                                                               \
+  do {                                                                                        \
+    uint16_t* ks_ = smem + (bufidx) * C::kBuf;                                                \
+    uint16_t* vt_ = ks_ + 64 * KP;                                                            \
+    _Pragma("unroll") for (int u = 0; u < C::KCH; ++u) {                                      \
+      const int e = tid + 256 * u;                                                            \
+      st16(ks_ + (e / (D / 8)) * KP + 8 * (e % (D / 8)), rk[u]);                             \
+      uint16_t* vd = vt_ + (e >> 3) * VP + 8 * (e & 7);                                       \
+      st8(vd, u32x2{rv[u][0], rv[u][1]});                                                     \
+      st8(vd + 4, u32x2{rv[u][2], rv[u][3]});                                                 \
+    }                                                                                         \
   } while (0)
 
   f32x16 acc[C::NCT];
@@ -146,19 +138,17 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs args) {
       st = mfma32(as_bf16x8(ld16(ks + (32 * kh + n32) * KP + 16 * cc + 8 * hl)), qf[cc], st);
     }
     const bool tail = (j + 1) * kBlock > L;
-    float mloc = -INFINITY;
+    float mraw = -INFINITY;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      float x = st[e] * sl2;
       if (tail) {
         const int key = j * kBlock + 32 * kh + 8 * (e / 4) + 4 * hl + (e % 4);
-        if (key >= L) x = -INFINITY;
+        if (key >= L) st[e] = -INFINITY;
       }
-      st[e] = x;
-      mloc = fmaxf(mloc, x);
+      mraw = fmaxf(mraw, st[e]);
     }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-    const float m_new = fmaxf(m_run, mloc);
+    mraw = fmaxf(mraw, __shfl_xor(mraw, 32));
+    const float m_new = fmaxf(m_run, mraw * sl2);
     const bool need = m_new > m_run + 8.0f;
     if (__any(need)) {
       const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
@@ -173,7 +163,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs args) {
     float p[16];
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      p[e] = __builtin_amdgcn_exp2f(st[e] - mu);
+      p[e] = __builtin_amdgcn_exp2f(__fmaf_rn(st[e], sl2, -mu));
       l_run += p[e];
     }
     bf16x8 pb[2];
@@ -354,11 +344,11 @@ static hipError_t launch_attn_t(const AttnArgs& a, unsigned grid, bool dense, bo
 }
 
 hipError_t launch_attn_fwd(const Dims& d, const uint16_t* q, const uint16_t* k,
-                           const uint16_t* v, const uint16_t* w, const int32_t* lut,
+                           const uint16_t* vT, const uint16_t* w, const int32_t* lut,
                            const int32_t* lut_cnt, bool dense, bool linear,
                            const uint16_t* hst, const float* zst, uint16_t* o, float* lse,
                            float* den, uint16_t* y, hipStream_t s) {
-  AttnArgs a{q, k, v, w, lut, lut_cnt, hst, zst, o, lse, den, y, d.N, d.L, d.T,
+  AttnArgs a{q, k, vT, w, lut, lut_cnt, hst, zst, o, lse, den, y, d.N, d.L, d.T,
              d.scale * kLog2e};
   const unsigned grid = static_cast<unsigned>(d.BH() * d.T);
   if (d.D == 128) return launch_attn_t<128>(a, grid, dense, linear, s);

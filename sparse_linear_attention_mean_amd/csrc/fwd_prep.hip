@@ -27,6 +27,8 @@ namespace sla {
 // phi(k) is rounded to bf16 once and the same rounded values feed h and z.
 // kbar sums column a in token order 0..63 in fp32, exactly as pool_kernel
 // does, so the pooled K is bit-identical in both paths.
+// The kernel also writes V^T per key block, vT[bh][j][c][t] (bf16, padded
+// tokens zero), which the attention kernels stage without transposing.
 // ---------------------------------------------------------------------------
 template <int D>
 struct KvCfg {
@@ -40,7 +42,7 @@ struct KvCfg {
 template <int D>
 __global__ __launch_bounds__(KvCfg<D>::kThreads) void kv_state_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, float* __restrict__ kbar,
-    uint16_t* __restrict__ states, int N, int L, int T, int Tp) {
+    uint16_t* __restrict__ states, uint16_t* __restrict__ vT, int N, int L, int T, int Tp) {
   using C = KvCfg<D>;
   constexpr int P = C::kPitch;
   constexpr int TPW = C::kTilesPerWave;
@@ -103,6 +105,14 @@ __global__ __launch_bounds__(KvCfg<D>::kThreads) void kv_state_kernel(
     }
     __syncthreads();
     if (jj < 7) load(j + 1);
+    if (j < T) {
+      // V^T of this key block: D rows of 64 tokens, 8 chunks of 16 bytes per row
+      uint16_t* dst = vT + (static_cast<size_t>(bh) * T + j) * D * kBlock;
+      for (int e = tid; e < D * 8; e += C::kThreads) {
+        const int c = e >> 3, m = e & 7;
+        st16(dst + c * kBlock + 8 * m, ld16(&vt[c * P + 8 * m]));
+      }
+    }
 
 #pragma unroll
     for (int x = 0; x < TPW; ++x) {
@@ -156,6 +166,34 @@ __global__ __launch_bounds__(KvCfg<D>::kThreads) void kv_state_kernel(
   }
   for (int e = tid; e < 2 * D; e += C::kThreads)
     st16(out + (static_cast<size_t>(D) * D + e) * 8, ld16(&zst[e * 8]));
+}
+
+// ---------------------------------------------------------------------------
+// v_transpose: vT[bh][j][c][t] = v[bh][64 j + t][c] (zero for padded tokens),
+// for the paths that run no state builder (all blocks critical).
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void v_transpose_kernel(const uint16_t* __restrict__ v,
+                                                          uint16_t* __restrict__ vT, int N, int L,
+                                                          int T) {
+  __shared__ uint16_t tile[D * 72];
+  const long long blk = blockIdx.x;   // bh * T + j
+  const int j = static_cast<int>(blk % T);
+  const long long bh = blk / T;
+  const uint16_t* src = v + (static_cast<size_t>(bh) * N + static_cast<size_t>(j) * kBlock) * D;
+  for (int e = threadIdx.x; e < kBlock * D / 8; e += 256) {
+    const int t = e / (D / 8), c8 = e % (D / 8);
+    u32x4 val = u32x4{0u, 0u, 0u, 0u};
+    if (j * kBlock + t < L) val = ld16(src + static_cast<size_t>(t) * D + 8 * c8);
+#pragma unroll
+    for (int s = 0; s < 8; ++s) tile[(8 * c8 + s) * 72 + t] = static_cast<uint16_t>(u4_elem(val, s));
+  }
+  __syncthreads();
+  uint16_t* dst = vT + static_cast<size_t>(blk) * D * kBlock;
+  for (int e = threadIdx.x; e < D * 8; e += 256) {
+    const int c = e >> 3, m = e & 7;
+    st16(dst + c * kBlock + 8 * m, ld16(&tile[c * 72 + 8 * m]));
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -376,14 +414,23 @@ __global__ void fill_mask_kernel(int8_t* __restrict__ mask, long long n, int8_t 
 // launchers
 // ---------------------------------------------------------------------------
 hipError_t launch_kv_state(const Dims& d, const uint16_t* k, const uint16_t* v, float* kbar,
-                           uint16_t* states, hipStream_t s) {
+                           uint16_t* states, uint16_t* vT, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(d.BH() * (d.Tp / 8)));
   if (d.D == 128)
     hipLaunchKernelGGL(kv_state_kernel<128>, grid, dim3(KvCfg<128>::kThreads), 0, s, k, v, kbar,
-                       states, d.N, d.L, d.T, d.Tp);
+                       states, vT, d.N, d.L, d.T, d.Tp);
   else
     hipLaunchKernelGGL(kv_state_kernel<64>, grid, dim3(KvCfg<64>::kThreads), 0, s, k, v, kbar,
-                       states, d.N, d.L, d.T, d.Tp);
+                       states, vT, d.N, d.L, d.T, d.Tp);
+  return hipGetLastError();
+}
+
+hipError_t launch_v_transpose(const Dims& d, const uint16_t* v, uint16_t* vT, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(d.BH() * d.T));
+  if (d.D == 128)
+    hipLaunchKernelGGL(v_transpose_kernel<128>, grid, dim3(256), 0, s, v, vT, d.N, d.L, d.T);
+  else
+    hipLaunchKernelGGL(v_transpose_kernel<64>, grid, dim3(256), 0, s, v, vT, d.N, d.L, d.T);
   return hipGetLastError();
 }
 

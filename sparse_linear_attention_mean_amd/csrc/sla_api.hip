@@ -140,6 +140,7 @@ WorkspaceLayout workspace_layout(const Dims& d) {
   w.rbits = take(BH * d.Tp * (d.Tp / 32) * 4);
   w.cbits = take(BH * d.Tp * (d.Tp / 32) * 4);
   w.states = take(BH * (d.Tp / 8) * d.NB * 8 * 2);
+  w.vT = take(BH * d.N * d.D * 2);
   w.dstate = take(BH * d.T * d.D * d.D * 2);
   w.dstate_z = take(BH * d.T * 2 * d.D * 4);
   w.dsum = take(BH * d.N * 4);
@@ -232,6 +233,7 @@ sla_status sla_forward(const sla_config* cfg, const void* q, const void* k, cons
   auto* lut_cnt = reinterpret_cast<int32_t*>(ws + wl.lut_cnt);
   auto* rbits = reinterpret_cast<uint32_t*>(ws + wl.rbits);
   auto* states = reinterpret_cast<uint16_t*>(ws + wl.states);
+  auto* vT = reinterpret_cast<uint16_t*>(ws + wl.vT);
   auto* hst = reinterpret_cast<uint16_t*>(sv + sl.hst);
   auto* zst = reinterpret_cast<float*>(sv + sl.zst);
   const auto* q16 = static_cast<const uint16_t*>(q);
@@ -245,13 +247,19 @@ sla_status sla_forward(const sla_config* cfg, const void* q, const void* k, cons
 
   if (dense) {
     SLA_CHECK(launched(launch_fill_mask(d, mask, 1, s), "fill_mask"));
+    SLA_CHECK(stg.begin(SLA_STAGE_KV_STATE));
+    SLA_CHECK(launched(launch_v_transpose(d, v16, vT, s), "v_transpose"));
+    SLA_CHECK(stg.end(SLA_STAGE_KV_STATE));
   } else {
+    SLA_CHECK(stg.begin(SLA_STAGE_KV_STATE));
     if (linear || !given) {
-      SLA_CHECK(stg.begin(SLA_STAGE_KV_STATE));
-      SLA_CHECK(launched(launch_kv_state(d, k16, v16, reinterpret_cast<float*>(ws + wl.kbar), states, s),
+      SLA_CHECK(launched(launch_kv_state(d, k16, v16, reinterpret_cast<float*>(ws + wl.kbar), states,
+                                         vT, s),
                          "kv_state"));
-      SLA_CHECK(stg.end(SLA_STAGE_KV_STATE));
+    } else {
+      SLA_CHECK(launched(launch_v_transpose(d, v16, vT, s), "v_transpose"));
     }
+    SLA_CHECK(stg.end(SLA_STAGE_KV_STATE));
     if (!given) {
       SLA_CHECK(stg.begin(SLA_STAGE_POOL_Q));
       SLA_CHECK(launched(launch_pool(d, q16, reinterpret_cast<float*>(ws + wl.qbar), s), "pool_q"));
@@ -278,7 +286,7 @@ sla_status sla_forward(const sla_config* cfg, const void* q, const void* k, cons
     }
   }
   SLA_CHECK(stg.begin(SLA_STAGE_ATTENTION));
-  SLA_CHECK(launched(launch_attn_fwd(d, q16, k16, v16, static_cast<const uint16_t*>(w), lut, lut_cnt,
+  SLA_CHECK(launched(launch_attn_fwd(d, q16, k16, vT, static_cast<const uint16_t*>(w), lut, lut_cnt,
                                      dense, linear, hst, zst, static_cast<uint16_t*>(o),
                                      reinterpret_cast<float*>(sv + sl.lse),
                                      reinterpret_cast<float*>(sv + sl.den),

@@ -29,6 +29,7 @@ struct WorkspaceLayout {
   size_t col, col_cnt;      // int32 [BH, T, T] critical query blocks per column, int32 [BH, T]
   size_t rbits, cbits;      // uint32 [BH, Tp, Tp/32] marginal bits by row / by column
   size_t states;            // bf16 [BH, Tp/8, NB, 8]  (forward h/z states; backward dH/dZ)
+  size_t vT;                // bf16 [BH, T, D, 64]  V transposed per key block
   size_t dstate;            // bf16 [BH, T, D*D] + fp32 [BH, T, 2, D] aggregated backward states
   size_t dstate_z;
   size_t dsum;              // fp32 [BH, N]  D_r of the backward
@@ -47,7 +48,8 @@ SavedLayout saved_layout(const Dims& d);
 
 // ---- launchers (return hipSuccess or the launch error) ----
 hipError_t launch_kv_state(const Dims& d, const uint16_t* k, const uint16_t* v, float* kbar,
-                           uint16_t* states, hipStream_t s);
+                           uint16_t* states, uint16_t* vT, hipStream_t s);
+hipError_t launch_v_transpose(const Dims& d, const uint16_t* v, uint16_t* vT, hipStream_t s);
 hipError_t launch_pool(const Dims& d, const uint16_t* x, float* xbar, hipStream_t s);
 hipError_t launch_scores(const Dims& d, const float* qbar, const float* kbar, float* scores,
                          hipStream_t s);
@@ -60,7 +62,7 @@ hipError_t launch_fill_mask(const Dims& d, int8_t* mask, int8_t value, hipStream
 hipError_t launch_aggregate(const Dims& d, const uint32_t* bits, const uint16_t* states,
                             uint16_t* hout, float* zout, hipStream_t s);
 hipError_t launch_attn_fwd(const Dims& d, const uint16_t* q, const uint16_t* k,
-                           const uint16_t* v, const uint16_t* w, const int32_t* lut,
+                           const uint16_t* vT, const uint16_t* w, const int32_t* lut,
                            const int32_t* lut_cnt, bool dense, bool linear,
                            const uint16_t* hst, const float* zst, uint16_t* o, float* lse,
                            float* den, uint16_t* y, hipStream_t s);
