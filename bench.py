@@ -95,8 +95,8 @@ def traffic_from_profile(kernel, workload, digest):
 
 def cpu_baseline(inp, wl, k_c, k_n):
     """The oracle as it stands, on a bounded sample of the same workload:
-    states of one head, the forward of half of its query blocks and the
-    backward of one head of the same structure at half the length."""
+    classification, states and forward of one full head, and the backward
+    of one full head."""
     import oracle as orc
 
     scale = orc.default_scale(wl.head_dim)
@@ -108,20 +108,18 @@ def cpu_baseline(inp, wl, k_c, k_n):
     t0 = time.perf_counter()
     scores = orc.compressed_scores(q, k, wl.valid_len, scale)
     mask = orc.classify(scores, k_c, k_n)
-    blocks = list(range(0, t, 2))
+    blocks = list(range(t))
     orc.forward_head(q, k, v, w, mask, wl.valid_len, scale, blocks=blocks)
     t_fwd = time.perf_counter() - t0
     flops_fwd = 4.0 * 64 * 64 * wl.head_dim * k_c * len(blocks)
-    # backward on the first half of the head (same block size and fractions)
-    nq = max(64, (wl.seq_len // 2) // 64 * 64)
-    tq = nq // 64
-    kc_q, kn_q, _ = orc.block_counts(tq, wl.frac_critical, wl.frac_negligible)
-    mq = orc.classify(orc.compressed_scores(q[:nq], k[:nq], nq, scale), kc_q, kn_q)
-    do = orc.decode_bf16(inp["do"][0, 0])[:nq] if "do" in inp else np.ones((nq, wl.head_dim))
+    # backward of the same head
+    nq = wl.seq_len
+    mq = mask
+    do = orc.decode_bf16(inp["do"][0, 0]) if "do" in inp else np.ones((nq, wl.head_dim))
     t1 = time.perf_counter()
-    orc.backward_head(q[:nq], k[:nq], v[:nq], w, do, mq, nq, scale)
+    orc.backward_head(q, k, v, w, do, mq, wl.valid_len, scale)
     t_bwd = time.perf_counter() - t1
-    flops_bwd = 10.0 * 64 * 64 * wl.head_dim * kc_q * tq
+    flops_bwd = 10.0 * 64 * 64 * wl.head_dim * k_c * t
     tflops = (flops_fwd + flops_bwd) / (t_fwd + t_bwd) / 1e12
     try:
         cores = len(os.sched_getaffinity(0))
@@ -133,8 +131,9 @@ def cpu_baseline(inp, wl, k_c, k_n):
         "unit": "TFLOP/s (critical-block FLOPs, fp64 oracle)",
         "cores": min(cores, threads),
         "kind": "oracle",
-        "sample": (f"head (0,0): scores+classify, states, forward of {len(blocks)} of {t} query "
-                   f"blocks ({t_fwd:.1f} s); backward of its first {nq} tokens ({t_bwd:.1f} s)"),
+        "sample": (f"head (0,0) of {wl.batch * wl.heads}: scores, classification, states and "
+                   f"forward of all {len(blocks)} query blocks ({t_fwd:.1f} s); backward of the "
+                   f"same head ({t_bwd:.1f} s)"),
     }
 
 

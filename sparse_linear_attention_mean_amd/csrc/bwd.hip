@@ -1,0 +1,702 @@
+// Backward of SLA for gfx950 with the block mask held fixed.
+//
+// "SLA: Beyond Sparsity in Diffusion Transformers via Fine-Tunable
+// Sparse-Linear Attention" (English abstract: the kernel supports both the
+// forward and the backward pass).  With O = O_s + Y W^T the gradients are
+// (per head, rows r of query block i, tokens t of key block j):
+//   dY = dO W,  dW = sum_r dO_r^T Y_r,  D_r = dO_r . O_s,r = dO_r . O_r - dY_r . Y_r
+//   sparse (critical pairs):  P = exp(S - lse), dP = dO V^T, dS = P (dP - D),
+//       dV += P^T dO, dK += scale dS^T Q, dQ += scale dS K
+//   linear (rows with den > 0):  dn = dY / den, dd = -(dY . Y) / den,
+//       dphi(q) = H_i dn + dd Z_i, dQ += dphi(q) phi'(q),
+//       dH_i = phi(Q_i)^T dN_i, dZ_i = phi(Q_i)^T dd_i,
+//       dh_j, dz_j = sums of dH_i, dZ_i over the rows i for which j is marginal,
+//       dphi(k_t) = dh_j v_t + dz_j, dK += dphi(k) phi'(k), dV += phi(K_j) dh_j
+// Deterministic: every reduction has a fixed order, no atomics.
+//
+// Kernels here: the query-side preparation (dY, D, dN, dd and the linear dQ),
+// the KV-major sparse + linear dK / dV kernel, the Q-major sparse dQ kernel,
+// the two-stage dW reduction and two small transposes.
+#include "sla_device.h"
+#include "sla_internal.h"
+
+namespace sla {
+
+// ---------------------------------------------------------------------------
+// w_transpose: wT[c][o] = W[o][c]
+// ---------------------------------------------------------------------------
+__global__ void w_transpose_kernel(const uint16_t* __restrict__ w, uint16_t* __restrict__ wT,
+                                   int D) {
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= D * D) return;
+  const int c = e / D, o = e % D;
+  wT[e] = w[static_cast<size_t>(o) * D + c];
+}
+
+// 8 bf16 values M[k0 + s][col] (s = 0..7) from a row-major LDS matrix.
+__device__ __forceinline__ bf16x8 lds_col8(const uint16_t* m, int pitch, int k0, int col) {
+  u32x4 r;
+#pragma unroll
+  for (int p = 0; p < 4; ++p)
+    r[p] = static_cast<uint32_t>(m[(k0 + 2 * p) * pitch + col]) |
+           (static_cast<uint32_t>(m[(k0 + 2 * p + 1) * pitch + col]) << 16);
+  return as_bf16x8(r);
+}
+
+// ---------------------------------------------------------------------------
+// bwd_prep: one workgroup (4 waves) per query block i.
+//   dY^T[c][r] = sum_o W[o][c] dO[r][o]             (wave: rows half qh, c half ch)
+//   D_r = dO_r . O_r - dY_r . Y_r,  dd_r = -(dY_r . Y_r) / den_r
+//   dN[r][c] = dY[r][c] / den_r     (bf16, also staged in LDS)
+//   dphi(q)^T[a][r] = sum_c H[a][c] dN[r][c] + dd_r Z[a]  (wave: rows half, a half)
+//   dq[r][a] = dphi(q)[r][a] phi'(q[r][a])           (initial value of dQ)
+// Rows r >= valid_len and rows with den = 0 get zero linear gradients.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ o,
+    const uint16_t* __restrict__ dO, const uint16_t* __restrict__ wT,
+    const float* __restrict__ den, const uint16_t* __restrict__ y,
+    const uint16_t* __restrict__ hst, const float* __restrict__ zst, float* __restrict__ dsum,
+    float* __restrict__ ddel, uint16_t* __restrict__ dn, float* __restrict__ dq, int N, int L,
+    int T, bool linear) {
+  constexpr int HP = D + 8;
+  constexpr int NCC = D / 16;
+  constexpr int NT = D / 64;   // 32-wide tiles per wave in each half
+  __shared__ __attribute__((aligned(16))) uint16_t hs[D * HP];   // H^T[c][a]
+  __shared__ __attribute__((aligned(16))) uint16_t dns[64 * HP]; // dN[r][c]
+  __shared__ float red[2][2][64];                                 // [c half][dO.O, dY.Y][row]
+  __shared__ float rowd[64];
+
+  const uint32_t wg = xcd_remap(blockIdx.x, gridDim.x);
+  const int i = wg % T;
+  const long long bh = wg / T;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n32 = lane & 31, hl = lane >> 5;
+  const int qh = wave & 1, ch = wave >> 1;
+  const size_t head = static_cast<size_t>(bh) * N * D;
+  const int rloc = 32 * qh + n32;
+  const int row = i * kBlock + rloc;
+  const bool valid = row < L;
+
+  // stage H^T of this query block
+  const uint16_t* hsrc = hst + (static_cast<size_t>(bh) * T + i) * D * D;
+  for (int e = tid; linear && e < D * D / 8; e += 256) {
+    const int c = e / (D / 8), a8 = e % (D / 8);
+    st16(&hs[c * HP + 8 * a8], ld16(hsrc + static_cast<size_t>(c) * D + 8 * a8));
+  }
+
+  // dY^T tiles for c in [D/2 ch, D/2 ch + D/2)
+  bf16x8 dof[NCC];
+  {
+    const uint16_t* src = dO + head + static_cast<size_t>(row) * D + 8 * hl;
+#pragma unroll
+    for (int cc = 0; cc < NCC; ++cc)
+      dof[cc] = valid ? as_bf16x8(ld16(src + 16 * cc)) : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+  }
+  f32x16 dyt[NT];
+#pragma unroll
+  for (int ct = 0; ct < NT; ++ct) {
+    dyt[ct] = f32x16{};
+    const uint16_t* wr = wT + static_cast<size_t>((D / 2) * ch + 32 * ct + n32) * D + 8 * hl;
+#pragma unroll
+    for (int cc = 0; cc < NCC; ++cc) dyt[ct] = mfma32(as_bf16x8(ld16(wr + 16 * cc)), dof[cc], dyt[ct]);
+  }
+  // partial row dots over this lane's c values
+  float p_oo = 0.f, p_yy = 0.f;
+  {
+    const size_t rb = head + static_cast<size_t>(row) * D;
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct)
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const int c0 = (D / 2) * ch + 32 * ct + 8 * e4 + 4 * hl;
+        const u32x2 yv = ld8(y + rb + c0), ov = ld8(o + rb + c0), dv = ld8(dO + rb + c0);
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          const float yy = bf16_to_f32(static_cast<uint16_t>(x & 1 ? yv[x >> 1] >> 16 : yv[x >> 1] & 0xffffu));
+          const float oo = bf16_to_f32(static_cast<uint16_t>(x & 1 ? ov[x >> 1] >> 16 : ov[x >> 1] & 0xffffu));
+          const float dd = bf16_to_f32(static_cast<uint16_t>(x & 1 ? dv[x >> 1] >> 16 : dv[x >> 1] & 0xffffu));
+          p_yy = __fmaf_rn(dyt[ct][4 * e4 + x], yy, p_yy);
+          p_oo = __fmaf_rn(dd, oo, p_oo);
+        }
+      }
+  }
+  p_oo += __shfl_xor(p_oo, 32);
+  p_yy += __shfl_xor(p_yy, 32);
+  if (hl == 0) {
+    red[ch][0][rloc] = p_oo;
+    red[ch][1][rloc] = p_yy;
+  }
+  __syncthreads();
+  const float s_oo = red[0][0][rloc] + red[1][0][rloc];
+  const float s_yy = red[0][1][rloc] + red[1][1][rloc];
+  const float dn_r = linear ? den[bh * N + row] : 0.f;
+  const bool lin = valid && dn_r > 0.f;
+  const float rden = lin ? 1.0f / dn_r : 0.f;
+  const float dd_r = lin ? -s_yy * rden : 0.f;
+  if (ch == 0 && hl == 0) {
+    dsum[bh * N + row] = valid ? s_oo - s_yy : 0.f;
+    ddel[bh * N + row] = dd_r;
+    rowd[rloc] = dd_r;
+  }
+  // dN = dY / den (bf16) to global and LDS
+  {
+    uint16_t* dst = dn + head + static_cast<size_t>(row) * D;
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct)
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const int c0 = (D / 2) * ch + 32 * ct + 8 * e4 + 4 * hl;
+        const u32x2 v = {pack_bf16x2(dyt[ct][4 * e4] * rden, dyt[ct][4 * e4 + 1] * rden),
+                         pack_bf16x2(dyt[ct][4 * e4 + 2] * rden, dyt[ct][4 * e4 + 3] * rden)};
+        st8(dst + c0, v);
+        st8(&dns[rloc * HP + c0], v);
+      }
+  }
+  __syncthreads();
+  // dphi(q)^T[a][r]: wave covers rows half qh and a in [D/2 ch, D/2 ch + D/2)
+  const float* zrow = zst + (static_cast<size_t>(bh) * T + i) * 2 * D;
+  const uint16_t* qrow = q + head + static_cast<size_t>(row) * D;
+  float* dqrow = dq + head + static_cast<size_t>(row) * D;
+  const float ddv = rowd[rloc];
+#pragma unroll
+  for (int at = 0; at < NT; ++at) {
+    const int abase = (D / 2) * ch + 32 * at;
+    f32x16 acc = {};
+#pragma unroll
+    for (int cc = 0; cc < NCC; ++cc) {
+      const bf16x8 a = lds_col8(hs, HP, 16 * cc + 8 * hl, abase + n32);
+      const bf16x8 b = as_bf16x8(ld16(&dns[rloc * HP + 16 * cc + 8 * hl]));
+      acc = mfma32(a, b, acc);
+    }
+    // lane holds dphi^T[a = abase + 8 (e/4) + 4 hl + e%4][row]
+#pragma unroll
+    for (int e4 = 0; e4 < 4; ++e4) {
+      const int a0 = abase + 8 * e4 + 4 * hl;
+      const u32x2 qv = ld8(qrow + a0);
+      float r[4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const float qa = bf16_to_f32(static_cast<uint16_t>(x & 1 ? qv[x >> 1] >> 16 : qv[x >> 1] & 0xffffu));
+        const float z = lin ? zrow[a0 + x] + zrow[D + a0 + x] : 0.f;
+        const float g = acc[4 * e4 + x] + ddv * z;
+        r[x] = lin ? g * phi_prime(qa) : 0.f;
+      }
+      *reinterpret_cast<float4*>(dqrow + a0) = make_float4(r[0], r[1], r[2], r[3]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bwd_q: one workgroup per query block i; sparse part of dQ over the critical
+// key blocks, added to the linear part already in dq.
+//   S^T = K Q^T, P^T = exp2(S^T scale log2e - lse log2e), dP^T = V dO^T,
+//   dS^T = P^T (dP^T - D), dQ += scale dS K
+// Waves (kh, qh) as in the forward; dS^T's result tile is the A operand of
+// dS K directly (k index permuted), with K^T staged in LDS.
+// ---------------------------------------------------------------------------
+template <int D>
+struct BqCfg {
+  static constexpr int KP = D + 8, TP = 68;
+  static constexpr int kBuf = 2 * 64 * KP + D * TP;   // K, V (rows) and K^T
+  static constexpr int KCH = D / 32;                   // 16-byte chunks per thread per tensor
+  static constexpr int NCC = D / 16, NAT = D / 32;
+};
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void bwd_q_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ kT, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ dO, const float* __restrict__ lse,
+    const float* __restrict__ dsum, const int32_t* __restrict__ lut,
+    const int32_t* __restrict__ lut_cnt, float* __restrict__ dq, int N, int L, int T,
+    float scale) {
+  using C = BqCfg<D>;
+  constexpr int KP = C::KP, TP = C::TP;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[C::kBuf];
+  uint16_t* ks = smem;
+  uint16_t* vs = smem + 64 * KP;
+  uint16_t* kts = smem + 2 * 64 * KP;
+
+  const uint32_t wg = xcd_remap(blockIdx.x, gridDim.x);
+  const int i = wg % T;
+  const long long bh = wg / T;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int kh = wave & 1, qh = wave >> 1;
+  const int n32 = lane & 31, hl = lane >> 5;
+  const size_t head = static_cast<size_t>(bh) * N * D;
+  const int row = i * kBlock + 32 * qh + n32;
+  const bool valid = row < L;
+  const float sl2 = scale * kLog2e;
+
+  bf16x8 qf[C::NCC], dof[C::NCC];
+  {
+    const uint16_t* qr = q + head + static_cast<size_t>(row) * D + 8 * hl;
+    const uint16_t* dr = dO + head + static_cast<size_t>(row) * D + 8 * hl;
+#pragma unroll
+    for (int cc = 0; cc < C::NCC; ++cc) {
+      qf[cc] = as_bf16x8(ld16(qr + 16 * cc));
+      dof[cc] = valid ? as_bf16x8(ld16(dr + 16 * cc)) : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+    }
+  }
+  const float lse2 = valid ? lse[bh * N + row] * kLog2e : 0.f;
+  const float dsv = valid ? dsum[bh * N + row] : 0.f;
+  const int cnt = lut_cnt[bh * T + i];
+  const int32_t* lrow = lut + (bh * T + i) * static_cast<long long>(T);
+
+  f32x16 acc[C::NAT];
+#pragma unroll
+  for (int at = 0; at < C::NAT; ++at) acc[at] = f32x16{};
+
+  u32x4 rk[C::KCH], rv[C::KCH], rt[C::KCH];
+  auto load = [&](int j) {
+    const size_t off = head + static_cast<size_t>(j) * kBlock * D;
+#pragma unroll
+    for (int u = 0; u < C::KCH; ++u) {
+      const int e = tid + 256 * u;
+      rk[u] = ld16(k + off + 8 * e);
+      rv[u] = ld16(v + off + 8 * e);
+      rt[u] = ld16(kT + off + 8 * e);
+    }
+  };
+  auto store = [&]() {
+#pragma unroll
+    for (int u = 0; u < C::KCH; ++u) {
+      const int e = tid + 256 * u;
+      st16(ks + (e / (D / 8)) * KP + 8 * (e % (D / 8)), rk[u]);
+      st16(vs + (e / (D / 8)) * KP + 8 * (e % (D / 8)), rv[u]);
+      uint16_t* td = kts + (e >> 3) * TP + 8 * (e & 7);
+      st8(td, u32x2{rt[u][0], rt[u][1]});
+      st8(td + 4, u32x2{rt[u][2], rt[u][3]});
+    }
+  };
+
+  if (cnt > 0) load(lrow[0]);
+  for (int n = 0; n < cnt; ++n) {
+    const int j = lrow[n];
+    __syncthreads();   // previous block's LDS reads are done
+    store();
+    __syncthreads();
+    if (n + 1 < cnt) load(lrow[n + 1]);
+    f32x16 st = {}, dpt = {};
+#pragma unroll
+    for (int cc = 0; cc < C::NCC; ++cc) {
+      st = mfma32(as_bf16x8(ld16(ks + (32 * kh + n32) * KP + 16 * cc + 8 * hl)), qf[cc], st);
+      dpt = mfma32(as_bf16x8(ld16(vs + (32 * kh + n32) * KP + 16 * cc + 8 * hl)), dof[cc], dpt);
+    }
+    const bool tail = (j + 1) * kBlock > L;
+    bf16x8 ds[2];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      float p = __builtin_amdgcn_exp2f(__fmaf_rn(st[e], sl2, -lse2));
+      if (tail) {
+        const int key = j * kBlock + 32 * kh + 8 * (e / 4) + 4 * hl + (e % 4);
+        if (key >= L) p = 0.f;
+      }
+      if (!valid) p = 0.f;
+      ds[e >> 3][e & 7] = static_cast<__bf16>(p != 0.f ? p * (dpt[e] - dsv) : 0.f);
+    }
+    // dQ[q][a] += dS[q][keys] K[keys][a]: B operand K^T[a][keys of chunk h]
+#pragma unroll
+    for (int at = 0; at < C::NAT; ++at) {
+      const uint16_t* tr = kts + (32 * at + n32) * TP + 32 * kh + 4 * hl;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        acc[at] = mfma32(ds[h], as_bf16x8(ld8(tr + 16 * h), ld8(tr + 16 * h + 8)), acc[at]);
+    }
+  }
+  // merge the key halves and add the linear part
+  __syncthreads();
+  float* ex = reinterpret_cast<float*>(smem);   // [qh][NAT*16][64]
+  constexpr int NACC = C::NAT * 16;
+  if (kh == 1) {
+#pragma unroll
+    for (int at = 0; at < C::NAT; ++at)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) ex[(qh * NACC + at * 16 + e) * 64 + lane] = acc[at][e];
+  }
+  __syncthreads();
+  if (kh == 0) {
+    // lane holds dQ[q = 32 qh + 8 (e/4) + 4 hl + e%4][a = 32 at + n32]
+#pragma unroll
+    for (int at = 0; at < C::NAT; ++at)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int qr = i * kBlock + 32 * qh + 8 * (e / 4) + 4 * hl + (e % 4);
+        float* p = dq + head + static_cast<size_t>(qr) * D + 32 * at + n32;
+        const float sparse = scale * (acc[at][e] + ex[(qh * NACC + at * 16 + e) * 64 + lane]);
+        *p = qr < L ? *p + sparse : 0.f;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bwd_kv: one workgroup per key block j; loops over the query blocks for which
+// j is critical (column list), then adds the linear-branch gradients.
+// Wave (kh, qh): keys 32 kh .. 32 kh + 31 of the block, queries 32 qh .. of
+// each query block.  S = Q K^T and dP = dO V^T take K_j, V_j from registers;
+// dV += P^T dO and dK += dS^T Q take P, dS straight from the S / dP result
+// tiles (k index permuted) with dO^T and Q^T staged in LDS.
+// ---------------------------------------------------------------------------
+template <int D>
+struct BkvCfg {
+  static constexpr int RP = D + 8, TP = 68;
+  static constexpr int kBuf = 2 * 64 * RP + 2 * D * TP;   // Q, dO rows; Q^T, dO^T
+  static constexpr int KCH = D / 32;
+  static constexpr int NCC = D / 16, NCT = D / 32;
+  static constexpr int kLds = (2 * kBuf * 2 + 2 * 64 * 4 * 2 > D * (D + 8) * 2 + 2 * 2 * 32 * D * 4)
+                                  ? 2 * kBuf * 2 + 2 * 64 * 4 * 2
+                                  : D * (D + 8) * 2 + 2 * 2 * 32 * D * 4;
+};
+
+template <int D>
+__global__ __launch_bounds__(256, 1) void bwd_kv_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ qT,
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ dO, const uint16_t* __restrict__ doT,
+    const float* __restrict__ lse, const float* __restrict__ dsum,
+    const int32_t* __restrict__ col, const int32_t* __restrict__ col_cnt,
+    const uint16_t* __restrict__ dh, const float* __restrict__ dz, bool linear,
+    float* __restrict__ dk, float* __restrict__ dv, int N, int L, int T, float scale) {
+  using C = BkvCfg<D>;
+  constexpr int RP = C::RP, TP = C::TP;
+  __shared__ __attribute__((aligned(16))) uint8_t smem_raw[C::kLds];
+  uint16_t* smem = reinterpret_cast<uint16_t*>(smem_raw);
+  float* lses = reinterpret_cast<float*>(smem_raw + 2 * C::kBuf * 2);   // [buf][64]
+  float* dss = lses + 128;                                              // [buf][64]
+
+  const uint32_t wg = xcd_remap(blockIdx.x, gridDim.x);
+  const int j = wg % T;
+  const long long bh = wg / T;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int kh = wave & 1, qh = wave >> 1;
+  const int n32 = lane & 31, hl = lane >> 5;
+  const size_t head = static_cast<size_t>(bh) * N * D;
+  const int key = j * kBlock + 32 * kh + n32;   // this lane's key (B operand column)
+  const float sl2 = scale * kLog2e;
+
+  // K_j, V_j as B operands (k = head-dim index 16 cc + 8 hl + s)
+  bf16x8 kf[C::NCC], vf[C::NCC];
+  {
+    const uint16_t* kr = k + head + static_cast<size_t>(key) * D + 8 * hl;
+    const uint16_t* vr = v + head + static_cast<size_t>(key) * D + 8 * hl;
+#pragma unroll
+    for (int cc = 0; cc < C::NCC; ++cc) {
+      kf[cc] = as_bf16x8(ld16(kr + 16 * cc));
+      vf[cc] = as_bf16x8(ld16(vr + 16 * cc));
+    }
+  }
+  const int cnt = col_cnt[bh * T + j];
+  const int32_t* crow = col + (bh * T + j) * static_cast<long long>(T);
+
+  f32x16 adv[C::NCT], adk[C::NCT];
+#pragma unroll
+  for (int ct = 0; ct < C::NCT; ++ct) {
+    adv[ct] = f32x16{};
+    adk[ct] = f32x16{};
+  }
+
+  u32x4 r_q[C::KCH], r_d[C::KCH], r_qt[C::KCH], r_dt[C::KCH];
+  float r_l = 0.f, r_s = 0.f;
+  auto load = [&](int ib) {
+    const size_t off = head + static_cast<size_t>(ib) * kBlock * D;
+#pragma unroll
+    for (int u = 0; u < C::KCH; ++u) {
+      const int e = tid + 256 * u;
+      r_q[u] = ld16(q + off + 8 * e);
+      r_d[u] = ld16(dO + off + 8 * e);
+      r_qt[u] = ld16(qT + off + 8 * e);
+      r_dt[u] = ld16(doT + off + 8 * e);
+    }
+    if (tid < kBlock) {
+      const int rr = ib * kBlock + tid;
+      r_l = rr < L ? lse[bh * N + rr] * kLog2e : INFINITY;
+      r_s = rr < L ? dsum[bh * N + rr] : 0.f;
+    }
+  };
+  auto store = [&](int buf) {
+    uint16_t* qs = smem + buf * C::kBuf;
+    uint16_t* ds_ = qs + 64 * RP;
+    uint16_t* qts = qs + 2 * 64 * RP;
+    uint16_t* dts = qts + D * TP;
+#pragma unroll
+    for (int u = 0; u < C::KCH; ++u) {
+      const int e = tid + 256 * u;
+      const int rr = e / (D / 8), cc8 = 8 * (e % (D / 8));
+      st16(qs + rr * RP + cc8, r_q[u]);
+      st16(ds_ + rr * RP + cc8, r_d[u]);
+      uint16_t* t1 = qts + (e >> 3) * TP + 8 * (e & 7);
+      uint16_t* t2 = dts + (e >> 3) * TP + 8 * (e & 7);
+      st8(t1, u32x2{r_qt[u][0], r_qt[u][1]});
+      st8(t1 + 4, u32x2{r_qt[u][2], r_qt[u][3]});
+      st8(t2, u32x2{r_dt[u][0], r_dt[u][1]});
+      st8(t2 + 4, u32x2{r_dt[u][2], r_dt[u][3]});
+    }
+    if (tid < kBlock) {
+      lses[buf * 64 + tid] = r_l;
+      dss[buf * 64 + tid] = r_s;
+    }
+  };
+
+  if (cnt > 0) {
+    load(crow[0]);
+    store(0);
+    __syncthreads();
+  }
+  const bool tail = (j + 1) * kBlock > L;
+  for (int n = 0; n < cnt; ++n) {
+    const int buf = n & 1;
+    if (n + 1 < cnt) load(crow[n + 1]);
+    const uint16_t* qs = smem + buf * C::kBuf;
+    const uint16_t* ds_ = qs + 64 * RP;
+    const uint16_t* qts = qs + 2 * 64 * RP;
+    const uint16_t* dts = qts + D * TP;
+    f32x16 s = {}, dp = {};
+#pragma unroll
+    for (int cc = 0; cc < C::NCC; ++cc) {
+      s = mfma32(as_bf16x8(ld16(qs + (32 * qh + n32) * RP + 16 * cc + 8 * hl)), kf[cc], s);
+      dp = mfma32(as_bf16x8(ld16(ds_ + (32 * qh + n32) * RP + 16 * cc + 8 * hl)), vf[cc], dp);
+    }
+    // lane holds S[q = 32 qh + 8 (e/4) + 4 hl + e%4][key]
+    bf16x8 pb[2], sb[2];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int qq = 32 * qh + 8 * (e / 4) + 4 * hl + (e % 4);
+      const float l2 = lses[buf * 64 + qq];
+      float p = __builtin_amdgcn_exp2f(__fmaf_rn(s[e], sl2, -l2));
+      if ((tail && key >= L) || l2 == INFINITY) p = 0.f;
+      pb[e >> 3][e & 7] = static_cast<__bf16>(p);
+      sb[e >> 3][e & 7] = static_cast<__bf16>(p != 0.f ? p * (dp[e] - dss[buf * 64 + qq]) : 0.f);
+    }
+    // dV[key][c] += P^T dO, dK[key][a] += dS^T Q; B operands from dO^T / Q^T rows
+#pragma unroll
+    for (int ct = 0; ct < C::NCT; ++ct) {
+      const uint16_t* dtr = dts + (32 * ct + n32) * TP + 32 * qh + 4 * hl;
+      const uint16_t* qtr = qts + (32 * ct + n32) * TP + 32 * qh + 4 * hl;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        adv[ct] = mfma32(pb[h], as_bf16x8(ld8(dtr + 16 * h), ld8(dtr + 16 * h + 8)), adv[ct]);
+        adk[ct] = mfma32(sb[h], as_bf16x8(ld8(qtr + 16 * h), ld8(qtr + 16 * h + 8)), adk[ct]);
+      }
+    }
+    if (n + 1 < cnt) store(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- merge the query halves; lane holds X[key = 32 kh + 8 (e/4) + 4 hl + e%4][c = 32 ct + n32]
+  __syncthreads();
+  float* ex = reinterpret_cast<float*>(smem_raw + D * (D + 8) * 2);   // [kh][2][NCT*16][64]
+  constexpr int NACC = C::NCT * 16;
+  if (qh == 1) {
+#pragma unroll
+    for (int ct = 0; ct < C::NCT; ++ct)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        ex[((kh * 2 + 0) * NACC + ct * 16 + e) * 64 + lane] = adv[ct][e];
+        ex[((kh * 2 + 1) * NACC + ct * 16 + e) * 64 + lane] = adk[ct][e];
+      }
+  }
+  // stage dh^T[c][a] of this key block for the linear part
+  uint16_t* dhs = smem;
+  constexpr int HP = D + 8;
+  if (linear) {
+    const uint16_t* src = dh + (static_cast<size_t>(bh) * T + j) * D * D;
+    for (int e = tid; e < D * D / 8; e += 256) {
+      const int c = e / (D / 8), a8 = e % (D / 8);
+      st16(&dhs[c * HP + 8 * a8], ld16(src + static_cast<size_t>(c) * D + 8 * a8));
+    }
+  }
+  __syncthreads();
+  if (qh == 1) return;
+#pragma unroll
+  for (int ct = 0; ct < C::NCT; ++ct)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      adv[ct][e] += ex[((kh * 2 + 0) * NACC + ct * 16 + e) * 64 + lane];
+      adk[ct][e] = scale * (adk[ct][e] + ex[((kh * 2 + 1) * NACC + ct * 16 + e) * 64 + lane]);
+    }
+  if (linear) {
+    // rows t of this wave: A operands phi(K_j)[t][a] and V_j[t][c] (k = 16 cc + 8 hl + s)
+    const int t = j * kBlock + 32 * kh + n32;
+    const uint16_t* kr = k + head + static_cast<size_t>(t) * D + 8 * hl;
+    const uint16_t* vr = v + head + static_cast<size_t>(t) * D + 8 * hl;
+    const bool tv = t < L;
+    bf16x8 pkf[C::NCC], vrf[C::NCC];
+#pragma unroll
+    for (int cc = 0; cc < C::NCC; ++cc) {
+      const u32x4 kv = ld16(kr + 16 * cc);
+#pragma unroll
+      for (int s2 = 0; s2 < 8; ++s2)
+        pkf[cc][s2] = static_cast<__bf16>(tv ? phi(bf16_to_f32(static_cast<uint16_t>(u4_elem(kv, s2)))) : 0.f);
+      vrf[cc] = as_bf16x8(ld16(vr + 16 * cc));
+    }
+    const float* dzr = dz + (static_cast<size_t>(bh) * T + j) * 2 * D;
+#pragma unroll
+    for (int ct = 0; ct < C::NCT; ++ct) {
+      // dV_lin[t][c] = sum_a phi(K)[t][a] dh[a][c]: B = dh^T[c][a .. a + 7] (row of dh^T)
+      f32x16 lv = {}, lk = {};
+#pragma unroll
+      for (int cc = 0; cc < C::NCC; ++cc) {
+        lv = mfma32(pkf[cc], as_bf16x8(ld16(&dhs[(32 * ct + n32) * HP + 16 * cc + 8 * hl])), lv);
+        // dphi(K)[t][a] = sum_c V[t][c] dh[a][c]: B = dh^T[c .. c + 7][a] (column of dh^T)
+        lk = mfma32(vrf[cc], lds_col8(dhs, HP, 16 * cc + 8 * hl, 32 * ct + n32), lk);
+      }
+      // lane holds X[t = 32 kh + 8 (e/4) + 4 hl + e%4][n = 32 ct + n32]
+      const int a = 32 * ct + n32;
+      const float dza = dzr[a] + dzr[D + a];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int tt = j * kBlock + 32 * kh + 8 * (e / 4) + 4 * hl + (e % 4);
+        const float kv = tt < L ? bf16_to_f32(k[head + static_cast<size_t>(tt) * D + a]) : 0.f;
+        adv[ct][e] += lv[e];
+        adk[ct][e] += (lk[e] + dza) * phi_prime(kv);
+      }
+    }
+  }
+#pragma unroll
+  for (int ct = 0; ct < C::NCT; ++ct)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int tt = j * kBlock + 32 * kh + 8 * (e / 4) + 4 * hl + (e % 4);
+      const size_t off = head + static_cast<size_t>(tt) * D + 32 * ct + n32;
+      dv[off] = tt < L ? adv[ct][e] : 0.f;
+      dk[off] = tt < L ? adk[ct][e] : 0.f;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dW: partial sums over chunks of 64-row blocks, dW^T[c][o] = sum_r Y[r][c] dO[r][o]
+// (A = Y^T staged by transposing in LDS, B = dO^T tile), then a fixed-order
+// reduction of the partials.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void dw_part_kernel(const uint16_t* __restrict__ y,
+                                                      const uint16_t* __restrict__ doT,
+                                                      float* __restrict__ part,
+                                                      long long nblocks, int parts) {
+  constexpr int P = 72;
+  constexpr int TILES = (D / 32) * (D / 32);
+  constexpr int TPW = TILES / 4;
+  __shared__ __attribute__((aligned(16))) uint16_t yt[D * P];
+  __shared__ __attribute__((aligned(16))) uint16_t dt[D * P];
+  const int w = blockIdx.x;
+  const long long b0 = nblocks * w / parts, b1 = nblocks * (w + 1) / parts;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n32 = lane & 31, hl = lane >> 5;
+  f32x16 acc[TPW];
+#pragma unroll
+  for (int x = 0; x < TPW; ++x) acc[x] = f32x16{};
+  for (long long b = b0; b < b1; ++b) {
+    const uint16_t* ysrc = y + static_cast<size_t>(b) * kBlock * D;
+    const uint16_t* dsrc = doT + static_cast<size_t>(b) * kBlock * D;
+    __syncthreads();
+    for (int e = tid; e < kBlock * D / 8; e += 256) {
+      const int t = e / (D / 8), c8 = e % (D / 8);
+      const u32x4 val = ld16(ysrc + static_cast<size_t>(t) * D + 8 * c8);
+#pragma unroll
+      for (int s = 0; s < 8; ++s) yt[(8 * c8 + s) * P + t] = static_cast<uint16_t>(u4_elem(val, s));
+      const int r = e >> 3, m = e & 7;
+      st16(&dt[r * P + 8 * m], ld16(dsrc + static_cast<size_t>(r) * kBlock + 8 * m));
+    }
+    __syncthreads();
+#pragma unroll
+    for (int x = 0; x < TPW; ++x) {
+      const int tt = wave * TPW + x;
+      const int ct = tt / (D / 32), ot = tt % (D / 32);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        acc[x] = mfma32(as_bf16x8(ld16(&yt[(32 * ct + n32) * P + 16 * kk + 8 * hl])),
+                        as_bf16x8(ld16(&dt[(32 * ot + n32) * P + 16 * kk + 8 * hl])), acc[x]);
+    }
+  }
+  float* out = part + static_cast<size_t>(w) * D * D;
+#pragma unroll
+  for (int x = 0; x < TPW; ++x) {
+    const int tt = wave * TPW + x;
+    const int ct = tt / (D / 32), ot = tt % (D / 32);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int c = 32 * ct + 8 * (e / 4) + 4 * hl + (e % 4);
+      const int o = 32 * ot + n32;
+      out[static_cast<size_t>(o) * D + c] = acc[x][e];   // dW[o][c]
+    }
+  }
+}
+
+__global__ void dw_reduce_kernel(const float* __restrict__ part, float* __restrict__ dw, int DD,
+                                 int parts) {
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= DD) return;
+  float s = 0.f;
+  for (int p = 0; p < parts; ++p) s += part[static_cast<size_t>(p) * DD + e];
+  dw[e] = s;
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+hipError_t launch_w_transpose(const Dims& d, const uint16_t* w, uint16_t* wT, hipStream_t s) {
+  hipLaunchKernelGGL(w_transpose_kernel, dim3((d.D * d.D + 255) / 256), dim3(256), 0, s, w, wT, d.D);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_prep(const Dims& d, const uint16_t* q, const uint16_t* o,
+                           const uint16_t* dO, const uint16_t* wT, const float* den,
+                           const uint16_t* y, const uint16_t* hst, const float* zst, bool linear,
+                           float* dsum, float* ddel, uint16_t* dn, float* dq, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(d.BH() * d.T));
+  if (d.D == 128)
+    hipLaunchKernelGGL(bwd_prep_kernel<128>, grid, dim3(256), 0, s, q, o, dO, wT, den, y, hst, zst,
+                       dsum, ddel, dn, dq, d.N, d.L, d.T, linear);
+  else
+    hipLaunchKernelGGL(bwd_prep_kernel<64>, grid, dim3(256), 0, s, q, o, dO, wT, den, y, hst, zst,
+                       dsum, ddel, dn, dq, d.N, d.L, d.T, linear);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_q(const Dims& d, const uint16_t* q, const uint16_t* k, const uint16_t* kT,
+                        const uint16_t* v, const uint16_t* dO, const float* lse,
+                        const float* dsum, const int32_t* lut, const int32_t* lut_cnt, float* dq,
+                        hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(d.BH() * d.T));
+  if (d.D == 128)
+    hipLaunchKernelGGL(bwd_q_kernel<128>, grid, dim3(256), 0, s, q, k, kT, v, dO, lse, dsum, lut,
+                       lut_cnt, dq, d.N, d.L, d.T, d.scale);
+  else
+    hipLaunchKernelGGL(bwd_q_kernel<64>, grid, dim3(256), 0, s, q, k, kT, v, dO, lse, dsum, lut,
+                       lut_cnt, dq, d.N, d.L, d.T, d.scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_kv(const Dims& d, const uint16_t* q, const uint16_t* qT, const uint16_t* k,
+                         const uint16_t* v, const uint16_t* dO, const uint16_t* doT,
+                         const float* lse, const float* dsum, const int32_t* col,
+                         const int32_t* col_cnt, const uint16_t* dh, const float* dz, bool linear,
+                         float* dk, float* dv, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(d.BH() * d.T));
+  if (d.D == 128)
+    hipLaunchKernelGGL(bwd_kv_kernel<128>, grid, dim3(256), 0, s, q, qT, k, v, dO, doT, lse, dsum,
+                       col, col_cnt, dh, dz, linear, dk, dv, d.N, d.L, d.T, d.scale);
+  else
+    hipLaunchKernelGGL(bwd_kv_kernel<64>, grid, dim3(256), 0, s, q, qT, k, v, dO, doT, lse, dsum,
+                       col, col_cnt, dh, dz, linear, dk, dv, d.N, d.L, d.T, d.scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_dw(const Dims& d, const uint16_t* y, const uint16_t* doT, float* part, float* dw,
+                     hipStream_t s) {
+  const long long nblocks = d.BH() * d.T;
+  const int parts = static_cast<int>(std::min<long long>(kDwParts, nblocks));
+  if (d.D == 128)
+    hipLaunchKernelGGL(dw_part_kernel<128>, dim3(parts), dim3(256), 0, s, y, doT, part, nblocks, parts);
+  else
+    hipLaunchKernelGGL(dw_part_kernel<64>, dim3(parts), dim3(256), 0, s, y, doT, part, nblocks, parts);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int dd = d.D * d.D;
+  hipLaunchKernelGGL(dw_reduce_kernel, dim3((dd + 255) / 256), dim3(256), 0, s, part, dw, dd, parts);
+  return hipGetLastError();
+}
+
+}  // namespace sla

@@ -35,27 +35,34 @@ struct KvCfg {
   static constexpr int kThreads = D * 4;               // one (row pair, 8 columns) unit each
   static constexpr int kWaves = kThreads / 64;
   static constexpr int kTiles = (D / 32) * (D / 32);   // 32x32 tiles of h^T
-  static constexpr int kTilesPerWave = kTiles / kWaves;
+  static constexpr int kTileGroups = kTiles / kWaves;  // workgroups per 8-block group (1 tile per wave)
   static constexpr int kPitch = 72;                    // LDS row pitch (bf16): 64 tokens + pad
 };
 
-template <int D>
+// BWD = true turns the same kernel into the backward's query-side state
+// builder: Y = Q, X = dN (bf16 rows), and the vector part is weighted,
+// dZ_i[a] = sum_r d_r * phi(q_r)[a] with the per-row weights d_r; no pooled
+// mean and no V^T are written then.
+template <int D, bool BWD>
 __global__ __launch_bounds__(KvCfg<D>::kThreads) void kv_state_kernel(
-    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, float* __restrict__ kbar,
-    uint16_t* __restrict__ states, uint16_t* __restrict__ vT, int N, int L, int T, int Tp) {
+    const uint16_t* __restrict__ ysrc, const uint16_t* __restrict__ xsrc,
+    const float* __restrict__ wrow, float* __restrict__ kbar, uint16_t* __restrict__ states,
+    uint16_t* __restrict__ vT, int N, int L, int T, int Tp) {
   using C = KvCfg<D>;
   constexpr int P = C::kPitch;
-  constexpr int TPW = C::kTilesPerWave;
   constexpr int NB = D * D + 2 * D;
-  __shared__ uint16_t pk[D * P];   // phi(K)^T, bf16
-  __shared__ uint16_t vt[D * P];   // V^T
-  __shared__ uint16_t kt[D * P];   // K^T (raw, for the pooled mean)
+  __shared__ uint16_t pk[D * P];   // phi(Y)^T, bf16
+  __shared__ uint16_t vt[D * P];   // X^T
+  __shared__ uint16_t kt[D * P];   // Y^T (raw, for the pooled mean)
   __shared__ uint16_t zst[2 * D * 8];
+  __shared__ float wts[kBlock];
 
   const int groups = Tp / 8;
   const uint32_t wg = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = wg / groups;
-  const int g = wg % groups;
+  const int tgrp = wg % C::kTileGroups;      // which tiles of h^T this workgroup computes
+  const int bh = (wg / C::kTileGroups) / groups;
+  const int g = (wg / C::kTileGroups) % groups;
+  const bool lead = tgrp == 0;               // writes V^T, kbar and z
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -74,8 +81,8 @@ __global__ __launch_bounds__(KvCfg<D>::kThreads) void kv_state_kernel(
       const int tok = j * kBlock + 2 * rp + r;
       if (j < T && tok < L) {
         const size_t off = head + static_cast<size_t>(tok) * D + 8 * c8;
-        rk[r] = ld16(k + off);
-        rv[r] = ld16(v + off);
+        rk[r] = ld16(ysrc + off);
+        rv[r] = ld16(xsrc + off);
       } else {
         rk[r] = u32x4{0u, 0u, 0u, 0u};
         rv[r] = u32x4{0u, 0u, 0u, 0u};
@@ -83,12 +90,14 @@ __global__ __launch_bounds__(KvCfg<D>::kThreads) void kv_state_kernel(
     }
   };
 
-  uint32_t stash[TPW][16][4];   // bf16 pairs of (block 2p, block 2p+1) per result entry
+  const int tt = tgrp * C::kWaves + wave;    // this wave's 32x32 tile of h^T
+  const int ct = tt / (D / 32), at = tt % (D / 32);
+  uint32_t stash[16][4];   // bf16 pairs of (block 2p, block 2p+1) per result entry
   load(g * 8);
 #pragma unroll
   for (int jj = 0; jj < 8; ++jj) {
     const int j = g * 8 + jj;
-    // transpose the staged rows into LDS; invalid tokens are zero in K^T, V^T and phi(K)^T
+    // transpose the staged rows into LDS; invalid tokens are zero in all three
     {
       const int tok0 = j * kBlock + 2 * rp;
       const bool ok0 = j < T && tok0 < L, ok1 = j < T && tok0 + 1 < L;
@@ -96,28 +105,33 @@ __global__ __launch_bounds__(KvCfg<D>::kThreads) void kv_state_kernel(
       for (int s = 0; s < 8; ++s) {
         const int row = (8 * c8 + s) * P + 2 * rp;
         const uint32_t k0 = u4_elem(rk[0], s), k1 = u4_elem(rk[1], s);
-        *reinterpret_cast<uint32_t*>(&kt[row]) = k0 | (k1 << 16);
+        if constexpr (!BWD) *reinterpret_cast<uint32_t*>(&kt[row]) = k0 | (k1 << 16);
         *reinterpret_cast<uint32_t*>(&vt[row]) = u4_elem(rv[0], s) | (u4_elem(rv[1], s) << 16);
         const float p0 = ok0 ? phi(bf16_to_f32(static_cast<uint16_t>(k0))) : 0.f;
         const float p1 = ok1 ? phi(bf16_to_f32(static_cast<uint16_t>(k1))) : 0.f;
         *reinterpret_cast<uint32_t*>(&pk[row]) = pack_bf16x2(p0, p1);
       }
+      if constexpr (BWD) {
+        if (lead && tid < kBlock) {
+          const int tok = j * kBlock + tid;
+          wts[tid] = (j < T && tok < L) ? wrow[static_cast<size_t>(bh) * N + tok] : 0.f;
+        }
+      }
     }
     __syncthreads();
     if (jj < 7) load(j + 1);
-    if (j < T) {
-      // V^T of this key block: D rows of 64 tokens, 8 chunks of 16 bytes per row
-      uint16_t* dst = vT + (static_cast<size_t>(bh) * T + j) * D * kBlock;
-      for (int e = tid; e < D * 8; e += C::kThreads) {
-        const int c = e >> 3, m = e & 7;
-        st16(dst + c * kBlock + 8 * m, ld16(&vt[c * P + 8 * m]));
+    if constexpr (!BWD) {
+      if (lead && j < T) {
+        // V^T of this key block: D rows of 64 tokens, 8 chunks of 16 bytes per row
+        uint16_t* dst = vT + (static_cast<size_t>(bh) * T + j) * D * kBlock;
+        for (int e = tid; e < D * 8; e += C::kThreads) {
+          const int c = e >> 3, m = e & 7;
+          st16(dst + c * kBlock + 8 * m, ld16(&vt[c * P + 8 * m]));
+        }
       }
     }
 
-#pragma unroll
-    for (int x = 0; x < TPW; ++x) {
-      const int tt = wave * TPW + x;
-      const int ct = tt / (D / 32), at = tt % (D / 32);
+    {
       f32x16 acc = {};
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
@@ -128,24 +142,30 @@ __global__ __launch_bounds__(KvCfg<D>::kThreads) void kv_state_kernel(
       for (int i = 0; i < 16; ++i) {
         const uint32_t hb = f32_to_bf16(acc[i]);
         if (jj & 1)
-          stash[x][i][jj >> 1] |= hb << 16;
+          stash[i][jj >> 1] |= hb << 16;
         else
-          stash[x][i][jj >> 1] = hb;
+          stash[i][jj >> 1] = hb;
       }
     }
-    if (tid < D) {
+    if (lead && tid < D) {
       const int a = tid;
       float zs = 0.f, ks = 0.f;
       for (int t = 0; t < kBlock; ++t) {
-        zs += bf16_to_f32(pk[a * P + t]);
-        ks += bf16_to_f32(kt[a * P + t]);
+        if constexpr (BWD) {
+          zs = __fmaf_rn(wts[t], bf16_to_f32(pk[a * P + t]), zs);
+        } else {
+          zs += bf16_to_f32(pk[a * P + t]);
+          ks += bf16_to_f32(kt[a * P + t]);
+        }
       }
       const uint16_t zh = f32_to_bf16(zs);
       zst[a * 8 + jj] = zh;
       zst[(D + a) * 8 + jj] = f32_to_bf16(zs - bf16_to_f32(zh));
-      if (j < T) {
-        const int nvalid = min(kBlock, L - j * kBlock);
-        kbar[(static_cast<size_t>(bh) * T + j) * D + a] = ks / static_cast<float>(nvalid);
+      if constexpr (!BWD) {
+        if (j < T) {
+          const int nvalid = min(kBlock, L - j * kBlock);
+          kbar[(static_cast<size_t>(bh) * T + j) * D + a] = ks / static_cast<float>(nvalid);
+        }
       }
     }
     __syncthreads();
@@ -153,17 +173,13 @@ __global__ __launch_bounds__(KvCfg<D>::kThreads) void kv_state_kernel(
 
   uint16_t* out = states + (static_cast<size_t>(bh) * groups + g) * NB * 8;
 #pragma unroll
-  for (int x = 0; x < TPW; ++x) {
-    const int tt = wave * TPW + x;
-    const int ct = tt / (D / 32), at = tt % (D / 32);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int c = 32 * ct + 8 * (i / 4) + 4 * hl + (i % 4);
-      const int a = 32 * at + n32;
-      st16(out + (static_cast<size_t>(c) * D + a) * 8,
-           u32x4{stash[x][i][0], stash[x][i][1], stash[x][i][2], stash[x][i][3]});
-    }
+  for (int i = 0; i < 16; ++i) {
+    const int c = 32 * ct + 8 * (i / 4) + 4 * hl + (i % 4);
+    const int a = 32 * at + n32;
+    st16(out + (static_cast<size_t>(c) * D + a) * 8,
+         u32x4{stash[i][0], stash[i][1], stash[i][2], stash[i][3]});
   }
+  if (!lead) return;
   for (int e = tid; e < 2 * D; e += C::kThreads)
     st16(out + (static_cast<size_t>(D) * D + e) * 8, ld16(&zst[e * 8]));
 }
@@ -415,13 +431,25 @@ __global__ void fill_mask_kernel(int8_t* __restrict__ mask, long long n, int8_t 
 // ---------------------------------------------------------------------------
 hipError_t launch_kv_state(const Dims& d, const uint16_t* k, const uint16_t* v, float* kbar,
                            uint16_t* states, uint16_t* vT, hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>(d.BH() * (d.Tp / 8)));
+  const dim3 grid(static_cast<unsigned>(d.BH() * (d.Tp / 8) * KvCfg<128>::kTileGroups / (d.D == 128 ? 1 : KvCfg<128>::kTileGroups)));
   if (d.D == 128)
-    hipLaunchKernelGGL(kv_state_kernel<128>, grid, dim3(KvCfg<128>::kThreads), 0, s, k, v, kbar,
-                       states, vT, d.N, d.L, d.T, d.Tp);
+    hipLaunchKernelGGL((kv_state_kernel<128, false>), grid, dim3(KvCfg<128>::kThreads), 0, s, k, v,
+                       nullptr, kbar, states, vT, d.N, d.L, d.T, d.Tp);
   else
-    hipLaunchKernelGGL(kv_state_kernel<64>, grid, dim3(KvCfg<64>::kThreads), 0, s, k, v, kbar,
-                       states, vT, d.N, d.L, d.T, d.Tp);
+    hipLaunchKernelGGL((kv_state_kernel<64, false>), grid, dim3(KvCfg<64>::kThreads), 0, s, k, v,
+                       nullptr, kbar, states, vT, d.N, d.L, d.T, d.Tp);
+  return hipGetLastError();
+}
+
+hipError_t launch_dstate(const Dims& d, const uint16_t* q, const uint16_t* dn, const float* ddel,
+                         uint16_t* states, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(d.BH() * (d.Tp / 8) * KvCfg<128>::kTileGroups / (d.D == 128 ? 1 : KvCfg<128>::kTileGroups)));
+  if (d.D == 128)
+    hipLaunchKernelGGL((kv_state_kernel<128, true>), grid, dim3(KvCfg<128>::kThreads), 0, s, q, dn,
+                       ddel, nullptr, states, nullptr, d.N, d.L, d.T, d.Tp);
+  else
+    hipLaunchKernelGGL((kv_state_kernel<64, true>), grid, dim3(KvCfg<64>::kThreads), 0, s, q, dn,
+                       ddel, nullptr, states, nullptr, d.N, d.L, d.T, d.Tp);
   return hipGetLastError();
 }
 

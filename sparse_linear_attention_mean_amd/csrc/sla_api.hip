@@ -144,6 +144,12 @@ WorkspaceLayout workspace_layout(const Dims& d) {
   w.dstate = take(BH * d.T * d.D * d.D * 2);
   w.dstate_z = take(BH * d.T * 2 * d.D * 4);
   w.dsum = take(BH * d.N * 4);
+  w.ddel = take(BH * d.N * 4);
+  w.dn = take(BH * d.N * d.D * 2);
+  w.kT = take(BH * d.N * d.D * 2);
+  w.qT = take(BH * d.N * d.D * 2);
+  w.doT = take(BH * d.N * d.D * 2);
+  w.wT = take(static_cast<size_t>(d.D) * d.D * 2);
   w.dw_part = take(static_cast<size_t>(kDwParts) * d.D * d.D * 4);
   w.total = off;
   return w;
@@ -319,8 +325,68 @@ sla_status sla_backward(const sla_config* cfg, const void* q, const void* k, con
   if (workspace_bytes < wl.total)
     return fail(SLA_ERR_WORKSPACE, "workspace of %zu bytes is below the required %zu",
                 workspace_bytes, wl.total);
-  (void)stream;
-  return fail(SLA_ERR_UNSUPPORTED, "backward not built yet");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Stages stg{static_cast<hipEvent_t*>(cfg->stage_events), s};
+  const SavedLayout sl = saved_layout(d);
+  char* ws = static_cast<char*>(workspace);
+  const char* sv = static_cast<const char*>(saved);
+  auto* lut = reinterpret_cast<int32_t*>(ws + wl.lut);
+  auto* lut_cnt = reinterpret_cast<int32_t*>(ws + wl.lut_cnt);
+  auto* col = reinterpret_cast<int32_t*>(ws + wl.col);
+  auto* col_cnt = reinterpret_cast<int32_t*>(ws + wl.col_cnt);
+  auto* rbits = reinterpret_cast<uint32_t*>(ws + wl.rbits);
+  auto* cbits = reinterpret_cast<uint32_t*>(ws + wl.cbits);
+  auto* states = reinterpret_cast<uint16_t*>(ws + wl.states);
+  auto* dh = reinterpret_cast<uint16_t*>(ws + wl.dstate);
+  auto* dz = reinterpret_cast<float*>(ws + wl.dstate_z);
+  auto* dsum = reinterpret_cast<float*>(ws + wl.dsum);
+  auto* ddel = reinterpret_cast<float*>(ws + wl.ddel);
+  auto* dn = reinterpret_cast<uint16_t*>(ws + wl.dn);
+  auto* kT = reinterpret_cast<uint16_t*>(ws + wl.kT);
+  auto* qT = reinterpret_cast<uint16_t*>(ws + wl.qT);
+  auto* doT = reinterpret_cast<uint16_t*>(ws + wl.doT);
+  auto* wT = reinterpret_cast<uint16_t*>(ws + wl.wT);
+  auto* dwp = reinterpret_cast<float*>(ws + wl.dw_part);
+  const auto* q16 = static_cast<const uint16_t*>(q);
+  const auto* k16 = static_cast<const uint16_t*>(k);
+  const auto* v16 = static_cast<const uint16_t*>(v);
+  const auto* o16 = static_cast<const uint16_t*>(o);
+  const auto* do16 = static_cast<const uint16_t*>(d_o);
+  const auto* lse = reinterpret_cast<const float*>(sv + sl.lse);
+  const auto* den = reinterpret_cast<const float*>(sv + sl.den);
+  const auto* y = reinterpret_cast<const uint16_t*>(sv + sl.y);
+  const auto* hst = reinterpret_cast<const uint16_t*>(sv + sl.hst);
+  const auto* zst = reinterpret_cast<const float*>(sv + sl.zst);
+  // the forward ran its linear branch exactly when this holds (same config)
+  const bool given = d.mask_mode == SLA_MASK_GIVEN;
+  const bool linear = given || (d.km > 0 && d.kc < d.T);
+
+  SLA_CHECK(stg.begin(SLA_STAGE_BWD_PRE));
+  SLA_CHECK(launched(launch_mask_lists(d, mask, lut, lut_cnt, rbits, col, col_cnt, cbits, s),
+                     "mask_lists"));
+  SLA_CHECK(launched(launch_v_transpose(d, k16, kT, s), "k_transpose"));
+  SLA_CHECK(launched(launch_v_transpose(d, q16, qT, s), "q_transpose"));
+  SLA_CHECK(launched(launch_v_transpose(d, do16, doT, s), "do_transpose"));
+  SLA_CHECK(launched(launch_w_transpose(d, static_cast<const uint16_t*>(w), wT, s), "w_transpose"));
+  SLA_CHECK(launched(launch_bwd_prep(d, q16, o16, do16, wT, den, y, hst, zst, linear, dsum, ddel, dn,
+                                     dq, s),
+                     "bwd_prep"));
+  if (linear) {
+    SLA_CHECK(launched(launch_dstate(d, q16, dn, ddel, states, s), "dstate"));
+    SLA_CHECK(launched(launch_aggregate(d, cbits, states, dh, dz, s), "aggregate_t"));
+  }
+  SLA_CHECK(stg.end(SLA_STAGE_BWD_PRE));
+  SLA_CHECK(stg.begin(SLA_STAGE_BWD_KV));
+  SLA_CHECK(launched(launch_bwd_kv(d, q16, qT, k16, v16, do16, doT, lse, dsum, col, col_cnt, dh, dz,
+                                   linear, dk, dv, s),
+                     "bwd_kv"));
+  SLA_CHECK(stg.end(SLA_STAGE_BWD_KV));
+  SLA_CHECK(stg.begin(SLA_STAGE_BWD_Q));
+  SLA_CHECK(launched(launch_bwd_q(d, q16, k16, kT, v16, do16, lse, dsum, lut, lut_cnt, dq, s),
+                     "bwd_q"));
+  SLA_CHECK(launched(launch_dw(d, y, doT, dwp, dw, s), "dw"));
+  SLA_CHECK(stg.end(SLA_STAGE_BWD_Q));
+  return SLA_OK;
 }
 
 sla_status sla_pool_scores(const sla_config* cfg, const void* q, const void* k, float* scores,

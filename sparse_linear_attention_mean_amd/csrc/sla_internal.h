@@ -33,6 +33,10 @@ struct WorkspaceLayout {
   size_t dstate;            // bf16 [BH, T, D*D] + fp32 [BH, T, 2, D] aggregated backward states
   size_t dstate_z;
   size_t dsum;              // fp32 [BH, N]  D_r of the backward
+  size_t ddel;              // fp32 [BH, N]  linear-denominator gradient per row
+  size_t dn;                // bf16 [BH, N, D]  dY / den per row
+  size_t kT, qT, doT;       // bf16 [BH, T, D, 64]  per-block transposes
+  size_t wT;                // bf16 [D, D]
   size_t dw_part;           // fp32 [P, D, D] dW partial sums
   size_t total;
 };
@@ -50,6 +54,8 @@ SavedLayout saved_layout(const Dims& d);
 hipError_t launch_kv_state(const Dims& d, const uint16_t* k, const uint16_t* v, float* kbar,
                            uint16_t* states, uint16_t* vT, hipStream_t s);
 hipError_t launch_v_transpose(const Dims& d, const uint16_t* v, uint16_t* vT, hipStream_t s);
+hipError_t launch_dstate(const Dims& d, const uint16_t* q, const uint16_t* dn, const float* ddel,
+                         uint16_t* states, hipStream_t s);
 hipError_t launch_pool(const Dims& d, const uint16_t* x, float* xbar, hipStream_t s);
 hipError_t launch_scores(const Dims& d, const float* qbar, const float* kbar, float* scores,
                          hipStream_t s);
@@ -68,18 +74,21 @@ hipError_t launch_attn_fwd(const Dims& d, const uint16_t* q, const uint16_t* k,
                            float* den, uint16_t* y, hipStream_t s);
 
 // backward
-hipError_t launch_bwd_q_lin(const Dims& d, const uint16_t* q, const uint16_t* o,
-                            const uint16_t* dO, const uint16_t* w, const float* den,
-                            const uint16_t* y, const uint16_t* hst, const float* zst,
-                            float* dsum, float* dq, uint16_t* dstates, hipStream_t s);
-hipError_t launch_dw(const Dims& d, const uint16_t* dO, const uint16_t* y, float* part, float* dw,
+hipError_t launch_w_transpose(const Dims& d, const uint16_t* w, uint16_t* wT, hipStream_t s);
+hipError_t launch_bwd_prep(const Dims& d, const uint16_t* q, const uint16_t* o,
+                           const uint16_t* dO, const uint16_t* wT, const float* den,
+                           const uint16_t* y, const uint16_t* hst, const float* zst, bool linear,
+                           float* dsum, float* ddel, uint16_t* dn, float* dq, hipStream_t s);
+hipError_t launch_bwd_q(const Dims& d, const uint16_t* q, const uint16_t* k, const uint16_t* kT,
+                        const uint16_t* v, const uint16_t* dO, const float* lse,
+                        const float* dsum, const int32_t* lut, const int32_t* lut_cnt, float* dq,
+                        hipStream_t s);
+hipError_t launch_bwd_kv(const Dims& d, const uint16_t* q, const uint16_t* qT, const uint16_t* k,
+                         const uint16_t* v, const uint16_t* dO, const uint16_t* doT,
+                         const float* lse, const float* dsum, const int32_t* col,
+                         const int32_t* col_cnt, const uint16_t* dh, const float* dz, bool linear,
+                         float* dk, float* dv, hipStream_t s);
+hipError_t launch_dw(const Dims& d, const uint16_t* y, const uint16_t* doT, float* part, float* dw,
                      hipStream_t s);
-hipError_t launch_bwd_kv(const Dims& d, const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                         const uint16_t* dO, const float* lse, const float* dsum,
-                         const int32_t* col, const int32_t* col_cnt, const uint16_t* dh,
-                         const float* dz, float* dk, float* dv, hipStream_t s);
-hipError_t launch_bwd_q(const Dims& d, const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                        const uint16_t* dO, const float* lse, const float* dsum,
-                        const int32_t* lut, const int32_t* lut_cnt, float* dq, hipStream_t s);
 
 }  // namespace sla
