@@ -17,12 +17,14 @@
 // then the S^T result tile, converted to bf16, is directly the B operand of
 // the P V product (k index permuted identically in the V^T operand), each
 // lane owns one query row, and row statistics need a single xor-32 exchange.
-// K_j is staged to LDS row-major and V_j^T (written once per key block by the
-// state builder) row-major too, so staging is a plain 16-byte copy; both are
-// double-buffered with the next block's global loads in flight during the
-// current block's MFMAs.  Row pitches (D + 8 and 68 bf16) keep the MFMA
-// operand reads free of LDS bank conflicts.
+// K_j and V_j are staged to LDS row-major (a plain 16-byte copy); the V^T
+// operand of the P V product is read from the V tile with LDS transpose reads.
+// Both tiles are double-buffered with the next block's global loads in flight
+// during the current block's MFMAs; the row pitch keeps the 16-byte operand
+// reads and the transpose reads free of LDS bank conflicts.
 // The two key halves are merged at the end like split-K partial softmaxes.
+#include <type_traits>
+
 #include "sla_device.h"
 #include "sla_internal.h"
 
@@ -31,7 +33,7 @@ namespace sla {
 struct AttnArgs {
   const uint16_t* q;
   const uint16_t* k;
-  const uint16_t* vT;
+  const uint16_t* v;
   const uint16_t* w;
   const int32_t* lut;
   const int32_t* lut_cnt;
@@ -47,9 +49,9 @@ struct AttnArgs {
 
 template <int D>
 struct AttnCfg {
-  static constexpr int KP = D + 8;                 // K row pitch in LDS (bf16)
-  static constexpr int VP = 68;                    // V^T row pitch (64 keys + pad)
-  static constexpr int kBuf = 64 * KP + D * VP;    // one K + V^T buffer (bf16 elements)
+  static constexpr int KP = D == 128 ? 152 : 72;   // K and V row pitch in LDS (bf16)
+  static constexpr int VP = KP;
+  static constexpr int kBuf = 2 * 64 * KP;         // one K + V buffer (bf16 elements)
   static constexpr int kLds = 2 * kBuf * 2;        // bytes, double buffered
   static constexpr int KCH = D / 32;               // 16-byte K chunks per thread
   static constexpr int NCT = D / 32;               // 32-row tiles of O^T per wave
@@ -80,73 +82,83 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs args) {
   {
     const uint16_t* qrow = args.q + head + static_cast<size_t>(row) * D + 8 * hl;
 #pragma unroll
-    for (int cc = 0; cc < C::NCC; ++cc) qf[cc] = as_bf16x8(ld16(qrow + 16 * cc));
+    for (int cc = 0; cc < C::NCC; ++cc)
+      qf[cc] = row < L ? as_bf16x8(ld16(qrow + 16 * cc)) : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
   }
 
   const int cnt = DENSE ? T : args.lut_cnt[bh * T + i];
   const int32_t* lrow = DENSE ? nullptr : args.lut + (bh * T + i) * static_cast<long long>(T);
 
-  // staging: 8 D chunks of 16 bytes for K (row t, 8 columns) and as many for
-  // V^T (row c, 8 tokens); chunk e = tid + 256 u
+  // staging: 8 D chunks of 16 bytes each for K and V (row t, 8 columns);
+  // chunk e = tid + 256 u.  Loads go through buffer resources of this head
+  // (block offset in an SGPR, lane offset in a VGPR).
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(args.k + head, static_cast<uint32_t>(N) * D * 2);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(args.v + head, static_cast<uint32_t>(N) * D * 2);
   u32x4 rk[C::KCH], rv[C::KCH];
-#define SLA_LOAD_BLOCK(jblk)                                                                  \
-  do {                                                                                        \
-    const int j_ = (jblk);                                                                    \
-    const uint16_t* kb = args.k + head + static_cast<size_t>(j_) * kBlock * D;                \
-    const uint16_t* vb = args.vT + head + static_cast<size_t>(j_) * kBlock * D;               \
-    _Pragma("unroll") for (int u = 0; u < C::KCH; ++u) {                                      \
-      const int e = tid + 256 * u;                                                            \
-      rk[u] = ld16(kb + 8 * e);                                                               \
-      rv[u] = ld16(vb + 8 * e);                                                               \
-    }                                                                                         \
-  } while (0)
-#define SLA_STORE_BLOCK(bufidx)                                                               \
-  do {                                                                                        \
-    uint16_t* ks_ = smem + (bufidx) * C::kBuf;                                                \
-    uint16_t* vt_ = ks_ + 64 * KP;                                                            \
-    _Pragma("unroll") for (int u = 0; u < C::KCH; ++u) {                                      \
-      const int e = tid + 256 * u;                                                            \
-      st16(ks_ + (e / (D / 8)) * KP + 8 * (e % (D / 8)), rk[u]);                             \
-      uint16_t* vd = vt_ + (e >> 3) * VP + 8 * (e & 7);                                       \
-      st8(vd, u32x2{rv[u][0], rv[u][1]});                                                     \
-      st8(vd + 4, u32x2{rv[u][2], rv[u][3]});                                                 \
-    }                                                                                         \
-  } while (0)
+  // chunk e = tid + 256 u: global byte offset 16 e; row e / (D / 8) = row0 + u (256 / (D / 8))
+  const uint32_t gbase = 16u * tid;
+  const int kst0 = (tid / (D / 8)) * KP + 8 * (tid % (D / 8));
+  constexpr int kRowsPerU = 256 / (D / 8);
+  auto load_block = [&](int jb) {
+    const uint32_t soff = static_cast<uint32_t>(jb) * kBlock * D * 2;
+#pragma unroll
+    for (int u = 0; u < C::KCH; ++u) {
+      rk[u] = buf_ld16(krs, gbase, soff + 4096u * u);
+      rv[u] = buf_ld16(vrs, gbase, soff + 4096u * u);
+    }
+    if ((jb + 1) * kBlock > L) {   // padded last block: zero V rows (their P is masked too)
+#pragma unroll
+      for (int u = 0; u < C::KCH; ++u)
+        if (jb * kBlock + (tid / (D / 8)) + u * kRowsPerU >= L) rv[u] = u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto store_block = [&](int bufidx) {
+    uint16_t* ks_ = smem + bufidx * C::kBuf;
+    uint16_t* vt_ = ks_ + 64 * KP;
+#pragma unroll
+    for (int u = 0; u < C::KCH; ++u) {
+      st16(ks_ + kst0 + u * kRowsPerU * KP, rk[u]);
+      st16(vt_ + kst0 + u * kRowsPerU * KP, rv[u]);
+    }
+  };
 
   f32x16 acc[C::NCT];
 #pragma unroll
   for (int ct = 0; ct < C::NCT; ++ct) acc[ct] = f32x16{};
   float m_run = -INFINITY;   // running max (log2 units) of this lane's query
   float l_run = 0.f;         // partial row sum over this lane's keys
+  const int kread = (32 * kh + n32) * KP + 8 * hl;          // S^T A operand (row of K)
 
-  if (cnt > 0) {
-    SLA_LOAD_BLOCK(DENSE ? 0 : lrow[0]);
-    SLA_STORE_BLOCK(0);
-    __syncthreads();
-  }
-  for (int n = 0; n < cnt; ++n) {
+  // One key block: S^T = K Q^T, online softmax (base 2, lazy rescale), O^T += V^T P^T.
+  // MASKED is used only for the padded last key block.
+  auto step = [&](int n, auto masked_tag) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
     const int j = DENSE ? n : lrow[n];
     const int buf = n & 1;
-    if (n + 1 < cnt) SLA_LOAD_BLOCK(DENSE ? n + 1 : lrow[n + 1]);
+    const bool more = n + 1 < cnt;
+    if (more) load_block(DENSE ? n + 1 : lrow[n + 1]);
     const uint16_t* ks = smem + buf * C::kBuf;
     const uint16_t* vt = ks + 64 * KP;
-
-    // S^T tile: 32 keys (32 kh ..) x 32 queries
     f32x16 st = {};
 #pragma unroll
-    for (int cc = 0; cc < C::NCC; ++cc) {
-      st = mfma32(as_bf16x8(ld16(ks + (32 * kh + n32) * KP + 16 * cc + 8 * hl)), qf[cc], st);
-    }
-    const bool tail = (j + 1) * kBlock > L;
-    float mraw = -INFINITY;
+    for (int cc = 0; cc < C::NCC; ++cc) st = mfma32(as_bf16x8(ld16(ks + kread + 16 * cc)), qf[cc], st);
+    // V^T operands of this block (transpose reads of the V tile, keys in the
+    // permuted order of the S^T tile), read ahead of the softmax arithmetic
+    bf16x8 va[C::NCT][2];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      if (tail) {
+    for (int ct = 0; ct < C::NCT; ++ct)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) va[ct][h] = lds_op32_tr<true>(vt, VP, 32 * kh + 16 * h, 32 * ct, lane);
+    if constexpr (MASKED) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
         const int key = j * kBlock + 32 * kh + 8 * (e / 4) + 4 * hl + (e % 4);
         if (key >= L) st[e] = -INFINITY;
       }
-      mraw = fmaxf(mraw, st[e]);
     }
+    float mraw = st[0];
+#pragma unroll
+    for (int e = 1; e < 16; ++e) mraw = fmaxf(mraw, st[e]);
     mraw = fmaxf(mraw, __shfl_xor(mraw, 32));
     const float m_new = fmaxf(m_run, mraw * sl2);
     const bool need = m_new > m_run + 8.0f;
@@ -166,23 +178,26 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs args) {
       p[e] = __builtin_amdgcn_exp2f(__fmaf_rn(st[e], sl2, -mu));
       l_run += p[e];
     }
-    bf16x8 pb[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int s = 0; s < 8; ++s) pb[h][s] = static_cast<__bf16>(p[8 * h + s]);
-
+    const bf16x8 pb[2] = {cvt_bf16x8(p), cvt_bf16x8(p + 8)};
     // O^T += V^T P^T; k index of chunk h: keys 16 h + {4 hl .. 4 hl + 3, 8 + 4 hl .. 8 + 4 hl + 3}
 #pragma unroll
-    for (int ct = 0; ct < C::NCT; ++ct) {
-      const uint16_t* vrow = vt + (32 * ct + n32) * VP + 32 * kh + 4 * hl;
+    for (int ct = 0; ct < C::NCT; ++ct)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        acc[ct] = mfma32(as_bf16x8(ld8(vrow + 16 * h), ld8(vrow + 16 * h + 8)), pb[h], acc[ct]);
-      }
-    }
-    if (n + 1 < cnt) SLA_STORE_BLOCK(buf ^ 1);
+      for (int h = 0; h < 2; ++h) acc[ct] = mfma32(va[ct][h], pb[h], acc[ct]);
+    if (more) store_block(buf ^ 1);
     __syncthreads();
+  };
+
+  if (cnt > 0) {
+    load_block(DENSE ? 0 : lrow[0]);
+    store_block(0);
+    __syncthreads();
+    for (int n = 0; n + 1 < cnt; ++n) step(n, std::false_type{});
+    const int jl = DENSE ? cnt - 1 : lrow[cnt - 1];   // ascending lists: only the last can be padded
+    if ((jl + 1) * kBlock > L)
+      step(cnt - 1, std::true_type{});
+    else
+      step(cnt - 1, std::false_type{});
   }
   l_run += __shfl_xor(l_run, 32);
 #undef SLA_LOAD_BLOCK
@@ -344,11 +359,11 @@ static hipError_t launch_attn_t(const AttnArgs& a, unsigned grid, bool dense, bo
 }
 
 hipError_t launch_attn_fwd(const Dims& d, const uint16_t* q, const uint16_t* k,
-                           const uint16_t* vT, const uint16_t* w, const int32_t* lut,
+                           const uint16_t* v, const uint16_t* w, const int32_t* lut,
                            const int32_t* lut_cnt, bool dense, bool linear,
                            const uint16_t* hst, const float* zst, uint16_t* o, float* lse,
                            float* den, uint16_t* y, hipStream_t s) {
-  AttnArgs a{q, k, vT, w, lut, lut_cnt, hst, zst, o, lse, den, y, d.N, d.L, d.T,
+  AttnArgs a{q, k, v, w, lut, lut_cnt, hst, zst, o, lse, den, y, d.N, d.L, d.T,
              d.scale * kLog2e};
   const unsigned grid = static_cast<unsigned>(d.BH() * d.T);
   if (d.D == 128) return launch_attn_t<128>(a, grid, dense, linear, s);

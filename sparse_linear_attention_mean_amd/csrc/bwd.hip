@@ -194,12 +194,14 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(
 //   S^T = K Q^T, P^T = exp2(S^T scale log2e - lse log2e), dP^T = V dO^T,
 //   dS^T = P^T (dP^T - D), dQ += scale dS K
 // Waves (kh, qh) as in the forward; dS^T's result tile is the A operand of
-// dS K directly (k index permuted), with K^T staged in LDS.
+// dS K directly (k index permuted) and K_j is read a second time from the
+// same LDS tile with transpose reads.  K_j and V_j are double-buffered with
+// the next block's loads in flight during the current block's MFMAs.
 // ---------------------------------------------------------------------------
 template <int D>
 struct BqCfg {
-  static constexpr int KP = D + 8, TP = 68;
-  static constexpr int kBuf = 2 * 64 * KP + D * TP;   // K, V (rows) and K^T
+  static constexpr int KP = D == 128 ? 152 : 72;      // row pitch (bf16)
+  static constexpr int kBuf = 2 * 64 * KP;             // K and V rows
   static constexpr int KCH = D / 32;                   // 16-byte chunks per thread per tensor
   static constexpr int NCC = D / 16, NAT = D / 32;
 };
@@ -207,17 +209,13 @@ struct BqCfg {
 template <int D>
 __global__ __launch_bounds__(256, 2) void bwd_q_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ kT, const uint16_t* __restrict__ v,
-    const uint16_t* __restrict__ dO, const float* __restrict__ lse,
-    const float* __restrict__ dsum, const int32_t* __restrict__ lut,
-    const int32_t* __restrict__ lut_cnt, float* __restrict__ dq, int N, int L, int T,
-    float scale) {
+    const uint16_t* __restrict__ v, const uint16_t* __restrict__ dO,
+    const float* __restrict__ lse, const float* __restrict__ dsum,
+    const int32_t* __restrict__ lut, const int32_t* __restrict__ lut_cnt,
+    float* __restrict__ dq, int N, int L, int T, float scale) {
   using C = BqCfg<D>;
-  constexpr int KP = C::KP, TP = C::TP;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[C::kBuf];
-  uint16_t* ks = smem;
-  uint16_t* vs = smem + 64 * KP;
-  uint16_t* kts = smem + 2 * 64 * KP;
+  constexpr int KP = C::KP;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * C::kBuf];
 
   const uint32_t wg = xcd_remap(blockIdx.x, gridDim.x);
   const int i = wg % T;
@@ -236,11 +234,12 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(
     const uint16_t* dr = dO + head + static_cast<size_t>(row) * D + 8 * hl;
 #pragma unroll
     for (int cc = 0; cc < C::NCC; ++cc) {
-      qf[cc] = as_bf16x8(ld16(qr + 16 * cc));
+      qf[cc] = valid ? as_bf16x8(ld16(qr + 16 * cc)) : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
       dof[cc] = valid ? as_bf16x8(ld16(dr + 16 * cc)) : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
     }
   }
-  const float lse2 = valid ? lse[bh * N + row] * kLog2e : 0.f;
+  // padded rows: zero Q and dO and an infinite lse make P = 0 and dS = 0
+  const float lse2 = valid ? lse[bh * N + row] * kLog2e : INFINITY;
   const float dsv = valid ? dsum[bh * N + row] : 0.f;
   const int cnt = lut_cnt[bh * T + i];
   const int32_t* lrow = lut + (bh * T + i) * static_cast<long long>(T);
@@ -249,7 +248,7 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(
 #pragma unroll
   for (int at = 0; at < C::NAT; ++at) acc[at] = f32x16{};
 
-  u32x4 rk[C::KCH], rv[C::KCH], rt[C::KCH];
+  u32x4 rk[C::KCH], rv[C::KCH];
   auto load = [&](int j) {
     const size_t off = head + static_cast<size_t>(j) * kBlock * D;
 #pragma unroll
@@ -257,54 +256,61 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(
       const int e = tid + 256 * u;
       rk[u] = ld16(k + off + 8 * e);
       rv[u] = ld16(v + off + 8 * e);
-      rt[u] = ld16(kT + off + 8 * e);
     }
   };
-  auto store = [&]() {
+  auto store = [&](int buf, int j) {
+    uint16_t* ks = smem + buf * C::kBuf;
+    uint16_t* vs = ks + 64 * KP;
+    const int nvalid = L - j * kBlock;   // < 64 only for the last (padded) key block
 #pragma unroll
     for (int u = 0; u < C::KCH; ++u) {
       const int e = tid + 256 * u;
-      st16(ks + (e / (D / 8)) * KP + 8 * (e % (D / 8)), rk[u]);
-      st16(vs + (e / (D / 8)) * KP + 8 * (e % (D / 8)), rv[u]);
-      uint16_t* td = kts + (e >> 3) * TP + 8 * (e & 7);
-      st8(td, u32x2{rt[u][0], rt[u][1]});
-      st8(td + 4, u32x2{rt[u][2], rt[u][3]});
+      const int t = e / (D / 8);
+      const bool ok = t < nvalid;        // padded keys: zero K and V rows
+      st16(ks + t * KP + 8 * (e % (D / 8)), ok ? rk[u] : u32x4{0u, 0u, 0u, 0u});
+      st16(vs + t * KP + 8 * (e % (D / 8)), ok ? rv[u] : u32x4{0u, 0u, 0u, 0u});
     }
   };
 
-  if (cnt > 0) load(lrow[0]);
+  if (cnt > 0) {
+    load(lrow[0]);
+    store(0, lrow[0]);
+    __syncthreads();
+  }
   for (int n = 0; n < cnt; ++n) {
     const int j = lrow[n];
-    __syncthreads();   // previous block's LDS reads are done
-    store();
-    __syncthreads();
-    if (n + 1 < cnt) load(lrow[n + 1]);
+    const int buf = n & 1;
+    const int jn = n + 1 < cnt ? lrow[n + 1] : 0;
+    if (n + 1 < cnt) load(jn);
+    const uint16_t* ks = smem + buf * C::kBuf;
+    const uint16_t* vs = ks + 64 * KP;
     f32x16 st = {}, dpt = {};
 #pragma unroll
     for (int cc = 0; cc < C::NCC; ++cc) {
       st = mfma32(as_bf16x8(ld16(ks + (32 * kh + n32) * KP + 16 * cc + 8 * hl)), qf[cc], st);
       dpt = mfma32(as_bf16x8(ld16(vs + (32 * kh + n32) * KP + 16 * cc + 8 * hl)), dof[cc], dpt);
     }
-    const bool tail = (j + 1) * kBlock > L;
-    bf16x8 ds[2];
+    float dsf[16];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      float p = __builtin_amdgcn_exp2f(__fmaf_rn(st[e], sl2, -lse2));
-      if (tail) {
+    for (int e = 0; e < 16; ++e) dsf[e] = __builtin_amdgcn_exp2f(__fmaf_rn(st[e], sl2, -lse2));
+    if ((j + 1) * kBlock > L) {   // uniform: only the padded last key block
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
         const int key = j * kBlock + 32 * kh + 8 * (e / 4) + 4 * hl + (e % 4);
-        if (key >= L) p = 0.f;
+        if (key >= L) dsf[e] = 0.f;
       }
-      if (!valid) p = 0.f;
-      ds[e >> 3][e & 7] = static_cast<__bf16>(p != 0.f ? p * (dpt[e] - dsv) : 0.f);
     }
-    // dQ[q][a] += dS[q][keys] K[keys][a]: B operand K^T[a][keys of chunk h]
 #pragma unroll
-    for (int at = 0; at < C::NAT; ++at) {
-      const uint16_t* tr = kts + (32 * at + n32) * TP + 32 * kh + 4 * hl;
+    for (int e = 0; e < 16; ++e) dsf[e] *= dpt[e] - dsv;
+    const bf16x8 ds[2] = {cvt_bf16x8(dsf), cvt_bf16x8(dsf + 8)};
+    // dQ[q][a] += dS[q][keys] K[keys][a]: B operand K[keys of chunk h][a] by transpose reads
+#pragma unroll
+    for (int at = 0; at < C::NAT; ++at)
 #pragma unroll
       for (int h = 0; h < 2; ++h)
-        acc[at] = mfma32(ds[h], as_bf16x8(ld8(tr + 16 * h), ld8(tr + 16 * h + 8)), acc[at]);
-    }
+        acc[at] = mfma32(ds[h], lds_op32_tr<true>(ks, KP, 32 * kh + 16 * h, 32 * at, lane), acc[at]);
+    if (n + 1 < cnt) store(buf ^ 1, jn);
+    __syncthreads();
   }
   // merge the key halves and add the linear part
   __syncthreads();
@@ -334,33 +340,39 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(
 // ---------------------------------------------------------------------------
 // bwd_kv: one workgroup per key block j; loops over the query blocks for which
 // j is critical (column list), then adds the linear-branch gradients.
-// Wave (kh, qh): keys 32 kh .. 32 kh + 31 of the block, queries 32 qh .. of
-// each query block.  S = Q K^T and dP = dO V^T take K_j, V_j from registers;
-// dV += P^T dO and dK += dS^T Q take P, dS straight from the S / dP result
-// tiles (k index permuted) with dO^T and Q^T staged in LDS.
+// Eight waves in two roles that share the staged Q_i / dO_i tiles: waves 0-3
+// accumulate dV (S -> P -> P^T dO), waves 4-7 accumulate dK (S, dP -> dS ->
+// dS^T Q).  Within a role, wave (kh, qh) owns keys 32 kh .. 32 kh + 31 of the
+// block and queries 32 qh .. 32 qh + 31 of each query block.  S = Q K^T and
+// dP = dO V^T take K_j, V_j from registers and Q_i, dO_i rows from LDS; the
+// products over queries take P or dS straight from the S / dP result tiles
+// (k index permuted) and read dO_i or Q_i from the same LDS tiles with
+// transpose reads, so only the natural tiles are staged.  The row pitch keeps
+// both kinds of LDS read free of bank conflicts.
 // ---------------------------------------------------------------------------
 template <int D>
 struct BkvCfg {
-  static constexpr int RP = D + 8, TP = 68;
-  static constexpr int kBuf = 2 * 64 * RP + 2 * D * TP;   // Q, dO rows; Q^T, dO^T
-  static constexpr int KCH = D / 32;
+  static constexpr int RP = D == 128 ? 152 : 72;      // Q / dO row pitch (bf16)
+  static constexpr int kBuf = 2 * 64 * RP;              // Q and dO of one query block
+  static constexpr int KCH = D / 64;                    // 16-byte chunks per thread per tensor
   static constexpr int NCC = D / 16, NCT = D / 32;
-  static constexpr int kLds = (2 * kBuf * 2 + 2 * 64 * 4 * 2 > D * (D + 8) * 2 + 2 * 2 * 32 * D * 4)
-                                  ? 2 * kBuf * 2 + 2 * 64 * 4 * 2
-                                  : D * (D + 8) * 2 + 2 * 2 * 32 * D * 4;
+  static constexpr int HP = D + 8;
+  static constexpr int kStage = 2 * kBuf * 2 + 2 * 2 * 64 * 4;          // bytes: 2 buffers + lse/D
+  // dh^T tile + merge area: 4 slots (role x key half) of NCT*16 registers x 64 lanes (fp32)
+  static constexpr int kEpi = D * HP * 2 + 4 * NCT * 16 * 64 * 4;
+  static constexpr int kLds = kStage > kEpi ? kStage : kEpi;
 };
 
 template <int D>
-__global__ __launch_bounds__(256, 1) void bwd_kv_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ qT,
-    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const uint16_t* __restrict__ dO, const uint16_t* __restrict__ doT,
+__global__ __launch_bounds__(512, 1) void bwd_kv_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const uint16_t* __restrict__ dO,
     const float* __restrict__ lse, const float* __restrict__ dsum,
     const int32_t* __restrict__ col, const int32_t* __restrict__ col_cnt,
     const uint16_t* __restrict__ dh, const float* __restrict__ dz, bool linear,
     float* __restrict__ dk, float* __restrict__ dv, int N, int L, int T, float scale) {
   using C = BkvCfg<D>;
-  constexpr int RP = C::RP, TP = C::TP;
+  constexpr int RP = C::RP, HP = C::HP;
   __shared__ __attribute__((aligned(16))) uint8_t smem_raw[C::kLds];
   uint16_t* smem = reinterpret_cast<uint16_t*>(smem_raw);
   float* lses = reinterpret_cast<float*>(smem_raw + 2 * C::kBuf * 2);   // [buf][64]
@@ -370,44 +382,41 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(
   const int j = wg % T;
   const long long bh = wg / T;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int kh = wave & 1, qh = wave >> 1;
+  const bool role_dk = wave >= 4;               // uniform per wave
+  const int kh = wave & 1, qh = (wave >> 1) & 1;
   const int n32 = lane & 31, hl = lane >> 5;
   const size_t head = static_cast<size_t>(bh) * N * D;
   const int key = j * kBlock + 32 * kh + n32;   // this lane's key (B operand column)
   const float sl2 = scale * kLog2e;
 
-  // K_j, V_j as B operands (k = head-dim index 16 cc + 8 hl + s)
+  // K_j (and V_j for the dK role) as B operands (k = head-dim index 16 cc + 8 hl + s)
   bf16x8 kf[C::NCC], vf[C::NCC];
   {
     const uint16_t* kr = k + head + static_cast<size_t>(key) * D + 8 * hl;
     const uint16_t* vr = v + head + static_cast<size_t>(key) * D + 8 * hl;
+    const bool kv_ok = key < L;   // padded keys: zero operands (their P is masked too)
 #pragma unroll
     for (int cc = 0; cc < C::NCC; ++cc) {
-      kf[cc] = as_bf16x8(ld16(kr + 16 * cc));
-      vf[cc] = as_bf16x8(ld16(vr + 16 * cc));
+      kf[cc] = kv_ok ? as_bf16x8(ld16(kr + 16 * cc)) : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+      vf[cc] = (role_dk && kv_ok) ? as_bf16x8(ld16(vr + 16 * cc)) : kf[cc];
     }
   }
   const int cnt = col_cnt[bh * T + j];
   const int32_t* crow = col + (bh * T + j) * static_cast<long long>(T);
 
-  f32x16 adv[C::NCT], adk[C::NCT];
+  f32x16 acc[C::NCT];   // dV (role 0) or the unscaled dK (role 1)
 #pragma unroll
-  for (int ct = 0; ct < C::NCT; ++ct) {
-    adv[ct] = f32x16{};
-    adk[ct] = f32x16{};
-  }
+  for (int ct = 0; ct < C::NCT; ++ct) acc[ct] = f32x16{};
 
-  u32x4 r_q[C::KCH], r_d[C::KCH], r_qt[C::KCH], r_dt[C::KCH];
+  u32x4 r_q[C::KCH], r_d[C::KCH];
   float r_l = 0.f, r_s = 0.f;
   auto load = [&](int ib) {
     const size_t off = head + static_cast<size_t>(ib) * kBlock * D;
 #pragma unroll
     for (int u = 0; u < C::KCH; ++u) {
-      const int e = tid + 256 * u;
+      const int e = tid + 512 * u;
       r_q[u] = ld16(q + off + 8 * e);
       r_d[u] = ld16(dO + off + 8 * e);
-      r_qt[u] = ld16(qT + off + 8 * e);
-      r_dt[u] = ld16(doT + off + 8 * e);
     }
     if (tid < kBlock) {
       const int rr = ib * kBlock + tid;
@@ -415,23 +424,17 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(
       r_s = rr < L ? dsum[bh * N + rr] : 0.f;
     }
   };
-  auto store = [&](int buf) {
+  auto store = [&](int buf, int ib) {
     uint16_t* qs = smem + buf * C::kBuf;
     uint16_t* ds_ = qs + 64 * RP;
-    uint16_t* qts = qs + 2 * 64 * RP;
-    uint16_t* dts = qts + D * TP;
+    const int nvalid = L - ib * kBlock;   // < 64 only for the last (padded) query block
 #pragma unroll
     for (int u = 0; u < C::KCH; ++u) {
-      const int e = tid + 256 * u;
+      const int e = tid + 512 * u;
       const int rr = e / (D / 8), cc8 = 8 * (e % (D / 8));
-      st16(qs + rr * RP + cc8, r_q[u]);
-      st16(ds_ + rr * RP + cc8, r_d[u]);
-      uint16_t* t1 = qts + (e >> 3) * TP + 8 * (e & 7);
-      uint16_t* t2 = dts + (e >> 3) * TP + 8 * (e & 7);
-      st8(t1, u32x2{r_qt[u][0], r_qt[u][1]});
-      st8(t1 + 4, u32x2{r_qt[u][2], r_qt[u][3]});
-      st8(t2, u32x2{r_dt[u][0], r_dt[u][1]});
-      st8(t2 + 4, u32x2{r_dt[u][2], r_dt[u][3]});
+      const bool ok = rr < nvalid;         // padded rows: zero Q and dO (and lse = inf)
+      st16(qs + rr * RP + cc8, ok ? r_q[u] : u32x4{0u, 0u, 0u, 0u});
+      st16(ds_ + rr * RP + cc8, ok ? r_d[u] : u32x4{0u, 0u, 0u, 0u});
     }
     if (tid < kBlock) {
       lses[buf * 64 + tid] = r_l;
@@ -441,68 +444,73 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(
 
   if (cnt > 0) {
     load(crow[0]);
-    store(0);
+    store(0, crow[0]);
     __syncthreads();
   }
-  const bool tail = (j + 1) * kBlock > L;
+  const bool tail_key = key >= L;
+  const bool tail_blk = (j + 1) * kBlock > L;   // uniform: the padded last key block
   for (int n = 0; n < cnt; ++n) {
     const int buf = n & 1;
-    if (n + 1 < cnt) load(crow[n + 1]);
+    const int inext = n + 1 < cnt ? crow[n + 1] : 0;
+    if (n + 1 < cnt) load(inext);
     const uint16_t* qs = smem + buf * C::kBuf;
     const uint16_t* ds_ = qs + 64 * RP;
-    const uint16_t* qts = qs + 2 * 64 * RP;
-    const uint16_t* dts = qts + D * TP;
-    f32x16 s = {}, dp = {};
+    f32x16 s = {};
 #pragma unroll
-    for (int cc = 0; cc < C::NCC; ++cc) {
+    for (int cc = 0; cc < C::NCC; ++cc)
       s = mfma32(as_bf16x8(ld16(qs + (32 * qh + n32) * RP + 16 * cc + 8 * hl)), kf[cc], s);
-      dp = mfma32(as_bf16x8(ld16(ds_ + (32 * qh + n32) * RP + 16 * cc + 8 * hl)), vf[cc], dp);
+    // lane holds S[q = 32 qh + 8 (e/4) + 4 hl + e%4][key]: row statistics by 4
+    float pf[16];
+#pragma unroll
+    for (int e4 = 0; e4 < 4; ++e4) {
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lses[buf * 64 + 32 * qh + 8 * e4 + 4 * hl]);
+#pragma unroll
+      for (int x = 0; x < 4; ++x) pf[4 * e4 + x] = __builtin_amdgcn_exp2f(__fmaf_rn(s[4 * e4 + x], sl2, -l4[x]));
     }
-    // lane holds S[q = 32 qh + 8 (e/4) + 4 hl + e%4][key]
-    bf16x8 pb[2], sb[2];
+    if (tail_blk) {   // keys past valid_len: no probability mass
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int qq = 32 * qh + 8 * (e / 4) + 4 * hl + (e % 4);
-      const float l2 = lses[buf * 64 + qq];
-      float p = __builtin_amdgcn_exp2f(__fmaf_rn(s[e], sl2, -l2));
-      if ((tail && key >= L) || l2 == INFINITY) p = 0.f;
-      pb[e >> 3][e & 7] = static_cast<__bf16>(p);
-      sb[e >> 3][e & 7] = static_cast<__bf16>(p != 0.f ? p * (dp[e] - dss[buf * 64 + qq]) : 0.f);
+      for (int e = 0; e < 16; ++e) pf[e] = tail_key ? 0.f : pf[e];
     }
-    // dV[key][c] += P^T dO, dK[key][a] += dS^T Q; B operands from dO^T / Q^T rows
+    if (role_dk) {
+      f32x16 dp = {};
 #pragma unroll
-    for (int ct = 0; ct < C::NCT; ++ct) {
-      const uint16_t* dtr = dts + (32 * ct + n32) * TP + 32 * qh + 4 * hl;
-      const uint16_t* qtr = qts + (32 * ct + n32) * TP + 32 * qh + 4 * hl;
+      for (int cc = 0; cc < C::NCC; ++cc)
+        dp = mfma32(as_bf16x8(ld16(ds_ + (32 * qh + n32) * RP + 16 * cc + 8 * hl)), vf[cc], dp);
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        adv[ct] = mfma32(pb[h], as_bf16x8(ld8(dtr + 16 * h), ld8(dtr + 16 * h + 8)), adv[ct]);
-        adk[ct] = mfma32(sb[h], as_bf16x8(ld8(qtr + 16 * h), ld8(qtr + 16 * h + 8)), adk[ct]);
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&dss[buf * 64 + 32 * qh + 8 * e4 + 4 * hl]);
+#pragma unroll
+        for (int x = 0; x < 4; ++x) pf[4 * e4 + x] *= dp[4 * e4 + x] - d4[x];
       }
     }
-    if (n + 1 < cnt) store(buf ^ 1);
+    const bf16x8 xb[2] = {cvt_bf16x8(pf), cvt_bf16x8(pf + 8)};
+    // dV[key][c] += P^T dO  or  dK[key][a] += dS^T Q  (B operand by transpose reads)
+    const uint16_t* bsrc = role_dk ? qs : ds_;
+#pragma unroll
+    for (int ct = 0; ct < C::NCT; ++ct)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        acc[ct] = mfma32(xb[h], lds_op32_tr<true>(bsrc, RP, 32 * qh + 16 * h, 32 * ct, lane), acc[ct]);
+    if (n + 1 < cnt) store(buf ^ 1, inext);
     __syncthreads();
   }
 
   // ---- merge the query halves; lane holds X[key = 32 kh + 8 (e/4) + 4 hl + e%4][c = 32 ct + n32]
   __syncthreads();
-  float* ex = reinterpret_cast<float*>(smem_raw + D * (D + 8) * 2);   // [kh][2][NCT*16][64]
+  float* ex = reinterpret_cast<float*>(smem_raw + D * HP * 2);   // [role][kh][NCT*16][64]
   constexpr int NACC = C::NCT * 16;
+  const int slot = (role_dk ? 2 : 0) + kh;
   if (qh == 1) {
 #pragma unroll
     for (int ct = 0; ct < C::NCT; ++ct)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        ex[((kh * 2 + 0) * NACC + ct * 16 + e) * 64 + lane] = adv[ct][e];
-        ex[((kh * 2 + 1) * NACC + ct * 16 + e) * 64 + lane] = adk[ct][e];
-      }
+      for (int e = 0; e < 16; ++e) ex[(slot * NACC + ct * 16 + e) * 64 + lane] = acc[ct][e];
   }
   // stage dh^T[c][a] of this key block for the linear part
   uint16_t* dhs = smem;
-  constexpr int HP = D + 8;
   if (linear) {
     const uint16_t* src = dh + (static_cast<size_t>(bh) * T + j) * D * D;
-    for (int e = tid; e < D * D / 8; e += 256) {
+    for (int e = tid; e < D * D / 8; e += 512) {
       const int c = e / (D / 8), a8 = e % (D / 8);
       st16(&dhs[c * HP + 8 * a8], ld16(src + static_cast<size_t>(c) * D + 8 * a8));
     }
@@ -513,55 +521,60 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(
   for (int ct = 0; ct < C::NCT; ++ct)
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      adv[ct][e] += ex[((kh * 2 + 0) * NACC + ct * 16 + e) * 64 + lane];
-      adk[ct][e] = scale * (adk[ct][e] + ex[((kh * 2 + 1) * NACC + ct * 16 + e) * 64 + lane]);
+      const float sum = acc[ct][e] + ex[(slot * NACC + ct * 16 + e) * 64 + lane];
+      acc[ct][e] = role_dk ? scale * sum : sum;
     }
+  const float* dzr = dz + (static_cast<size_t>(bh) * T + j) * 2 * D;
   if (linear) {
-    // rows t of this wave: A operands phi(K_j)[t][a] and V_j[t][c] (k = 16 cc + 8 hl + s)
+    // rows t of this wave: A operand phi(K_j)[t][a] (dV role) or V_j[t][c] (dK role)
     const int t = j * kBlock + 32 * kh + n32;
-    const uint16_t* kr = k + head + static_cast<size_t>(t) * D + 8 * hl;
-    const uint16_t* vr = v + head + static_cast<size_t>(t) * D + 8 * hl;
     const bool tv = t < L;
-    bf16x8 pkf[C::NCC], vrf[C::NCC];
+    const uint16_t* xr = (role_dk ? v : k) + head + static_cast<size_t>(t) * D + 8 * hl;
+    bf16x8 af[C::NCC];
 #pragma unroll
     for (int cc = 0; cc < C::NCC; ++cc) {
-      const u32x4 kv = ld16(kr + 16 * cc);
+      const u32x4 xv = tv ? ld16(xr + 16 * cc) : u32x4{0u, 0u, 0u, 0u};
+      if (role_dk) {
+        af[cc] = as_bf16x8(xv);
+      } else {
 #pragma unroll
-      for (int s2 = 0; s2 < 8; ++s2)
-        pkf[cc][s2] = static_cast<__bf16>(tv ? phi(bf16_to_f32(static_cast<uint16_t>(u4_elem(kv, s2)))) : 0.f);
-      vrf[cc] = as_bf16x8(ld16(vr + 16 * cc));
+        for (int s2 = 0; s2 < 8; ++s2)
+          af[cc][s2] = static_cast<__bf16>(tv ? phi(bf16_to_f32(static_cast<uint16_t>(u4_elem(xv, s2)))) : 0.f);
+      }
     }
-    const float* dzr = dz + (static_cast<size_t>(bh) * T + j) * 2 * D;
 #pragma unroll
     for (int ct = 0; ct < C::NCT; ++ct) {
-      // dV_lin[t][c] = sum_a phi(K)[t][a] dh[a][c]: B = dh^T[c][a .. a + 7] (row of dh^T)
-      f32x16 lv = {}, lk = {};
+      f32x16 lin = {};
 #pragma unroll
       for (int cc = 0; cc < C::NCC; ++cc) {
-        lv = mfma32(pkf[cc], as_bf16x8(ld16(&dhs[(32 * ct + n32) * HP + 16 * cc + 8 * hl])), lv);
-        // dphi(K)[t][a] = sum_c V[t][c] dh[a][c]: B = dh^T[c .. c + 7][a] (column of dh^T)
-        lk = mfma32(vrf[cc], lds_col8(dhs, HP, 16 * cc + 8 * hl, 32 * ct + n32), lk);
+        // dV role: dV_lin[t][c] = sum_a phi(K)[t][a] dh[a][c], B = dh^T[c][a .. a + 7] (row)
+        // dK role: dphi(K)[t][a] = sum_c V[t][c] dh[a][c],     B = dh^T[c .. c + 7][a] (transpose read)
+        const bf16x8 b = role_dk ? lds_op32_tr<false>(dhs, HP, 16 * cc, 32 * ct, lane)
+                                 : as_bf16x8(ld16(&dhs[(32 * ct + n32) * HP + 16 * cc + 8 * hl]));
+        lin = mfma32(af[cc], b, lin);
       }
       // lane holds X[t = 32 kh + 8 (e/4) + 4 hl + e%4][n = 32 ct + n32]
       const int a = 32 * ct + n32;
-      const float dza = dzr[a] + dzr[D + a];
+      const float dza = role_dk ? dzr[a] + dzr[D + a] : 0.f;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int tt = j * kBlock + 32 * kh + 8 * (e / 4) + 4 * hl + (e % 4);
-        const float kv = tt < L ? bf16_to_f32(k[head + static_cast<size_t>(tt) * D + a]) : 0.f;
-        adv[ct][e] += lv[e];
-        adk[ct][e] += (lk[e] + dza) * phi_prime(kv);
+        if (role_dk) {
+          const int tt = j * kBlock + 32 * kh + 8 * (e / 4) + 4 * hl + (e % 4);
+          const float kv = tt < L ? bf16_to_f32(k[head + static_cast<size_t>(tt) * D + a]) : 0.f;
+          acc[ct][e] += (lin[e] + dza) * phi_prime(kv);
+        } else {
+          acc[ct][e] += lin[e];
+        }
       }
     }
   }
+  float* out = role_dk ? dk : dv;
 #pragma unroll
   for (int ct = 0; ct < C::NCT; ++ct)
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int tt = j * kBlock + 32 * kh + 8 * (e / 4) + 4 * hl + (e % 4);
-      const size_t off = head + static_cast<size_t>(tt) * D + 32 * ct + n32;
-      dv[off] = tt < L ? adv[ct][e] : 0.f;
-      dk[off] = tt < L ? adk[ct][e] : 0.f;
+      out[head + static_cast<size_t>(tt) * D + 32 * ct + n32] = tt < L ? acc[ct][e] : 0.f;
     }
 }
 
@@ -572,42 +585,44 @@ __global__ __launch_bounds__(256, 1) void bwd_kv_kernel(
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void dw_part_kernel(const uint16_t* __restrict__ y,
-                                                      const uint16_t* __restrict__ doT,
+                                                      const uint16_t* __restrict__ dO,
                                                       float* __restrict__ part,
-                                                      long long nblocks, int parts) {
-  constexpr int P = 72;
+                                                      long long nblocks, int parts, int N, int L,
+                                                      int T) {
+  constexpr int P = D == 128 ? 152 : 72;
   constexpr int TILES = (D / 32) * (D / 32);
   constexpr int TPW = TILES / 4;
-  __shared__ __attribute__((aligned(16))) uint16_t yt[D * P];
-  __shared__ __attribute__((aligned(16))) uint16_t dt[D * P];
+  __shared__ __attribute__((aligned(16))) uint16_t ys[64 * P];
+  __shared__ __attribute__((aligned(16))) uint16_t ds_[64 * P];
   const int w = blockIdx.x;
   const long long b0 = nblocks * w / parts, b1 = nblocks * (w + 1) / parts;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n32 = lane & 31, hl = lane >> 5;
+  (void)hl;
   f32x16 acc[TPW];
 #pragma unroll
   for (int x = 0; x < TPW; ++x) acc[x] = f32x16{};
   for (long long b = b0; b < b1; ++b) {
+    const int blk = static_cast<int>(b % T);
     const uint16_t* ysrc = y + static_cast<size_t>(b) * kBlock * D;
-    const uint16_t* dsrc = doT + static_cast<size_t>(b) * kBlock * D;
+    const uint16_t* dsrc = dO + static_cast<size_t>(b) * kBlock * D;
     __syncthreads();
     for (int e = tid; e < kBlock * D / 8; e += 256) {
-      const int t = e / (D / 8), c8 = e % (D / 8);
-      const u32x4 val = ld16(ysrc + static_cast<size_t>(t) * D + 8 * c8);
-#pragma unroll
-      for (int s = 0; s < 8; ++s) yt[(8 * c8 + s) * P + t] = static_cast<uint16_t>(u4_elem(val, s));
-      const int r = e >> 3, m = e & 7;
-      st16(&dt[r * P + 8 * m], ld16(dsrc + static_cast<size_t>(r) * kBlock + 8 * m));
+      const int t = e / (D / 8), c8 = 8 * (e % (D / 8));
+      st16(&ys[t * P + c8], ld16(ysrc + static_cast<size_t>(t) * D + c8));
+      const bool ok = blk * kBlock + t < L;   // padded rows of dO do not count
+      st16(&ds_[t * P + c8], ok ? ld16(dsrc + static_cast<size_t>(t) * D + c8) : u32x4{0u, 0u, 0u, 0u});
     }
     __syncthreads();
+    // dW^T[c][o] = sum_t Y[t][c] dO[t][o]: both operands by transpose reads (k = t)
 #pragma unroll
     for (int x = 0; x < TPW; ++x) {
       const int tt = wave * TPW + x;
       const int ct = tt / (D / 32), ot = tt % (D / 32);
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
-        acc[x] = mfma32(as_bf16x8(ld16(&yt[(32 * ct + n32) * P + 16 * kk + 8 * hl])),
-                        as_bf16x8(ld16(&dt[(32 * ot + n32) * P + 16 * kk + 8 * hl])), acc[x]);
+        acc[x] = mfma32(lds_op32_tr<false>(ys, P, 16 * kk, 32 * ct, lane),
+                        lds_op32_tr<false>(ds_, P, 16 * kk, 32 * ot, lane), acc[x]);
     }
   }
   float* out = part + static_cast<size_t>(w) * D * D;
@@ -617,7 +632,7 @@ __global__ __launch_bounds__(256) void dw_part_kernel(const uint16_t* __restrict
     const int ct = tt / (D / 32), ot = tt % (D / 32);
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const int c = 32 * ct + 8 * (e / 4) + 4 * hl + (e % 4);
+      const int c = 32 * ct + 8 * (e / 4) + 4 * (lane >> 5) + (e % 4);
       const int o = 32 * ot + n32;
       out[static_cast<size_t>(o) * D + c] = acc[x][e];   // dW[o][c]
     }
@@ -655,43 +670,43 @@ hipError_t launch_bwd_prep(const Dims& d, const uint16_t* q, const uint16_t* o,
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_q(const Dims& d, const uint16_t* q, const uint16_t* k, const uint16_t* kT,
-                        const uint16_t* v, const uint16_t* dO, const float* lse,
-                        const float* dsum, const int32_t* lut, const int32_t* lut_cnt, float* dq,
-                        hipStream_t s) {
+hipError_t launch_bwd_q(const Dims& d, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                        const uint16_t* dO, const float* lse, const float* dsum,
+                        const int32_t* lut, const int32_t* lut_cnt, float* dq, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(d.BH() * d.T));
   if (d.D == 128)
-    hipLaunchKernelGGL(bwd_q_kernel<128>, grid, dim3(256), 0, s, q, k, kT, v, dO, lse, dsum, lut,
+    hipLaunchKernelGGL(bwd_q_kernel<128>, grid, dim3(256), 0, s, q, k, v, dO, lse, dsum, lut,
                        lut_cnt, dq, d.N, d.L, d.T, d.scale);
   else
-    hipLaunchKernelGGL(bwd_q_kernel<64>, grid, dim3(256), 0, s, q, k, kT, v, dO, lse, dsum, lut,
+    hipLaunchKernelGGL(bwd_q_kernel<64>, grid, dim3(256), 0, s, q, k, v, dO, lse, dsum, lut,
                        lut_cnt, dq, d.N, d.L, d.T, d.scale);
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_kv(const Dims& d, const uint16_t* q, const uint16_t* qT, const uint16_t* k,
-                         const uint16_t* v, const uint16_t* dO, const uint16_t* doT,
-                         const float* lse, const float* dsum, const int32_t* col,
-                         const int32_t* col_cnt, const uint16_t* dh, const float* dz, bool linear,
-                         float* dk, float* dv, hipStream_t s) {
+hipError_t launch_bwd_kv(const Dims& d, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                         const uint16_t* dO, const float* lse, const float* dsum,
+                         const int32_t* col, const int32_t* col_cnt, const uint16_t* dh,
+                         const float* dz, bool linear, float* dk, float* dv, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(d.BH() * d.T));
   if (d.D == 128)
-    hipLaunchKernelGGL(bwd_kv_kernel<128>, grid, dim3(256), 0, s, q, qT, k, v, dO, doT, lse, dsum,
-                       col, col_cnt, dh, dz, linear, dk, dv, d.N, d.L, d.T, d.scale);
+    hipLaunchKernelGGL(bwd_kv_kernel<128>, grid, dim3(512), 0, s, q, k, v, dO, lse, dsum, col,
+                       col_cnt, dh, dz, linear, dk, dv, d.N, d.L, d.T, d.scale);
   else
-    hipLaunchKernelGGL(bwd_kv_kernel<64>, grid, dim3(256), 0, s, q, qT, k, v, dO, doT, lse, dsum,
-                       col, col_cnt, dh, dz, linear, dk, dv, d.N, d.L, d.T, d.scale);
+    hipLaunchKernelGGL(bwd_kv_kernel<64>, grid, dim3(512), 0, s, q, k, v, dO, lse, dsum, col,
+                       col_cnt, dh, dz, linear, dk, dv, d.N, d.L, d.T, d.scale);
   return hipGetLastError();
 }
 
-hipError_t launch_dw(const Dims& d, const uint16_t* y, const uint16_t* doT, float* part, float* dw,
+hipError_t launch_dw(const Dims& d, const uint16_t* y, const uint16_t* dO, float* part, float* dw,
                      hipStream_t s) {
   const long long nblocks = d.BH() * d.T;
   const int parts = static_cast<int>(std::min<long long>(kDwParts, nblocks));
   if (d.D == 128)
-    hipLaunchKernelGGL(dw_part_kernel<128>, dim3(parts), dim3(256), 0, s, y, doT, part, nblocks, parts);
+    hipLaunchKernelGGL(dw_part_kernel<128>, dim3(parts), dim3(256), 0, s, y, dO, part, nblocks,
+                       parts, d.N, d.L, d.T);
   else
-    hipLaunchKernelGGL(dw_part_kernel<64>, dim3(parts), dim3(256), 0, s, y, doT, part, nblocks, parts);
+    hipLaunchKernelGGL(dw_part_kernel<64>, dim3(parts), dim3(256), 0, s, y, dO, part, nblocks,
+                       parts, d.N, d.L, d.T);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int dd = d.D * d.D;

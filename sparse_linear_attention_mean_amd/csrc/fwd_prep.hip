@@ -23,12 +23,17 @@ namespace sla {
 // reads as its A operand: states[bh][j / 8][n][j % 8], n = c*D + a for h^T,
 // n = D*D + a for bf16(z), n = D*D + D + a for bf16(z - bf16(z)).  One
 // workgroup handles 8 consecutive key blocks so that every lane can write the
-// 8 block values of one state entry as a single 16-byte store.
+// 8 block values of one state entry as a single 16-byte store; D = 128 splits
+// the 16 output tiles over two workgroups (one 32x32 tile per wave).
+// The tiles are staged row-major (a plain copy, phi applied on the way) and
+// both MFMA operands, which run over tokens, come from LDS transpose reads.
 // phi(k) is rounded to bf16 once and the same rounded values feed h and z.
 // kbar sums column a in token order 0..63 in fp32, exactly as pool_kernel
 // does, so the pooled K is bit-identical in both paths.
-// The kernel also writes V^T per key block, vT[bh][j][c][t] (bf16, padded
-// tokens zero), which the attention kernels stage without transposing.
+// BWD = true turns the same kernel into the backward's query-side state
+// builder: Y = Q, X = dN (bf16 rows), and the vector part is weighted,
+// dZ_i[a] = sum_r d_r * phi(q_r)[a] with the per-row weights d_r; no pooled
+// mean is written then.
 // ---------------------------------------------------------------------------
 template <int D>
 struct KvCfg {
@@ -36,24 +41,20 @@ struct KvCfg {
   static constexpr int kWaves = kThreads / 64;
   static constexpr int kTiles = (D / 32) * (D / 32);   // 32x32 tiles of h^T
   static constexpr int kTileGroups = kTiles / kWaves;  // workgroups per 8-block group (1 tile per wave)
-  static constexpr int kPitch = 72;                    // LDS row pitch (bf16): 64 tokens + pad
+  static constexpr int kPitch = D == 128 ? 152 : 72;   // LDS row pitch (bf16), conflict-free transpose reads
 };
 
-// BWD = true turns the same kernel into the backward's query-side state
-// builder: Y = Q, X = dN (bf16 rows), and the vector part is weighted,
-// dZ_i[a] = sum_r d_r * phi(q_r)[a] with the per-row weights d_r; no pooled
-// mean and no V^T are written then.
 template <int D, bool BWD>
 __global__ __launch_bounds__(KvCfg<D>::kThreads) void kv_state_kernel(
     const uint16_t* __restrict__ ysrc, const uint16_t* __restrict__ xsrc,
     const float* __restrict__ wrow, float* __restrict__ kbar, uint16_t* __restrict__ states,
-    uint16_t* __restrict__ vT, int N, int L, int T, int Tp) {
+    int N, int L, int T, int Tp) {
   using C = KvCfg<D>;
   constexpr int P = C::kPitch;
   constexpr int NB = D * D + 2 * D;
-  __shared__ uint16_t pk[D * P];   // phi(Y)^T, bf16
-  __shared__ uint16_t vt[D * P];   // X^T
-  __shared__ uint16_t kt[D * P];   // Y^T (raw, for the pooled mean)
+  __shared__ __attribute__((aligned(16))) uint16_t pk[64 * P];   // phi(Y)[t][a], bf16
+  __shared__ __attribute__((aligned(16))) uint16_t xs[64 * P];   // X[t][c]
+  __shared__ __attribute__((aligned(16))) uint16_t ks[64 * P];   // Y[t][a] (raw, for the pooled mean)
   __shared__ uint16_t zst[2 * D * 8];
   __shared__ float wts[kBlock];
 
@@ -62,7 +63,7 @@ __global__ __launch_bounds__(KvCfg<D>::kThreads) void kv_state_kernel(
   const int tgrp = wg % C::kTileGroups;      // which tiles of h^T this workgroup computes
   const int bh = (wg / C::kTileGroups) / groups;
   const int g = (wg / C::kTileGroups) % groups;
-  const bool lead = tgrp == 0;               // writes V^T, kbar and z
+  const bool lead = tgrp == 0;               // writes kbar and z
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -97,19 +98,20 @@ __global__ __launch_bounds__(KvCfg<D>::kThreads) void kv_state_kernel(
 #pragma unroll
   for (int jj = 0; jj < 8; ++jj) {
     const int j = g * 8 + jj;
-    // transpose the staged rows into LDS; invalid tokens are zero in all three
+    // stage the rows (invalid tokens are zero in all three tiles)
     {
-      const int tok0 = j * kBlock + 2 * rp;
-      const bool ok0 = j < T && tok0 < L, ok1 = j < T && tok0 + 1 < L;
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const int row = (8 * c8 + s) * P + 2 * rp;
-        const uint32_t k0 = u4_elem(rk[0], s), k1 = u4_elem(rk[1], s);
-        if constexpr (!BWD) *reinterpret_cast<uint32_t*>(&kt[row]) = k0 | (k1 << 16);
-        *reinterpret_cast<uint32_t*>(&vt[row]) = u4_elem(rv[0], s) | (u4_elem(rv[1], s) << 16);
-        const float p0 = ok0 ? phi(bf16_to_f32(static_cast<uint16_t>(k0))) : 0.f;
-        const float p1 = ok1 ? phi(bf16_to_f32(static_cast<uint16_t>(k1))) : 0.f;
-        *reinterpret_cast<uint32_t*>(&pk[row]) = pack_bf16x2(p0, p1);
+      for (int r = 0; r < 2; ++r) {
+        const int row = (2 * rp + r) * P + 8 * c8;
+        st16(&xs[row], rv[r]);
+        if constexpr (!BWD) st16(&ks[row], rk[r]);
+        const int tok = j * kBlock + 2 * rp + r;
+        const bool ok = j < T && tok < L;
+        float f[8];
+#pragma unroll
+        for (int s2 = 0; s2 < 8; ++s2)
+          f[s2] = ok ? phi(bf16_to_f32(static_cast<uint16_t>(u4_elem(rk[r], s2)))) : 0.f;
+        st16(&pk[row], __builtin_bit_cast(u32x4, cvt_bf16x8(f)));
       }
       if constexpr (BWD) {
         if (lead && tid < kBlock) {
@@ -120,24 +122,13 @@ __global__ __launch_bounds__(KvCfg<D>::kThreads) void kv_state_kernel(
     }
     __syncthreads();
     if (jj < 7) load(j + 1);
-    if constexpr (!BWD) {
-      if (lead && j < T) {
-        // V^T of this key block: D rows of 64 tokens, 8 chunks of 16 bytes per row
-        uint16_t* dst = vT + (static_cast<size_t>(bh) * T + j) * D * kBlock;
-        for (int e = tid; e < D * 8; e += C::kThreads) {
-          const int c = e >> 3, m = e & 7;
-          st16(dst + c * kBlock + 8 * m, ld16(&vt[c * P + 8 * m]));
-        }
-      }
-    }
-
     {
+      // C[m = c][n = a] = sum_t X[t][c] phi(Y)[t][a]: both operands by transpose reads (k = t)
       f32x16 acc = {};
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        acc = mfma32(as_bf16x8(ld16(&vt[(32 * ct + n32) * P + 16 * kk + 8 * hl])),
-                     as_bf16x8(ld16(&pk[(32 * at + n32) * P + 16 * kk + 8 * hl])), acc);
-      }
+      for (int kk = 0; kk < 4; ++kk)
+        acc = mfma32(lds_op32_tr<false>(xs, P, 16 * kk, 32 * ct, lane),
+                     lds_op32_tr<false>(pk, P, 16 * kk, 32 * at, lane), acc);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const uint32_t hb = f32_to_bf16(acc[i]);
@@ -149,13 +140,13 @@ __global__ __launch_bounds__(KvCfg<D>::kThreads) void kv_state_kernel(
     }
     if (lead && tid < D) {
       const int a = tid;
-      float zs = 0.f, ks = 0.f;
+      float zs = 0.f, ksum = 0.f;
       for (int t = 0; t < kBlock; ++t) {
         if constexpr (BWD) {
-          zs = __fmaf_rn(wts[t], bf16_to_f32(pk[a * P + t]), zs);
+          zs = __fmaf_rn(wts[t], bf16_to_f32(pk[t * P + a]), zs);
         } else {
-          zs += bf16_to_f32(pk[a * P + t]);
-          ks += bf16_to_f32(kt[a * P + t]);
+          zs += bf16_to_f32(pk[t * P + a]);
+          ksum += bf16_to_f32(ks[t * P + a]);
         }
       }
       const uint16_t zh = f32_to_bf16(zs);
@@ -164,7 +155,7 @@ __global__ __launch_bounds__(KvCfg<D>::kThreads) void kv_state_kernel(
       if constexpr (!BWD) {
         if (j < T) {
           const int nvalid = min(kBlock, L - j * kBlock);
-          kbar[(static_cast<size_t>(bh) * T + j) * D + a] = ks / static_cast<float>(nvalid);
+          kbar[(static_cast<size_t>(bh) * T + j) * D + a] = ksum / static_cast<float>(nvalid);
         }
       }
     }
@@ -182,34 +173,6 @@ __global__ __launch_bounds__(KvCfg<D>::kThreads) void kv_state_kernel(
   if (!lead) return;
   for (int e = tid; e < 2 * D; e += C::kThreads)
     st16(out + (static_cast<size_t>(D) * D + e) * 8, ld16(&zst[e * 8]));
-}
-
-// ---------------------------------------------------------------------------
-// v_transpose: vT[bh][j][c][t] = v[bh][64 j + t][c] (zero for padded tokens),
-// for the paths that run no state builder (all blocks critical).
-// ---------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(256) void v_transpose_kernel(const uint16_t* __restrict__ v,
-                                                          uint16_t* __restrict__ vT, int N, int L,
-                                                          int T) {
-  __shared__ uint16_t tile[D * 72];
-  const long long blk = blockIdx.x;   // bh * T + j
-  const int j = static_cast<int>(blk % T);
-  const long long bh = blk / T;
-  const uint16_t* src = v + (static_cast<size_t>(bh) * N + static_cast<size_t>(j) * kBlock) * D;
-  for (int e = threadIdx.x; e < kBlock * D / 8; e += 256) {
-    const int t = e / (D / 8), c8 = e % (D / 8);
-    u32x4 val = u32x4{0u, 0u, 0u, 0u};
-    if (j * kBlock + t < L) val = ld16(src + static_cast<size_t>(t) * D + 8 * c8);
-#pragma unroll
-    for (int s = 0; s < 8; ++s) tile[(8 * c8 + s) * 72 + t] = static_cast<uint16_t>(u4_elem(val, s));
-  }
-  __syncthreads();
-  uint16_t* dst = vT + static_cast<size_t>(blk) * D * kBlock;
-  for (int e = threadIdx.x; e < D * 8; e += 256) {
-    const int c = e >> 3, m = e & 7;
-    st16(dst + c * kBlock + 8 * m, ld16(&tile[c * 72 + 8 * m]));
-  }
 }
 
 // ---------------------------------------------------------------------------
@@ -430,35 +393,28 @@ __global__ void fill_mask_kernel(int8_t* __restrict__ mask, long long n, int8_t 
 // launchers
 // ---------------------------------------------------------------------------
 hipError_t launch_kv_state(const Dims& d, const uint16_t* k, const uint16_t* v, float* kbar,
-                           uint16_t* states, uint16_t* vT, hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>(d.BH() * (d.Tp / 8) * KvCfg<128>::kTileGroups / (d.D == 128 ? 1 : KvCfg<128>::kTileGroups)));
+                           uint16_t* states, hipStream_t s) {
+  const int tg = d.D == 128 ? KvCfg<128>::kTileGroups : KvCfg<64>::kTileGroups;
+  const dim3 grid(static_cast<unsigned>(d.BH() * (d.Tp / 8) * tg));
   if (d.D == 128)
     hipLaunchKernelGGL((kv_state_kernel<128, false>), grid, dim3(KvCfg<128>::kThreads), 0, s, k, v,
-                       nullptr, kbar, states, vT, d.N, d.L, d.T, d.Tp);
+                       nullptr, kbar, states, d.N, d.L, d.T, d.Tp);
   else
     hipLaunchKernelGGL((kv_state_kernel<64, false>), grid, dim3(KvCfg<64>::kThreads), 0, s, k, v,
-                       nullptr, kbar, states, vT, d.N, d.L, d.T, d.Tp);
+                       nullptr, kbar, states, d.N, d.L, d.T, d.Tp);
   return hipGetLastError();
 }
 
 hipError_t launch_dstate(const Dims& d, const uint16_t* q, const uint16_t* dn, const float* ddel,
                          uint16_t* states, hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>(d.BH() * (d.Tp / 8) * KvCfg<128>::kTileGroups / (d.D == 128 ? 1 : KvCfg<128>::kTileGroups)));
+  const int tg = d.D == 128 ? KvCfg<128>::kTileGroups : KvCfg<64>::kTileGroups;
+  const dim3 grid(static_cast<unsigned>(d.BH() * (d.Tp / 8) * tg));
   if (d.D == 128)
     hipLaunchKernelGGL((kv_state_kernel<128, true>), grid, dim3(KvCfg<128>::kThreads), 0, s, q, dn,
-                       ddel, nullptr, states, nullptr, d.N, d.L, d.T, d.Tp);
+                       ddel, nullptr, states, d.N, d.L, d.T, d.Tp);
   else
     hipLaunchKernelGGL((kv_state_kernel<64, true>), grid, dim3(KvCfg<64>::kThreads), 0, s, q, dn,
-                       ddel, nullptr, states, nullptr, d.N, d.L, d.T, d.Tp);
-  return hipGetLastError();
-}
-
-hipError_t launch_v_transpose(const Dims& d, const uint16_t* v, uint16_t* vT, hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>(d.BH() * d.T));
-  if (d.D == 128)
-    hipLaunchKernelGGL(v_transpose_kernel<128>, grid, dim3(256), 0, s, v, vT, d.N, d.L, d.T);
-  else
-    hipLaunchKernelGGL(v_transpose_kernel<64>, grid, dim3(256), 0, s, v, vT, d.N, d.L, d.T);
+                       ddel, nullptr, states, d.N, d.L, d.T, d.Tp);
   return hipGetLastError();
 }
 

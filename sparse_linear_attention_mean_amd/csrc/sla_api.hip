@@ -140,15 +140,11 @@ WorkspaceLayout workspace_layout(const Dims& d) {
   w.rbits = take(BH * d.Tp * (d.Tp / 32) * 4);
   w.cbits = take(BH * d.Tp * (d.Tp / 32) * 4);
   w.states = take(BH * (d.Tp / 8) * d.NB * 8 * 2);
-  w.vT = take(BH * d.N * d.D * 2);
   w.dstate = take(BH * d.T * d.D * d.D * 2);
   w.dstate_z = take(BH * d.T * 2 * d.D * 4);
   w.dsum = take(BH * d.N * 4);
   w.ddel = take(BH * d.N * 4);
   w.dn = take(BH * d.N * d.D * 2);
-  w.kT = take(BH * d.N * d.D * 2);
-  w.qT = take(BH * d.N * d.D * 2);
-  w.doT = take(BH * d.N * d.D * 2);
   w.wT = take(static_cast<size_t>(d.D) * d.D * 2);
   w.dw_part = take(static_cast<size_t>(kDwParts) * d.D * d.D * 4);
   w.total = off;
@@ -239,7 +235,6 @@ sla_status sla_forward(const sla_config* cfg, const void* q, const void* k, cons
   auto* lut_cnt = reinterpret_cast<int32_t*>(ws + wl.lut_cnt);
   auto* rbits = reinterpret_cast<uint32_t*>(ws + wl.rbits);
   auto* states = reinterpret_cast<uint16_t*>(ws + wl.states);
-  auto* vT = reinterpret_cast<uint16_t*>(ws + wl.vT);
   auto* hst = reinterpret_cast<uint16_t*>(sv + sl.hst);
   auto* zst = reinterpret_cast<float*>(sv + sl.zst);
   const auto* q16 = static_cast<const uint16_t*>(q);
@@ -253,19 +248,13 @@ sla_status sla_forward(const sla_config* cfg, const void* q, const void* k, cons
 
   if (dense) {
     SLA_CHECK(launched(launch_fill_mask(d, mask, 1, s), "fill_mask"));
-    SLA_CHECK(stg.begin(SLA_STAGE_KV_STATE));
-    SLA_CHECK(launched(launch_v_transpose(d, v16, vT, s), "v_transpose"));
-    SLA_CHECK(stg.end(SLA_STAGE_KV_STATE));
   } else {
-    SLA_CHECK(stg.begin(SLA_STAGE_KV_STATE));
     if (linear || !given) {
-      SLA_CHECK(launched(launch_kv_state(d, k16, v16, reinterpret_cast<float*>(ws + wl.kbar), states,
-                                         vT, s),
+      SLA_CHECK(stg.begin(SLA_STAGE_KV_STATE));
+      SLA_CHECK(launched(launch_kv_state(d, k16, v16, reinterpret_cast<float*>(ws + wl.kbar), states, s),
                          "kv_state"));
-    } else {
-      SLA_CHECK(launched(launch_v_transpose(d, v16, vT, s), "v_transpose"));
+      SLA_CHECK(stg.end(SLA_STAGE_KV_STATE));
     }
-    SLA_CHECK(stg.end(SLA_STAGE_KV_STATE));
     if (!given) {
       SLA_CHECK(stg.begin(SLA_STAGE_POOL_Q));
       SLA_CHECK(launched(launch_pool(d, q16, reinterpret_cast<float*>(ws + wl.qbar), s), "pool_q"));
@@ -292,7 +281,7 @@ sla_status sla_forward(const sla_config* cfg, const void* q, const void* k, cons
     }
   }
   SLA_CHECK(stg.begin(SLA_STAGE_ATTENTION));
-  SLA_CHECK(launched(launch_attn_fwd(d, q16, k16, vT, static_cast<const uint16_t*>(w), lut, lut_cnt,
+  SLA_CHECK(launched(launch_attn_fwd(d, q16, k16, v16, static_cast<const uint16_t*>(w), lut, lut_cnt,
                                      dense, linear, hst, zst, static_cast<uint16_t*>(o),
                                      reinterpret_cast<float*>(sv + sl.lse),
                                      reinterpret_cast<float*>(sv + sl.den),
@@ -342,9 +331,6 @@ sla_status sla_backward(const sla_config* cfg, const void* q, const void* k, con
   auto* dsum = reinterpret_cast<float*>(ws + wl.dsum);
   auto* ddel = reinterpret_cast<float*>(ws + wl.ddel);
   auto* dn = reinterpret_cast<uint16_t*>(ws + wl.dn);
-  auto* kT = reinterpret_cast<uint16_t*>(ws + wl.kT);
-  auto* qT = reinterpret_cast<uint16_t*>(ws + wl.qT);
-  auto* doT = reinterpret_cast<uint16_t*>(ws + wl.doT);
   auto* wT = reinterpret_cast<uint16_t*>(ws + wl.wT);
   auto* dwp = reinterpret_cast<float*>(ws + wl.dw_part);
   const auto* q16 = static_cast<const uint16_t*>(q);
@@ -364,9 +350,6 @@ sla_status sla_backward(const sla_config* cfg, const void* q, const void* k, con
   SLA_CHECK(stg.begin(SLA_STAGE_BWD_PRE));
   SLA_CHECK(launched(launch_mask_lists(d, mask, lut, lut_cnt, rbits, col, col_cnt, cbits, s),
                      "mask_lists"));
-  SLA_CHECK(launched(launch_v_transpose(d, k16, kT, s), "k_transpose"));
-  SLA_CHECK(launched(launch_v_transpose(d, q16, qT, s), "q_transpose"));
-  SLA_CHECK(launched(launch_v_transpose(d, do16, doT, s), "do_transpose"));
   SLA_CHECK(launched(launch_w_transpose(d, static_cast<const uint16_t*>(w), wT, s), "w_transpose"));
   SLA_CHECK(launched(launch_bwd_prep(d, q16, o16, do16, wT, den, y, hst, zst, linear, dsum, ddel, dn,
                                      dq, s),
@@ -377,14 +360,14 @@ sla_status sla_backward(const sla_config* cfg, const void* q, const void* k, con
   }
   SLA_CHECK(stg.end(SLA_STAGE_BWD_PRE));
   SLA_CHECK(stg.begin(SLA_STAGE_BWD_KV));
-  SLA_CHECK(launched(launch_bwd_kv(d, q16, qT, k16, v16, do16, doT, lse, dsum, col, col_cnt, dh, dz,
-                                   linear, dk, dv, s),
+  SLA_CHECK(launched(launch_bwd_kv(d, q16, k16, v16, do16, lse, dsum, col, col_cnt, dh, dz, linear,
+                                   dk, dv, s),
                      "bwd_kv"));
   SLA_CHECK(stg.end(SLA_STAGE_BWD_KV));
   SLA_CHECK(stg.begin(SLA_STAGE_BWD_Q));
-  SLA_CHECK(launched(launch_bwd_q(d, q16, k16, kT, v16, do16, lse, dsum, lut, lut_cnt, dq, s),
+  SLA_CHECK(launched(launch_bwd_q(d, q16, k16, v16, do16, lse, dsum, lut, lut_cnt, dq, s),
                      "bwd_q"));
-  SLA_CHECK(launched(launch_dw(d, y, doT, dwp, dw, s), "dw"));
+  SLA_CHECK(launched(launch_dw(d, y, do16, dwp, dw, s), "dw"));
   SLA_CHECK(stg.end(SLA_STAGE_BWD_Q));
   return SLA_OK;
 }

@@ -44,8 +44,20 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float x) {
   return static_cast<uint16_t>(u >> 16);
 }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> two bf16 (round-to-nearest-even) in one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
+}
+
+// 8 fp32 -> bf16x8 operand (4 packed conversions).
+__device__ __forceinline__ bf16x8 cvt_bf16x8(const float* x) {
+  typedef uint32_t u32x4_ __attribute__((ext_vector_type(4)));
+  const u32x4_ w = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
+                    pack_bf16x2(x[6], x[7])};
+  return __builtin_bit_cast(bf16x8, w);
 }
 
 // elu(x) + 1
@@ -87,6 +99,47 @@ __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<
 __device__ __forceinline__ u32x2 ld8(const void* p) { return *reinterpret_cast<const u32x2*>(p); }
 __device__ __forceinline__ void st16(void* p, const u32x4& v) { *reinterpret_cast<u32x4*>(p) = v; }
 __device__ __forceinline__ void st8(void* p, const u32x2& v) { *reinterpret_cast<u32x2*>(p) = v; }
+
+// ds_read_b64_tr_b16 (gfx950 LDS transpose read).  Within each group of 16
+// lanes, lane i receives element (i % 4) of the 8-byte chunks addressed by
+// lanes 4 s + i / 4 of its group, s = 0..3 (verified on the MI355X).  So when
+// lane c of a group points at row kb + c / 4, column n0 + 4 (c % 4) of a
+// row-major matrix, every lane gets M[kb + s][n0 + c], s = 0..3: four
+// consecutive k values of its own column, i.e. a slice of an MFMA operand
+// whose k index runs down the rows of the LDS tile.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 lds_tr4(const uint16_t* p) {
+  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (s16x4 __attribute__((address_space(3)))*)(p));
+  return __builtin_bit_cast(u32x2, r);
+}
+
+// Operand of v_mfma_f32_32x32x16 from a row-major LDS tile M[k][n] (pitch in
+// elements, a multiple of 4): lane l gets M[r0 + s][n0 + l % 32] for the 8 k
+// slots s, with row r0 + s for s < 4 and row r1 + s - 4 for s >= 4, where
+// (r0, r1) = (kb + 8 h, kb + 8 h + 4) for natural k order, or
+// (kb + 4 h, kb + 8 + 4 h) for the permuted order pi(h, s) that a 32x32 result
+// tile has when it is reused as an operand (h = l / 32).
+template <bool PERMUTED>
+__device__ __forceinline__ bf16x8 lds_op32_tr(const uint16_t* m, int pitch, int kb, int n0,
+                                              int lane) {
+  const int g = lane >> 4, c = lane & 15, h = lane >> 5;
+  const int col = n0 + 16 * (g & 1) + 4 * (c & 3);
+  const int r0 = PERMUTED ? kb + 4 * h + (c >> 2) : kb + 8 * h + (c >> 2);
+  const u32x2 lo = lds_tr4(m + r0 * pitch + col);
+  const u32x2 hi = lds_tr4(m + (r0 + (PERMUTED ? 8 : 4)) * pitch + col);
+  return as_bf16x8(lo, hi);
+}
+
+// Buffer resource over [base, base + bytes) (raw buffer, bounds-checked: reads
+// past the end return zero) and a 16-byte load at voffset + soffset bytes.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           static_cast<int>(bytes), 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
 
 // Workgroup id remapped so that consecutive logical ids share an XCD: the
 // hardware deals workgroups round-robin over the 8 XCDs, each with its own L2.

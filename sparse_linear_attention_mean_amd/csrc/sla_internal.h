@@ -29,13 +29,11 @@ struct WorkspaceLayout {
   size_t col, col_cnt;      // int32 [BH, T, T] critical query blocks per column, int32 [BH, T]
   size_t rbits, cbits;      // uint32 [BH, Tp, Tp/32] marginal bits by row / by column
   size_t states;            // bf16 [BH, Tp/8, NB, 8]  (forward h/z states; backward dH/dZ)
-  size_t vT;                // bf16 [BH, T, D, 64]  V transposed per key block
   size_t dstate;            // bf16 [BH, T, D*D] + fp32 [BH, T, 2, D] aggregated backward states
   size_t dstate_z;
   size_t dsum;              // fp32 [BH, N]  D_r of the backward
   size_t ddel;              // fp32 [BH, N]  linear-denominator gradient per row
   size_t dn;                // bf16 [BH, N, D]  dY / den per row
-  size_t kT, qT, doT;       // bf16 [BH, T, D, 64]  per-block transposes
   size_t wT;                // bf16 [D, D]
   size_t dw_part;           // fp32 [P, D, D] dW partial sums
   size_t total;
@@ -52,8 +50,7 @@ SavedLayout saved_layout(const Dims& d);
 
 // ---- launchers (return hipSuccess or the launch error) ----
 hipError_t launch_kv_state(const Dims& d, const uint16_t* k, const uint16_t* v, float* kbar,
-                           uint16_t* states, uint16_t* vT, hipStream_t s);
-hipError_t launch_v_transpose(const Dims& d, const uint16_t* v, uint16_t* vT, hipStream_t s);
+                           uint16_t* states, hipStream_t s);
 hipError_t launch_dstate(const Dims& d, const uint16_t* q, const uint16_t* dn, const float* ddel,
                          uint16_t* states, hipStream_t s);
 hipError_t launch_pool(const Dims& d, const uint16_t* x, float* xbar, hipStream_t s);
@@ -68,7 +65,7 @@ hipError_t launch_fill_mask(const Dims& d, int8_t* mask, int8_t value, hipStream
 hipError_t launch_aggregate(const Dims& d, const uint32_t* bits, const uint16_t* states,
                             uint16_t* hout, float* zout, hipStream_t s);
 hipError_t launch_attn_fwd(const Dims& d, const uint16_t* q, const uint16_t* k,
-                           const uint16_t* vT, const uint16_t* w, const int32_t* lut,
+                           const uint16_t* v, const uint16_t* w, const int32_t* lut,
                            const int32_t* lut_cnt, bool dense, bool linear,
                            const uint16_t* hst, const float* zst, uint16_t* o, float* lse,
                            float* den, uint16_t* y, hipStream_t s);
@@ -79,16 +76,14 @@ hipError_t launch_bwd_prep(const Dims& d, const uint16_t* q, const uint16_t* o,
                            const uint16_t* dO, const uint16_t* wT, const float* den,
                            const uint16_t* y, const uint16_t* hst, const float* zst, bool linear,
                            float* dsum, float* ddel, uint16_t* dn, float* dq, hipStream_t s);
-hipError_t launch_bwd_q(const Dims& d, const uint16_t* q, const uint16_t* k, const uint16_t* kT,
-                        const uint16_t* v, const uint16_t* dO, const float* lse,
-                        const float* dsum, const int32_t* lut, const int32_t* lut_cnt, float* dq,
-                        hipStream_t s);
-hipError_t launch_bwd_kv(const Dims& d, const uint16_t* q, const uint16_t* qT, const uint16_t* k,
-                         const uint16_t* v, const uint16_t* dO, const uint16_t* doT,
-                         const float* lse, const float* dsum, const int32_t* col,
-                         const int32_t* col_cnt, const uint16_t* dh, const float* dz, bool linear,
-                         float* dk, float* dv, hipStream_t s);
-hipError_t launch_dw(const Dims& d, const uint16_t* y, const uint16_t* doT, float* part, float* dw,
+hipError_t launch_bwd_q(const Dims& d, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                        const uint16_t* dO, const float* lse, const float* dsum,
+                        const int32_t* lut, const int32_t* lut_cnt, float* dq, hipStream_t s);
+hipError_t launch_bwd_kv(const Dims& d, const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                         const uint16_t* dO, const float* lse, const float* dsum,
+                         const int32_t* col, const int32_t* col_cnt, const uint16_t* dh,
+                         const float* dz, bool linear, float* dk, float* dv, hipStream_t s);
+hipError_t launch_dw(const Dims& d, const uint16_t* y, const uint16_t* dO, float* part, float* dw,
                      hipStream_t s);
 
 }  // namespace sla
