@@ -65,21 +65,35 @@ __global__ __launch_bounds__(256, 2) void aggregate_kernel(const uint32_t* __res
 #pragma unroll
     for (int q = 0; q < 8; ++q) acc[m][q] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const uint16_t* sbase = states + static_cast<size_t>(bh) * (Tp / 8) * NB * 8;
+  // A operand (states) through a buffer resource of this head: lane part of the
+  // byte offset in a VGPR, the k step and column tile in the SGPR offset.
+  const uint32_t sbytes = static_cast<uint32_t>(Tp / 8) * NB * 16u;
+  const __amdgpu_buffer_rsrc_t srs = make_rsrc(states + static_cast<size_t>(bh) * (Tp / 8) * NB * 8, sbytes);
+  const uint32_t voff = (static_cast<uint32_t>(g) * NB + r16) * 16u;
   const uint32_t* bbase = bits + static_cast<size_t>(bh) * Tp * words;
   const int ksteps = Tp / 32;
+  // marginal-bit words of this lane's rows; rows past the wave's valid tiles read nothing
+  const uint32_t* brow[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) brow[q] = bbase + static_cast<size_t>(i0 + 16 * q + r16) * words;
 
+  u32x4 an[4];
+  uint32_t wn[8];
+  auto fetch = [&](int kk) {
+    const uint32_t soff = (static_cast<uint32_t>(4 * kk) * NB + n0) * 16u;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) an[m] = buf_ld16(srs, voff, soff + 256u * m);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) wn[q] = q < nval ? brow[q][kk] : 0u;
+  };
+  fetch(0);
   for (int kk = 0; kk < ksteps; ++kk) {
     bf16x8 a[4], b[8];
-    const uint16_t* srow = sbase + (static_cast<size_t>(4 * kk + g) * NB + n0 + r16) * 8;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) a[m] = as_bf16x8(ld16(srow + 16 * m * 8));
+    for (int m = 0; m < 4; ++m) a[m] = as_bf16x8(an[m]);
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      uint32_t word = 0;
-      if (q < nval) word = bbase[static_cast<size_t>(i0 + 16 * q + r16) * words + kk];
-      b[q] = as_bf16x8(table[(word >> (8 * g)) & 0xffu]);
-    }
+    for (int q = 0; q < 8; ++q) b[q] = as_bf16x8(table[(wn[q] >> (8 * g)) & 0xffu]);
+    if (kk + 1 < ksteps) fetch(kk + 1);
 #pragma unroll
     for (int m = 0; m < 4; ++m)
 #pragma unroll

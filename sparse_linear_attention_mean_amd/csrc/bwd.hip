@@ -33,16 +33,6 @@ __global__ void w_transpose_kernel(const uint16_t* __restrict__ w, uint16_t* __r
   wT[e] = w[static_cast<size_t>(o) * D + c];
 }
 
-// 8 bf16 values M[k0 + s][col] (s = 0..7) from a row-major LDS matrix.
-__device__ __forceinline__ bf16x8 lds_col8(const uint16_t* m, int pitch, int k0, int col) {
-  u32x4 r;
-#pragma unroll
-  for (int p = 0; p < 4; ++p)
-    r[p] = static_cast<uint32_t>(m[(k0 + 2 * p) * pitch + col]) |
-           (static_cast<uint32_t>(m[(k0 + 2 * p + 1) * pitch + col]) << 16);
-  return as_bf16x8(r);
-}
-
 // ---------------------------------------------------------------------------
 // bwd_prep: one workgroup (4 waves) per query block i.
 //   dY^T[c][r] = sum_o W[o][c] dO[r][o]             (wave: rows half qh, c half ch)
@@ -60,7 +50,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(
     const uint16_t* __restrict__ hst, const float* __restrict__ zst, float* __restrict__ dsum,
     float* __restrict__ ddel, uint16_t* __restrict__ dn, float* __restrict__ dq, int N, int L,
     int T, bool linear) {
-  constexpr int HP = D + 8;
+  constexpr int HP = D + 8;    // row pitch (keeps three workgroups per CU)
   constexpr int NCC = D / 16;
   constexpr int NT = D / 64;   // 32-wide tiles per wave in each half
   __shared__ __attribute__((aligned(16))) uint16_t hs[D * HP];   // H^T[c][a]
@@ -166,7 +156,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(
     f32x16 acc = {};
 #pragma unroll
     for (int cc = 0; cc < NCC; ++cc) {
-      const bf16x8 a = lds_col8(hs, HP, 16 * cc + 8 * hl, abase + n32);
+      const bf16x8 a = lds_op32_tr<false>(hs, HP, 16 * cc, abase, lane);
       const bf16x8 b = as_bf16x8(ld16(&dns[rloc * HP + 16 * cc + 8 * hl]));
       acc = mfma32(a, b, acc);
     }
