@@ -12,8 +12,9 @@
 //
 // Operands: S in the K-tiled layout states[bh][j / 8][n][j % 8] (bf16), so
 // that one 16-byte load gives a lane the 8 consecutive key blocks an MFMA A
-// operand needs; M0 as 32-bit words of marginal bits per row, expanded to
-// bf16 through a 256-entry LDS table.  C^T[n][i] = sum_j S[j][n] M0[i][j] is
+// operand needs; M0 as 32-bit words of marginal bits, stored word-major
+// (word w of every row contiguous), expanded to bf16 through a 256-entry LDS
+// table.  C^T[n][i] = sum_j S[j][n] M0[i][j] is
 // computed with v_mfma_f32_16x16x32_bf16, fp32 accumulation.  Columns
 // n < D*D are stored as bf16 (H_i transposed, element (c, a) at c*D + a);
 // the 2*D columns after them (z split into two bf16 parts) as fp32.
@@ -25,7 +26,14 @@ namespace sla {
 constexpr int kAggNTile = 64;    // state columns per workgroup
 constexpr int kAggIWave = 128;   // query rows per wave
 constexpr int kAggIChunk = 512;  // query rows per workgroup (4 waves)
+constexpr int kAggKChunk = 512;  // key blocks of the state strip staged in LDS per pass
 
+// One workgroup owns a 64-column strip of S and 512 rows of C.  The strip is
+// shared by the four waves (each owns 128 rows), so it is copied once into
+// LDS with asynchronous global->LDS loads (64 KB per pass of 512 key blocks)
+// instead of being fetched by every wave; the marginal words stream from
+// global memory (they are small and stay in L2) two k-steps ahead, 32
+// contiguous bytes per lane and k-step.
 __global__ __launch_bounds__(256, 2) void aggregate_kernel(const uint32_t* __restrict__ bits,
                                                           const uint16_t* __restrict__ states,
                                                           uint16_t* __restrict__ hout,
@@ -33,6 +41,7 @@ __global__ __launch_bounds__(256, 2) void aggregate_kernel(const uint32_t* __res
                                                           int NB, int DD, int ntiles,
                                                           int ichunks) {
   __shared__ u32x4 table[256];
+  __shared__ __attribute__((aligned(16))) uint16_t strip[kAggKChunk / 8 * kAggNTile * 8];
   const int tid = threadIdx.x;
   {
     uint32_t w[4];
@@ -41,7 +50,6 @@ __global__ __launch_bounds__(256, 2) void aggregate_kernel(const uint32_t* __res
       w[p] = ((tid >> (2 * p)) & 1 ? 0x3F80u : 0u) | ((tid >> (2 * p + 1)) & 1 ? 0x3F800000u : 0u);
     table[tid] = u32x4{w[0], w[1], w[2], w[3]};
   }
-  __syncthreads();
 
   const uint32_t wg = xcd_remap(blockIdx.x, gridDim.x);
   const int nt = wg % ntiles;
@@ -54,10 +62,11 @@ __global__ __launch_bounds__(256, 2) void aggregate_kernel(const uint32_t* __res
   const int g = lane >> 4;
   const int n0 = nt * kAggNTile;
   const int i0 = ic * kAggIChunk + wave * kAggIWave;
-  if (i0 >= Tp) return;
-  const int words = Tp / 32;
-  int nval = (Tp - i0) / 16;     // valid 16-row tiles of this wave
-  if (nval > 8) nval = 8;
+  // Tile q, column r16 of this wave is query row i0 + 8 r16 + q: a lane's eight
+  // rows are consecutive, so its marginal words for one k-step are 32 contiguous
+  // bytes of the word-major bit matrix.
+  const int rbase = i0 + 8 * r16;
+  const bool rows_ok = rbase < Tp;   // lanes past the padded row count compute, never store
 
   f32x4 acc[4][8];
 #pragma unroll
@@ -65,47 +74,63 @@ __global__ __launch_bounds__(256, 2) void aggregate_kernel(const uint32_t* __res
 #pragma unroll
     for (int q = 0; q < 8; ++q) acc[m][q] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // A operand (states) through a buffer resource of this head: lane part of the
-  // byte offset in a VGPR, the k step and column tile in the SGPR offset.
-  const uint32_t sbytes = static_cast<uint32_t>(Tp / 8) * NB * 16u;
-  const __amdgpu_buffer_rsrc_t srs = make_rsrc(states + static_cast<size_t>(bh) * (Tp / 8) * NB * 8, sbytes);
-  const uint32_t voff = (static_cast<uint32_t>(g) * NB + r16) * 16u;
-  const uint32_t* bbase = bits + static_cast<size_t>(bh) * Tp * words;
+  const uint16_t* sbase = states + static_cast<size_t>(bh) * (Tp / 8) * NB * 8;
   const int ksteps = Tp / 32;
-  // marginal-bit words of this lane's rows; rows past the wave's valid tiles read nothing
-  const uint32_t* brow[8];
-#pragma unroll
-  for (int q = 0; q < 8; ++q) brow[q] = bbase + static_cast<size_t>(i0 + 16 * q + r16) * words;
-
-  u32x4 an[4];
-  uint32_t wn[8];
-  auto fetch = [&](int kk) {
-    const uint32_t soff = (static_cast<uint32_t>(4 * kk) * NB + n0) * 16u;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) an[m] = buf_ld16(srs, voff, soff + 256u * m);
-#pragma unroll
-    for (int q = 0; q < 8; ++q) wn[q] = q < nval ? brow[q][kk] : 0u;
+  const uint32_t* bcol = bits + static_cast<size_t>(bh) * ksteps * Tp + (rows_ok ? rbase : 0);
+  struct Words {
+    u32x4 lo, hi;   // the words of rows rbase .. rbase + 3 and rbase + 4 .. rbase + 7
   };
-  fetch(0);
-  for (int kk = 0; kk < ksteps; ++kk) {
+  Words w0, w1;
+  auto fetch = [&](Words& w, int kk) {
+    const int kc = kk < ksteps ? kk : ksteps - 1;   // past the end: a harmless re-read
+    w.lo = ld16(bcol + static_cast<size_t>(kc) * Tp);
+    w.hi = ld16(bcol + static_cast<size_t>(kc) * Tp + 4);
+  };
+  // one k-step (32 key blocks): A = S^T tile from the staged strip, B = bits -> bf16
+  auto step = [&](const Words& w, int kl) {
     bf16x8 a[4], b[8];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) a[m] = as_bf16x8(an[m]);
+    for (int m = 0; m < 4; ++m) a[m] = as_bf16x8(ld16(strip + ((4 * kl + g) * kAggNTile + 16 * m + r16) * 8));
 #pragma unroll
-    for (int q = 0; q < 8; ++q) b[q] = as_bf16x8(table[(wn[q] >> (8 * g)) & 0xffu]);
-    if (kk + 1 < ksteps) fetch(kk + 1);
+    for (int q = 0; q < 8; ++q)
+      b[q] = as_bf16x8(table[((q < 4 ? w.lo[q & 3] : w.hi[q & 3]) >> (8 * g)) & 0xffu]);
 #pragma unroll
     for (int m = 0; m < 4; ++m)
 #pragma unroll
       for (int q = 0; q < 8; ++q) acc[m][q] = mfma16(a[m], b[q], acc[m][q]);
+  };
+
+  fetch(w0, 0);
+  fetch(w1, 1);
+  for (int kc0 = 0; kc0 < Tp; kc0 += kAggKChunk) {
+    const int kn = Tp - kc0 < kAggKChunk ? Tp - kc0 : kAggKChunk;   // multiple of 32
+    __syncthreads();   // table ready / previous pass fully consumed
+    for (int gi = wave; gi < kn / 8; gi += 4)
+      gl_to_lds16(sbase + ((static_cast<size_t>(kc0 / 8 + gi)) * NB + n0 + lane) * 8,
+                  strip + gi * kAggNTile * 8);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    const int k0 = kc0 / 32;
+    for (int kl = 0; kl < kn / 32; kl += 2) {
+      step(w0, kl);
+      fetch(w0, k0 + kl + 2);
+      if (kl + 1 >= kn / 32) break;
+      step(w1, kl + 1);
+      fetch(w1, k0 + kl + 3);
+    }
+    if ((kn / 32) & 1) {   // odd k-step count: the next pass starts with w1
+      const Words t = w0;
+      w0 = w1;
+      w1 = t;
+    }
   }
 
-  // acc[m][q][s] = C^T[n0 + 16 m + 4 g + s][i0 + 16 q + r16]
+  // acc[m][q][s] = C^T[n0 + 16 m + 4 g + s][rbase + q]
   if (n0 < DD) {
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-      const int i = i0 + 16 * q + r16;
-      if (q >= nval || i >= T) continue;
+      const int i = rbase + q;
+      if (!rows_ok || i >= T) continue;
       uint16_t* dst = hout + (static_cast<size_t>(bh) * T + i) * DD + n0 + 4 * g;
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
@@ -117,8 +142,8 @@ __global__ __launch_bounds__(256, 2) void aggregate_kernel(const uint32_t* __res
     const int zw = NB - DD;
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-      const int i = i0 + 16 * q + r16;
-      if (q >= nval || i >= T) continue;
+      const int i = rbase + q;
+      if (!rows_ok || i >= T) continue;
       float* dst = zout + (static_cast<size_t>(bh) * T + i) * zw + (n0 - DD) + 4 * g;
 #pragma unroll
       for (int m = 0; m < 4; ++m)

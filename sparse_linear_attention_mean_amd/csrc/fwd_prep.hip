@@ -270,7 +270,7 @@ __global__ __launch_bounds__(256) void classify_kernel(const float* __restrict__
   const int words = Tp / 32;
   if (i >= T) {
     if (rbits)
-      for (int w = tid; w < words; w += 256) rbits[(bh * Tp + i) * words + w] = 0u;
+      for (int w = tid; w < words; w += 256) rbits[(bh * words + w) * Tp + i] = 0u;
     return;
   }
   int n2 = 1;
@@ -318,14 +318,14 @@ __global__ __launch_bounds__(256) void classify_kernel(const float* __restrict__
       if (lane == 0) lut_cnt[bh * T + i] = cnt;
     }
     if (rbits) {
-      uint32_t* brow = rbits + (bh * Tp + i) * words;
+      uint32_t* brow = rbits + bh * words * Tp + i;   // word w of this row at brow[w * Tp]
       for (int base = 0; base < Tp; base += 64) {
         const int j = base + lane;
         const bool f = j < T && cls[j] == 0;
         const unsigned long long bal = __ballot(f);
         if (lane == 0) {
-          brow[base / 32] = static_cast<uint32_t>(bal);
-          if (base / 32 + 1 < words) brow[base / 32 + 1] = static_cast<uint32_t>(bal >> 32);
+          brow[(base / 32) * Tp] = static_cast<uint32_t>(bal);
+          if (base / 32 + 1 < words) brow[(base / 32 + 1) * Tp] = static_cast<uint32_t>(bal >> 32);
         }
       }
     }
@@ -356,10 +356,10 @@ __global__ __launch_bounds__(64) void mask_lists_kernel(const int8_t* __restrict
   int32_t* cnts = by_col ? col_cnt : lut_cnt;
   uint32_t* bits = by_col ? cbits : rbits;
   if (list == nullptr) return;
-  uint32_t* brow = bits ? bits + (bh * Tp + x) * words : nullptr;
+  uint32_t* brow = bits ? bits + bh * words * Tp + x : nullptr;   // word w at brow[w * Tp]
   if (x >= T) {
     if (brow)
-      for (int w = lane; w < words; w += 64) brow[w] = 0u;
+      for (int w = lane; w < words; w += 64) brow[w * Tp] = 0u;
     return;
   }
   const int8_t* m = mask + bh * T * T;
@@ -376,8 +376,8 @@ __global__ __launch_bounds__(64) void mask_lists_kernel(const int8_t* __restrict
     cnt += __popcll(bc);
     const unsigned long long bm = __ballot(marg);
     if (brow && lane == 0) {
-      brow[base / 32] = static_cast<uint32_t>(bm);
-      if (base / 32 + 1 < words) brow[base / 32 + 1] = static_cast<uint32_t>(bm >> 32);
+      brow[(base / 32) * Tp] = static_cast<uint32_t>(bm);
+      if (base / 32 + 1 < words) brow[(base / 32 + 1) * Tp] = static_cast<uint32_t>(bm >> 32);
     }
   }
   if (lane == 0) cnts[bh * T + x] = cnt;

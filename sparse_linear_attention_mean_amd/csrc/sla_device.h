@@ -143,6 +143,15 @@ __device__ __forceinline__ u32x4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t vof
 
 // Workgroup id remapped so that consecutive logical ids share an XCD: the
 // hardware deals workgroups round-robin over the 8 XCDs, each with its own L2.
+// Asynchronous 16-byte global -> LDS copy (global_load_lds_dwordx4): lane l of
+// the wave writes its 16 bytes at lds_base + 16 l; lds_base must be uniform.
+// Completion is tracked by vmcnt like any other vector load.
+__device__ __forceinline__ void gl_to_lds16(const void* gsrc, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(
+      (__attribute__((address_space(1))) void*)(const_cast<void*>(gsrc)),
+      (__attribute__((address_space(3))) void*)(lds_base), 16, 0, 0);
+}
+
 __device__ __forceinline__ uint32_t xcd_remap(uint32_t bid, uint32_t total) {
   if (total % 8u != 0u) return bid;
   return (bid % 8u) * (total / 8u) + bid / 8u;

@@ -27,7 +27,8 @@ struct WorkspaceLayout {
   size_t scores;            // fp32 [BH, T, T]
   size_t lut, lut_cnt;      // int32 [BH, T, T] critical key blocks per row (ascending), int32 [BH, T]
   size_t col, col_cnt;      // int32 [BH, T, T] critical query blocks per column, int32 [BH, T]
-  size_t rbits, cbits;      // uint32 [BH, Tp, Tp/32] marginal bits by row / by column
+  size_t rbits, cbits;      // uint32 [BH, Tp/32, Tp] marginal bits by row / by column, word-major:
+                            // bit b of word w of row x is entry (x, 32 w + b)
   size_t states;            // bf16 [BH, Tp/8, NB, 8]  (forward h/z states; backward dH/dZ)
   size_t dstate;            // bf16 [BH, T, D*D] + fp32 [BH, T, 2, D] aggregated backward states
   size_t dstate_z;
