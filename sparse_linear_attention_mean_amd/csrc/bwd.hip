@@ -41,20 +41,44 @@ __global__ void w_transpose_kernel(const uint16_t* __restrict__ w, uint16_t* __r
 //   dphi(q)^T[a][r] = sum_c H[a][c] dN[r][c] + dd_r Z[a]  (wave: rows half, a half)
 //   dq[r][a] = dphi(q)[r][a] phi'(q[r][a])           (initial value of dQ)
 // Rows r >= valid_len and rows with den = 0 get zero linear gradients.
+// Every global read is issued up front: H_i^T and Z_i go straight to LDS
+// with asynchronous copies, the row operands into registers, so their
+// latencies overlap each other and the dY products.
 // ---------------------------------------------------------------------------
+
+// H^T is kept in LDS without row padding; 16-byte chunk k of row c sits in
+// slot k ^ hswz(c), which spreads the four rows one transpose read touches
+// over all banks.
 template <int D>
-__global__ __launch_bounds__(256) void bwd_prep_kernel(
+__device__ __forceinline__ int hswz(int r) {
+  return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
+}
+
+// lds_op32_tr<false> on the swizzled H^T tile
+template <int D>
+__device__ __forceinline__ bf16x8 hs_op32_tr(const uint16_t* hs, int kb, int n0, int lane) {
+  const int g = lane >> 4, c = lane & 15, h = lane >> 5;
+  const int col = n0 + 16 * (g & 1) + 4 * (c & 3);
+  const int r0 = kb + 8 * h + (c >> 2), r1 = r0 + 4;
+  const u32x2 lo = lds_tr4(hs + r0 * D + (((col >> 3) ^ hswz<D>(r0)) << 3) + (col & 7));
+  const u32x2 hi = lds_tr4(hs + r1 * D + (((col >> 3) ^ hswz<D>(r1)) << 3) + (col & 7));
+  return as_bf16x8(lo, hi);
+}
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void bwd_prep_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ o,
     const uint16_t* __restrict__ dO, const uint16_t* __restrict__ wT,
     const float* __restrict__ den, const uint16_t* __restrict__ y,
     const uint16_t* __restrict__ hst, const float* __restrict__ zst, float* __restrict__ dsum,
     float* __restrict__ ddel, uint16_t* __restrict__ dn, float* __restrict__ dq, int N, int L,
     int T, bool linear) {
-  constexpr int HP = D + 8;    // row pitch (keeps three workgroups per CU)
+  constexpr int HP = D + 8;    // dN row pitch
   constexpr int NCC = D / 16;
   constexpr int NT = D / 64;   // 32-wide tiles per wave in each half
-  __shared__ __attribute__((aligned(16))) uint16_t hs[D * HP];   // H^T[c][a]
-  __shared__ __attribute__((aligned(16))) uint16_t dns[64 * HP]; // dN[r][c]
+  __shared__ __attribute__((aligned(16))) uint16_t hs[D * D];     // H^T[c][a], swizzled
+  __shared__ __attribute__((aligned(16))) uint16_t dns[64 * HP];  // dN[r][c]
+  __shared__ __attribute__((aligned(16))) float zs[2 * D];        // Z_i (two parts)
   __shared__ float red[2][2][64];                                 // [c half][dO.O, dY.Y][row]
   __shared__ float rowd[64];
 
@@ -66,17 +90,24 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(
   const int qh = wave & 1, ch = wave >> 1;
   const size_t head = static_cast<size_t>(bh) * N * D;
   const int rloc = 32 * qh + n32;
-  const int row = i * kBlock + rloc;
+  const int row = i * kBlock + rloc;   // < N always; rows >= valid_len are read, never used
   const bool valid = row < L;
 
-  // stage H^T of this query block
-  const uint16_t* hsrc = hst + (static_cast<size_t>(bh) * T + i) * D * D;
-  for (int e = tid; linear && e < D * D / 8; e += 256) {
-    const int c = e / (D / 8), a8 = e % (D / 8);
-    st16(&hs[c * HP + 8 * a8], ld16(hsrc + static_cast<size_t>(c) * D + 8 * a8));
+  // asynchronous copies of H_i^T and Z_i
+  if (linear) {
+    const uint16_t* hsrc = hst + (static_cast<size_t>(bh) * T + i) * D * D;
+    constexpr int kCopies = D * D / 8 / 64;   // 64 chunks of 16 bytes per copy
+    for (int it = wave; it < kCopies; it += 4) {
+      const int p = it * 64 + lane;
+      const int r = p / (D / 8), sl = p % (D / 8);
+      gl_to_lds16(hsrc + r * D + 8 * (sl ^ hswz<D>(r)), hs + it * 512);
+    }
+    if (wave == 0 && lane < D / 2)
+      gl_to_lds16(zst + (static_cast<size_t>(bh) * T + i) * 2 * D + 4 * lane, zs);
   }
 
-  // dY^T tiles for c in [D/2 ch, D/2 ch + D/2)
+  // dO fragments for dY, and the row pieces of O, Y, dO and Q that match the
+  // dY^T / dphi(q)^T accumulator layout (column 8 e4 + 4 hl + x of each tile)
   bf16x8 dof[NCC];
   {
     const uint16_t* src = dO + head + static_cast<size_t>(row) * D + 8 * hl;
@@ -84,6 +115,21 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(
     for (int cc = 0; cc < NCC; ++cc)
       dof[cc] = valid ? as_bf16x8(ld16(src + 16 * cc)) : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
   }
+  const size_t rb = head + static_cast<size_t>(row) * D;
+  u32x2 yv[NT][4], ov[NT][4], dv[NT][4], qv[NT][4];
+#pragma unroll
+  for (int ct = 0; ct < NT; ++ct)
+#pragma unroll
+    for (int e4 = 0; e4 < 4; ++e4) {
+      const int c0 = (D / 2) * ch + 32 * ct + 8 * e4 + 4 * hl;
+      yv[ct][e4] = ld8(y + rb + c0);
+      ov[ct][e4] = ld8(o + rb + c0);
+      dv[ct][e4] = ld8(dO + rb + c0);
+      qv[ct][e4] = ld8(q + rb + c0);
+    }
+  const float dn_r = (linear && valid) ? den[bh * N + row] : 0.f;
+
+  // dY^T tiles for c in [D/2 ch, D/2 ch + D/2)
   f32x16 dyt[NT];
 #pragma unroll
   for (int ct = 0; ct < NT; ++ct) {
@@ -94,24 +140,18 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(
   }
   // partial row dots over this lane's c values
   float p_oo = 0.f, p_yy = 0.f;
-  {
-    const size_t rb = head + static_cast<size_t>(row) * D;
 #pragma unroll
-    for (int ct = 0; ct < NT; ++ct)
+  for (int ct = 0; ct < NT; ++ct)
 #pragma unroll
-      for (int e4 = 0; e4 < 4; ++e4) {
-        const int c0 = (D / 2) * ch + 32 * ct + 8 * e4 + 4 * hl;
-        const u32x2 yv = ld8(y + rb + c0), ov = ld8(o + rb + c0), dv = ld8(dO + rb + c0);
+    for (int e4 = 0; e4 < 4; ++e4)
 #pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          const float yy = bf16_to_f32(static_cast<uint16_t>(x & 1 ? yv[x >> 1] >> 16 : yv[x >> 1] & 0xffffu));
-          const float oo = bf16_to_f32(static_cast<uint16_t>(x & 1 ? ov[x >> 1] >> 16 : ov[x >> 1] & 0xffffu));
-          const float dd = bf16_to_f32(static_cast<uint16_t>(x & 1 ? dv[x >> 1] >> 16 : dv[x >> 1] & 0xffffu));
-          p_yy = __fmaf_rn(dyt[ct][4 * e4 + x], yy, p_yy);
-          p_oo = __fmaf_rn(dd, oo, p_oo);
-        }
+      for (int x = 0; x < 4; ++x) {
+        const float yy = bf16_to_f32(u4_half(yv[ct][e4], x));
+        const float oo = bf16_to_f32(u4_half(ov[ct][e4], x));
+        const float dd = bf16_to_f32(u4_half(dv[ct][e4], x));
+        p_yy = __fmaf_rn(dyt[ct][4 * e4 + x], yy, p_yy);
+        p_oo = __fmaf_rn(dd, oo, p_oo);
       }
-  }
   p_oo += __shfl_xor(p_oo, 32);
   p_yy += __shfl_xor(p_yy, 32);
   if (hl == 0) {
@@ -121,7 +161,6 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(
   __syncthreads();
   const float s_oo = red[0][0][rloc] + red[1][0][rloc];
   const float s_yy = red[0][1][rloc] + red[1][1][rloc];
-  const float dn_r = linear ? den[bh * N + row] : 0.f;
   const bool lin = valid && dn_r > 0.f;
   const float rden = lin ? 1.0f / dn_r : 0.f;
   const float dd_r = lin ? -s_yy * rden : 0.f;
@@ -144,32 +183,32 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(
         st8(&dns[rloc * HP + c0], v);
       }
   }
+  __builtin_amdgcn_s_waitcnt(0);   // this wave's copies into hs / zs have landed
   __syncthreads();
   // dphi(q)^T[a][r]: wave covers rows half qh and a in [D/2 ch, D/2 ch + D/2)
-  const float* zrow = zst + (static_cast<size_t>(bh) * T + i) * 2 * D;
-  const uint16_t* qrow = q + head + static_cast<size_t>(row) * D;
-  float* dqrow = dq + head + static_cast<size_t>(row) * D;
+  float* dqrow = dq + rb;
   const float ddv = rowd[rloc];
 #pragma unroll
   for (int at = 0; at < NT; ++at) {
     const int abase = (D / 2) * ch + 32 * at;
     f32x16 acc = {};
+    if (linear) {
 #pragma unroll
-    for (int cc = 0; cc < NCC; ++cc) {
-      const bf16x8 a = lds_op32_tr<false>(hs, HP, 16 * cc, abase, lane);
-      const bf16x8 b = as_bf16x8(ld16(&dns[rloc * HP + 16 * cc + 8 * hl]));
-      acc = mfma32(a, b, acc);
+      for (int cc = 0; cc < NCC; ++cc) {
+        const bf16x8 a = hs_op32_tr<D>(hs, 16 * cc, abase, lane);
+        const bf16x8 b = as_bf16x8(ld16(&dns[rloc * HP + 16 * cc + 8 * hl]));
+        acc = mfma32(a, b, acc);
+      }
     }
     // lane holds dphi^T[a = abase + 8 (e/4) + 4 hl + e%4][row]
 #pragma unroll
     for (int e4 = 0; e4 < 4; ++e4) {
       const int a0 = abase + 8 * e4 + 4 * hl;
-      const u32x2 qv = ld8(qrow + a0);
       float r[4];
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
-        const float qa = bf16_to_f32(static_cast<uint16_t>(x & 1 ? qv[x >> 1] >> 16 : qv[x >> 1] & 0xffffu));
-        const float z = lin ? zrow[a0 + x] + zrow[D + a0 + x] : 0.f;
+        const float qa = bf16_to_f32(u4_half(qv[at][e4], x));
+        const float z = lin ? zs[a0 + x] + zs[D + a0 + x] : 0.f;
         const float g = acc[4 * e4 + x] + ddv * z;
         r[x] = lin ? g * phi_prime(qa) : 0.f;
       }
@@ -582,27 +621,45 @@ __global__ __launch_bounds__(256) void dw_part_kernel(const uint16_t* __restrict
   constexpr int P = D == 128 ? 152 : 72;
   constexpr int TILES = (D / 32) * (D / 32);
   constexpr int TPW = TILES / 4;
+  constexpr int CH = kBlock * D / 8 / 256;   // 16-byte chunks per thread per tensor
   __shared__ __attribute__((aligned(16))) uint16_t ys[64 * P];
   __shared__ __attribute__((aligned(16))) uint16_t ds_[64 * P];
   const int w = blockIdx.x;
   const long long b0 = nblocks * w / parts, b1 = nblocks * (w + 1) / parts;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n32 = lane & 31, hl = lane >> 5;
-  (void)hl;
+  const int n32 = lane & 31;
   f32x16 acc[TPW];
 #pragma unroll
   for (int x = 0; x < TPW; ++x) acc[x] = f32x16{};
-  for (long long b = b0; b < b1; ++b) {
+  // the next block's rows are loaded into registers while the current one is multiplied
+  u32x4 ry[CH], rd[CH];
+  auto load = [&](long long b) {
     const int blk = static_cast<int>(b % T);
     const uint16_t* ysrc = y + static_cast<size_t>(b) * kBlock * D;
     const uint16_t* dsrc = dO + static_cast<size_t>(b) * kBlock * D;
-    __syncthreads();
-    for (int e = tid; e < kBlock * D / 8; e += 256) {
-      const int t = e / (D / 8), c8 = 8 * (e % (D / 8));
-      st16(&ys[t * P + c8], ld16(ysrc + static_cast<size_t>(t) * D + c8));
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      const int e = tid + 256 * u;
+      const int t = e / (D / 8);
+      ry[u] = ld16(ysrc + 8 * static_cast<size_t>(e));
       const bool ok = blk * kBlock + t < L;   // padded rows of dO do not count
-      st16(&ds_[t * P + c8], ok ? ld16(dsrc + static_cast<size_t>(t) * D + c8) : u32x4{0u, 0u, 0u, 0u});
+      rd[u] = ok ? ld16(dsrc + 8 * static_cast<size_t>(e)) : u32x4{0u, 0u, 0u, 0u};
     }
+  };
+  auto store = [&]() {
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      const int e = tid + 256 * u;
+      const int t = e / (D / 8), c8 = 8 * (e % (D / 8));
+      st16(&ys[t * P + c8], ry[u]);
+      st16(&ds_[t * P + c8], rd[u]);
+    }
+  };
+  if (b0 < b1) load(b0);
+  for (long long b = b0; b < b1; ++b) {
+    __syncthreads();
+    store();
+    if (b + 1 < b1) load(b + 1);
     __syncthreads();
     // dW^T[c][o] = sum_t Y[t][c] dO[t][o]: both operands by transpose reads (k = t)
 #pragma unroll
@@ -629,13 +686,29 @@ __global__ __launch_bounds__(256) void dw_part_kernel(const uint16_t* __restrict
   }
 }
 
-__global__ void dw_reduce_kernel(const float* __restrict__ part, float* __restrict__ dw, int DD,
-                                 int parts) {
-  const int e = blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= DD) return;
+// Fixed-order reduction of the partials: workgroup of 256 threads per 64
+// entries; thread group g (of 4) sums partials g, g + 4, ... in order, and the
+// four group sums are added in order.
+__global__ __launch_bounds__(256) void dw_reduce_kernel(const float* __restrict__ part,
+                                                        float* __restrict__ dw, int DD, int parts) {
+  __shared__ float red[4][64];
+  const int tid = threadIdx.x, g = tid >> 6;
+  const int e = blockIdx.x * 64 + (tid & 63);
   float s = 0.f;
-  for (int p = 0; p < parts; ++p) s += part[static_cast<size_t>(p) * DD + e];
-  dw[e] = s;
+  if (e < DD) {
+    int p = g;
+    for (; p + 28 < parts; p += 32) {   // eight loads in flight, summed in order
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = part[static_cast<size_t>(p + 4 * u) * DD + e];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s += v[u];
+    }
+    for (; p < parts; p += 4) s += part[static_cast<size_t>(p) * DD + e];
+  }
+  red[g][tid & 63] = s;
+  __syncthreads();
+  if (g == 0 && e < DD) dw[e] = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
 }
 
 // ---------------------------------------------------------------------------
@@ -700,7 +773,7 @@ hipError_t launch_dw(const Dims& d, const uint16_t* y, const uint16_t* dO, float
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int dd = d.D * d.D;
-  hipLaunchKernelGGL(dw_reduce_kernel, dim3((dd + 255) / 256), dim3(256), 0, s, part, dw, dd, parts);
+  hipLaunchKernelGGL(dw_reduce_kernel, dim3((dd + 63) / 64), dim3(256), 0, s, part, dw, dd, parts);
   return hipGetLastError();
 }
 

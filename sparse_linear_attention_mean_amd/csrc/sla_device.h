@@ -91,6 +91,11 @@ __device__ __forceinline__ uint32_t u4_elem(const u32x4& v, int s) {
   const uint32_t w = v[s >> 1];
   return (s & 1) ? (w >> 16) : (w & 0xffffu);
 }
+// 16-bit element s (0..3) of an 8-byte register vector.
+__device__ __forceinline__ uint16_t u4_half(const u32x2& v, int s) {
+  const uint32_t w = v[s >> 1];
+  return static_cast<uint16_t>((s & 1) ? (w >> 16) : (w & 0xffffu));
+}
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x2& lo, const u32x2& hi) {
   return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});

@@ -44,7 +44,7 @@ struct SavedLayout {
   size_t lse, den, y, hst, zst, total;
 };
 
-constexpr int kDwParts = 256;
+constexpr int kDwParts = 1024;
 
 WorkspaceLayout workspace_layout(const Dims& d);
 SavedLayout saved_layout(const Dims& d);
