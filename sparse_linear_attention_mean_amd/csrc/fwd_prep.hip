@@ -16,20 +16,39 @@
 namespace sla {
 
 // ---------------------------------------------------------------------------
+// Column sums over a 64-token block (z, the pooled means) use one fixed
+// order everywhere: 16 chunks of 4 consecutive tokens, each summed in token
+// order from 0, then the 16 chunk sums combined as a balanced binary tree.
+// pool_kernel and kv_state_kernel share it, so the pooled K of the forward is
+// bit-identical to the one the standalone pool/score entry point computes.
+// ---------------------------------------------------------------------------
+constexpr int kSumChunks = 16;
+
+// p[c * stride], c = 0..15, added as a balanced binary tree
+__device__ __forceinline__ float tree16(const float* p, int stride) {
+  float l1[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) l1[c] = p[(2 * c) * stride] + p[(2 * c + 1) * stride];
+  const float a = (l1[0] + l1[1]) + (l1[2] + l1[3]);
+  const float b = (l1[4] + l1[5]) + (l1[6] + l1[7]);
+  return a + b;
+}
+
+// ---------------------------------------------------------------------------
 // kv_state: for key block j of head bh
 //   h_j^T[c][a] = sum_t v_t[c] * phi(k_t)[a],  z_j[a] = sum_t phi(k_t)[a],
 //   kbar_j[a]   = mean_t k_t[a]            (valid tokens t only)
 // h^T and z are written as bf16 in the "K-tiled" layout the aggregation GEMM
 // reads as its A operand: states[bh][j / 8][n][j % 8], n = c*D + a for h^T,
 // n = D*D + a for bf16(z), n = D*D + D + a for bf16(z - bf16(z)).  One
-// workgroup handles 8 consecutive key blocks so that every lane can write the
-// 8 block values of one state entry as a single 16-byte store; D = 128 splits
-// the 16 output tiles over two workgroups (one 32x32 tile per wave).
-// The tiles are staged row-major (a plain copy, phi applied on the way) and
-// both MFMA operands, which run over tokens, come from LDS transpose reads.
-// phi(k) is rounded to bf16 once and the same rounded values feed h and z.
-// kbar sums column a in token order 0..63 in fp32, exactly as pool_kernel
-// does, so the pooled K is bit-identical in both paths.
+// workgroup handles 8 consecutive key blocks; every lane writes the block
+// values of one state entry as two 8-byte stores (blocks 0-3, 4-7); it has one
+// wave per 32x32 tile of h^T (16 waves for D = 128), so K and V are read
+// once.  The tiles are staged row-major (a plain copy, phi applied on the
+// way) and both MFMA operands, which run over tokens, come from LDS
+// transpose reads.  phi(k) is rounded to bf16 once and the same rounded
+// values feed h and z.  The next block's rows are loaded during the current
+// block's products.
 // BWD = true turns the same kernel into the backward's query-side state
 // builder: Y = Q, X = dN (bf16 rows), and the vector part is weighted,
 // dZ_i[a] = sum_r d_r * phi(q_r)[a] with the per-row weights d_r; no pooled
@@ -37,10 +56,10 @@ namespace sla {
 // ---------------------------------------------------------------------------
 template <int D>
 struct KvCfg {
-  static constexpr int kThreads = D * 4;               // one (row pair, 8 columns) unit each
-  static constexpr int kWaves = kThreads / 64;
   static constexpr int kTiles = (D / 32) * (D / 32);   // 32x32 tiles of h^T
-  static constexpr int kTileGroups = kTiles / kWaves;  // workgroups per 8-block group (1 tile per wave)
+  static constexpr int kThreads = kTiles * 64;         // one tile per wave
+  static constexpr int kCh = 64 * D / 8 / kThreads;    // 16-byte row chunks per thread and tensor
+  static constexpr int kSlices = kThreads / D;         // threads per column in the column sums
   static constexpr int kPitch = D == 128 ? 152 : 72;   // LDS row pitch (bf16), conflict-free transpose reads
 };
 
@@ -52,72 +71,71 @@ __global__ __launch_bounds__(KvCfg<D>::kThreads) void kv_state_kernel(
   using C = KvCfg<D>;
   constexpr int P = C::kPitch;
   constexpr int NB = D * D + 2 * D;
+  constexpr int CPS = kSumChunks / C::kSlices;   // chunks summed per thread
   __shared__ __attribute__((aligned(16))) uint16_t pk[64 * P];   // phi(Y)[t][a], bf16
   __shared__ __attribute__((aligned(16))) uint16_t xs[64 * P];   // X[t][c]
-  __shared__ __attribute__((aligned(16))) uint16_t ks[64 * P];   // Y[t][a] (raw, for the pooled mean)
+  __shared__ __attribute__((aligned(16))) uint16_t ks[BWD ? 8 : 64 * P];   // Y[t][a] raw (pooled mean)
+  __shared__ float zpart[kSumChunks][D];
+  __shared__ float kpart[BWD ? 1 : kSumChunks][D];
   __shared__ uint16_t zst[2 * D * 8];
   __shared__ float wts[kBlock];
 
   const int groups = Tp / 8;
   const uint32_t wg = xcd_remap(blockIdx.x, gridDim.x);
-  const int tgrp = wg % C::kTileGroups;      // which tiles of h^T this workgroup computes
-  const int bh = (wg / C::kTileGroups) / groups;
-  const int g = (wg / C::kTileGroups) % groups;
-  const bool lead = tgrp == 0;               // writes kbar and z
+  const int bh = wg / groups;
+  const int g = wg % groups;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int n32 = lane & 31;
   const int hl = lane >> 5;
-
-  // staging unit of this thread: rows 2*rp, 2*rp+1; columns 8*c8 .. 8*c8+7
-  const int rp = tid / (D / 8);
-  const int c8 = tid % (D / 8);
   const size_t head = static_cast<size_t>(bh) * N * D;
 
-  u32x4 rk[2], rv[2];
+  u32x4 rk[C::kCh], rv[C::kCh];
   auto load = [&](int j) {
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int tok = j * kBlock + 2 * rp + r;
+    for (int u = 0; u < C::kCh; ++u) {
+      const int e = tid + C::kThreads * u;
+      const int tok = j * kBlock + e / (D / 8);
       if (j < T && tok < L) {
-        const size_t off = head + static_cast<size_t>(tok) * D + 8 * c8;
-        rk[r] = ld16(ysrc + off);
-        rv[r] = ld16(xsrc + off);
+        const size_t off = head + static_cast<size_t>(tok) * D + 8 * (e % (D / 8));
+        rk[u] = ld16(ysrc + off);
+        rv[u] = ld16(xsrc + off);
       } else {
-        rk[r] = u32x4{0u, 0u, 0u, 0u};
-        rv[r] = u32x4{0u, 0u, 0u, 0u};
+        rk[u] = u32x4{0u, 0u, 0u, 0u};
+        rv[u] = u32x4{0u, 0u, 0u, 0u};
       }
     }
   };
 
-  const int tt = tgrp * C::kWaves + wave;    // this wave's 32x32 tile of h^T
-  const int ct = tt / (D / 32), at = tt % (D / 32);
-  uint32_t stash[16][4];   // bf16 pairs of (block 2p, block 2p+1) per result entry
+  const int ct = wave / (D / 32), at = wave % (D / 32);   // this wave's 32x32 tile of h^T
+  const int sa = tid % D, sl = tid / D;                     // column-sum unit: column, slice
+  // bf16 pairs of (block 2p, block 2p+1) per result entry, four blocks at a time
+  uint32_t stash[16][2];
+  uint16_t* out = states + (static_cast<size_t>(bh) * groups + g) * NB * 8;
   load(g * 8);
 #pragma unroll
   for (int jj = 0; jj < 8; ++jj) {
     const int j = g * 8 + jj;
     // stage the rows (invalid tokens are zero in all three tiles)
-    {
 #pragma unroll
-      for (int r = 0; r < 2; ++r) {
-        const int row = (2 * rp + r) * P + 8 * c8;
-        st16(&xs[row], rv[r]);
-        if constexpr (!BWD) st16(&ks[row], rk[r]);
-        const int tok = j * kBlock + 2 * rp + r;
-        const bool ok = j < T && tok < L;
-        float f[8];
+    for (int u = 0; u < C::kCh; ++u) {
+      const int e = tid + C::kThreads * u;
+      const int r = e / (D / 8), c8 = e % (D / 8);
+      const int row = r * P + 8 * c8;
+      st16(&xs[row], rv[u]);
+      if constexpr (!BWD) st16(&ks[row], rk[u]);
+      const bool ok = j < T && j * kBlock + r < L;
+      float f[8];
 #pragma unroll
-        for (int s2 = 0; s2 < 8; ++s2)
-          f[s2] = ok ? phi(bf16_to_f32(static_cast<uint16_t>(u4_elem(rk[r], s2)))) : 0.f;
-        st16(&pk[row], __builtin_bit_cast(u32x4, cvt_bf16x8(f)));
-      }
-      if constexpr (BWD) {
-        if (lead && tid < kBlock) {
-          const int tok = j * kBlock + tid;
-          wts[tid] = (j < T && tok < L) ? wrow[static_cast<size_t>(bh) * N + tok] : 0.f;
-        }
+      for (int s2 = 0; s2 < 8; ++s2)
+        f[s2] = ok ? phi(bf16_to_f32(static_cast<uint16_t>(u4_elem(rk[u], s2)))) : 0.f;
+      st16(&pk[row], __builtin_bit_cast(u32x4, cvt_bf16x8(f)));
+    }
+    if constexpr (BWD) {
+      if (tid < kBlock) {
+        const int tok = j * kBlock + tid;
+        wts[tid] = (j < T && tok < L) ? wrow[static_cast<size_t>(bh) * N + tok] : 0.f;
       }
     }
     __syncthreads();
@@ -133,69 +151,89 @@ __global__ __launch_bounds__(KvCfg<D>::kThreads) void kv_state_kernel(
       for (int i = 0; i < 16; ++i) {
         const uint32_t hb = f32_to_bf16(acc[i]);
         if (jj & 1)
-          stash[i][jj >> 1] |= hb << 16;
+          stash[i][(jj >> 1) & 1] |= hb << 16;
         else
-          stash[i][jj >> 1] = hb;
+          stash[i][(jj >> 1) & 1] = hb;
       }
-    }
-    if (lead && tid < D) {
-      const int a = tid;
-      float zs = 0.f, ksum = 0.f;
-      for (int t = 0; t < kBlock; ++t) {
-        if constexpr (BWD) {
-          zs = __fmaf_rn(wts[t], bf16_to_f32(pk[t * P + a]), zs);
-        } else {
-          zs += bf16_to_f32(pk[t * P + a]);
-          ksum += bf16_to_f32(ks[t * P + a]);
+      if ((jj & 3) == 3) {   // blocks jj-3 .. jj: one 8-byte half of each 16-byte entry
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int c = 32 * ct + 8 * (i / 4) + 4 * hl + (i % 4);
+          const int a = 32 * at + n32;
+          st8(out + (static_cast<size_t>(c) * D + a) * 8 + 4 * (jj >> 2), u32x2{stash[i][0], stash[i][1]});
         }
       }
+    }
+    // chunk sums of z (weighted in BWD mode) and of the raw rows
+#pragma unroll
+    for (int cc = 0; cc < CPS; ++cc) {
+      const int c = sl * CPS + cc;
+      float zs = 0.f, ksum = 0.f;
+#pragma unroll
+      for (int t = 4 * c; t < 4 * c + 4; ++t) {
+        if constexpr (BWD) {
+          zs = __fmaf_rn(wts[t], bf16_to_f32(pk[t * P + sa]), zs);
+        } else {
+          zs += bf16_to_f32(pk[t * P + sa]);
+          ksum += bf16_to_f32(ks[t * P + sa]);
+        }
+      }
+      zpart[c][sa] = zs;
+      if constexpr (!BWD) kpart[c][sa] = ksum;
+    }
+    __syncthreads();
+    if (tid < D) {
+      const int a = tid;
+      const float zs = tree16(&zpart[0][a], D);
       const uint16_t zh = f32_to_bf16(zs);
       zst[a * 8 + jj] = zh;
       zst[(D + a) * 8 + jj] = f32_to_bf16(zs - bf16_to_f32(zh));
       if constexpr (!BWD) {
         if (j < T) {
           const int nvalid = min(kBlock, L - j * kBlock);
-          kbar[(static_cast<size_t>(bh) * T + j) * D + a] = ksum / static_cast<float>(nvalid);
+          kbar[(static_cast<size_t>(bh) * T + j) * D + a] =
+              tree16(&kpart[0][a], D) / static_cast<float>(nvalid);
         }
       }
     }
-    __syncthreads();
   }
 
-  uint16_t* out = states + (static_cast<size_t>(bh) * groups + g) * NB * 8;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int c = 32 * ct + 8 * (i / 4) + 4 * hl + (i % 4);
-    const int a = 32 * at + n32;
-    st16(out + (static_cast<size_t>(c) * D + a) * 8,
-         u32x4{stash[i][0], stash[i][1], stash[i][2], stash[i][3]});
-  }
-  if (!lead) return;
+  __syncthreads();   // zst complete
   for (int e = tid; e < 2 * D; e += C::kThreads)
     st16(out + (static_cast<size_t>(D) * D + e) * 8, ld16(&zst[e * 8]));
 }
 
 // ---------------------------------------------------------------------------
-// pool: xbar[bh][i][a] = mean of the valid rows of block i, summed in token
-// order 0..63 in fp32 (same order as kv_state_kernel's pooled K).
+// pool: xbar[bh][i][a] = mean of the valid rows of block i, in the column-sum
+// order above.  One workgroup (2 D threads) per block: thread (column group of
+// 8, chunk c) loads its chunk's four rows with 16-byte loads.
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(256) void pool_kernel(const uint16_t* __restrict__ x,
-                                                   float* __restrict__ xbar, int N, int L,
-                                                   int T, long long rows) {
-  const long long r = static_cast<long long>(blockIdx.x) * (256 / D) + threadIdx.x / D;
-  const int a = threadIdx.x % D;
-  if (r >= rows) return;
+__global__ __launch_bounds__(2 * D) void pool_kernel(const uint16_t* __restrict__ x,
+                                                     float* __restrict__ xbar, int N, int L,
+                                                     int T) {
+  __shared__ float part[kSumChunks][D];
+  const long long r = blockIdx.x;
   const long long bh = r / T;
   const int i = static_cast<int>(r % T);
-  const uint16_t* src = x + (static_cast<size_t>(bh) * N + static_cast<size_t>(i) * kBlock) * D + a;
+  const int tid = threadIdx.x;
+  const int cg = tid % (D / 8), c = tid / (D / 8);
+  const uint16_t* src = x + (static_cast<size_t>(bh) * N + static_cast<size_t>(i) * kBlock) * D + 8 * cg;
   const int nvalid = min(kBlock, L - i * kBlock);
-  float s = 0.f;
-  for (int t = 0; t < kBlock; ++t) {
-    const float val = t < nvalid ? bf16_to_f32(src[static_cast<size_t>(t) * D]) : 0.f;
-    s += val;
+  u32x4 v[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+    v[t] = 4 * c + t < nvalid ? ld16(src + static_cast<size_t>(4 * c + t) * D) : u32x4{0u, 0u, 0u, 0u};
+  float s[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    s[e] = 0.f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) s[e] += bf16_to_f32(static_cast<uint16_t>(u4_elem(v[t], e)));
+    part[c][8 * cg + e] = s[e];
   }
-  xbar[static_cast<size_t>(r) * D + a] = s / static_cast<float>(nvalid);
+  __syncthreads();
+  if (tid < D) xbar[static_cast<size_t>(r) * D + tid] = tree16(&part[0][tid], D) / static_cast<float>(nvalid);
 }
 
 // ---------------------------------------------------------------------------
@@ -394,8 +432,7 @@ __global__ void fill_mask_kernel(int8_t* __restrict__ mask, long long n, int8_t 
 // ---------------------------------------------------------------------------
 hipError_t launch_kv_state(const Dims& d, const uint16_t* k, const uint16_t* v, float* kbar,
                            uint16_t* states, hipStream_t s) {
-  const int tg = d.D == 128 ? KvCfg<128>::kTileGroups : KvCfg<64>::kTileGroups;
-  const dim3 grid(static_cast<unsigned>(d.BH() * (d.Tp / 8) * tg));
+  const dim3 grid(static_cast<unsigned>(d.BH() * (d.Tp / 8)));
   if (d.D == 128)
     hipLaunchKernelGGL((kv_state_kernel<128, false>), grid, dim3(KvCfg<128>::kThreads), 0, s, k, v,
                        nullptr, kbar, states, d.N, d.L, d.T, d.Tp);
@@ -407,8 +444,7 @@ hipError_t launch_kv_state(const Dims& d, const uint16_t* k, const uint16_t* v, 
 
 hipError_t launch_dstate(const Dims& d, const uint16_t* q, const uint16_t* dn, const float* ddel,
                          uint16_t* states, hipStream_t s) {
-  const int tg = d.D == 128 ? KvCfg<128>::kTileGroups : KvCfg<64>::kTileGroups;
-  const dim3 grid(static_cast<unsigned>(d.BH() * (d.Tp / 8) * tg));
+  const dim3 grid(static_cast<unsigned>(d.BH() * (d.Tp / 8)));
   if (d.D == 128)
     hipLaunchKernelGGL((kv_state_kernel<128, true>), grid, dim3(KvCfg<128>::kThreads), 0, s, q, dn,
                        ddel, nullptr, states, d.N, d.L, d.T, d.Tp);
@@ -419,13 +455,11 @@ hipError_t launch_dstate(const Dims& d, const uint16_t* q, const uint16_t* dn, c
 }
 
 hipError_t launch_pool(const Dims& d, const uint16_t* x, float* xbar, hipStream_t s) {
-  const long long rows = d.BH() * d.T;
-  const int per = 256 / d.D;
-  const dim3 grid(static_cast<unsigned>((rows + per - 1) / per));
+  const dim3 grid(static_cast<unsigned>(d.BH() * d.T));
   if (d.D == 128)
-    hipLaunchKernelGGL(pool_kernel<128>, grid, dim3(256), 0, s, x, xbar, d.N, d.L, d.T, rows);
+    hipLaunchKernelGGL(pool_kernel<128>, grid, dim3(256), 0, s, x, xbar, d.N, d.L, d.T);
   else
-    hipLaunchKernelGGL(pool_kernel<64>, grid, dim3(256), 0, s, x, xbar, d.N, d.L, d.T, rows);
+    hipLaunchKernelGGL(pool_kernel<64>, grid, dim3(128), 0, s, x, xbar, d.N, d.L, d.T);
   return hipGetLastError();
 }
 
