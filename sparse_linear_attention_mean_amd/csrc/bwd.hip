@@ -46,25 +46,6 @@ __global__ void w_transpose_kernel(const uint16_t* __restrict__ w, uint16_t* __r
 // latencies overlap each other and the dY products.
 // ---------------------------------------------------------------------------
 
-// H^T is kept in LDS without row padding; 16-byte chunk k of row c sits in
-// slot k ^ hswz(c), which spreads the four rows one transpose read touches
-// over all banks.
-template <int D>
-__device__ __forceinline__ int hswz(int r) {
-  return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
-}
-
-// lds_op32_tr<false> on the swizzled H^T tile
-template <int D>
-__device__ __forceinline__ bf16x8 hs_op32_tr(const uint16_t* hs, int kb, int n0, int lane) {
-  const int g = lane >> 4, c = lane & 15, h = lane >> 5;
-  const int col = n0 + 16 * (g & 1) + 4 * (c & 3);
-  const int r0 = kb + 8 * h + (c >> 2), r1 = r0 + 4;
-  const u32x2 lo = lds_tr4(hs + r0 * D + (((col >> 3) ^ hswz<D>(r0)) << 3) + (col & 7));
-  const u32x2 hi = lds_tr4(hs + r1 * D + (((col >> 3) ^ hswz<D>(r1)) << 3) + (col & 7));
-  return as_bf16x8(lo, hi);
-}
-
 template <int D>
 __global__ __launch_bounds__(256, 2) void bwd_prep_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ o,
@@ -76,7 +57,7 @@ __global__ __launch_bounds__(256, 2) void bwd_prep_kernel(
   constexpr int HP = D + 8;    // dN row pitch
   constexpr int NCC = D / 16;
   constexpr int NT = D / 64;   // 32-wide tiles per wave in each half
-  __shared__ __attribute__((aligned(16))) uint16_t hs[D * D];     // H^T[c][a], swizzled
+  __shared__ __attribute__((aligned(16))) uint16_t hs[D * D];     // H^T[c][a], swizzled tile
   __shared__ __attribute__((aligned(16))) uint16_t dns[64 * HP];  // dN[r][c]
   __shared__ __attribute__((aligned(16))) float zs[2 * D];        // Z_i (two parts)
   __shared__ float red[2][2][64];                                 // [c half][dO.O, dY.Y][row]
@@ -95,13 +76,7 @@ __global__ __launch_bounds__(256, 2) void bwd_prep_kernel(
 
   // asynchronous copies of H_i^T and Z_i
   if (linear) {
-    const uint16_t* hsrc = hst + (static_cast<size_t>(bh) * T + i) * D * D;
-    constexpr int kCopies = D * D / 8 / 64;   // 64 chunks of 16 bytes per copy
-    for (int it = wave; it < kCopies; it += 4) {
-      const int p = it * 64 + lane;
-      const int r = p / (D / 8), sl = p % (D / 8);
-      gl_to_lds16(hsrc + r * D + 8 * (sl ^ hswz<D>(r)), hs + it * 512);
-    }
+    copy_swz<D>(hst + (static_cast<size_t>(bh) * T + i) * D * D, hs, D, wave, 4, lane);
     if (wave == 0 && lane < D / 2)
       gl_to_lds16(zst + (static_cast<size_t>(bh) * T + i) * 2 * D + 4 * lane, zs);
   }
@@ -195,7 +170,7 @@ __global__ __launch_bounds__(256, 2) void bwd_prep_kernel(
     if (linear) {
 #pragma unroll
       for (int cc = 0; cc < NCC; ++cc) {
-        const bf16x8 a = hs_op32_tr<D>(hs, 16 * cc, abase, lane);
+        const bf16x8 a = swz_op32_tr<D>(hs, 16 * cc, abase, lane);
         const bf16x8 b = as_bf16x8(ld16(&dns[rloc * HP + 16 * cc + 8 * hl]));
         acc = mfma32(a, b, acc);
       }
@@ -378,6 +353,11 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(
 // (k index permuted) and read dO_i or Q_i from the same LDS tiles with
 // transpose reads, so only the natural tiles are staged.  The row pitch keeps
 // both kinds of LDS read free of bank conflicts.
+// Everything the block needs besides the Q_i / dO_i stream -- K_j, V_j, dh_j^T
+// and dz_j -- is copied into LDS asynchronously when the workgroup starts, so
+// those reads overlap the first query block and the linear epilogue reads LDS
+// only.  After the loop the two query halves are merged so that every wave
+// finishes two of the four 32-column tiles.
 // ---------------------------------------------------------------------------
 template <int D>
 struct BkvCfg {
@@ -385,11 +365,14 @@ struct BkvCfg {
   static constexpr int kBuf = 2 * 64 * RP;              // Q and dO of one query block
   static constexpr int KCH = D / 64;                    // 16-byte chunks per thread per tensor
   static constexpr int NCC = D / 16, NCT = D / 32;
-  static constexpr int HP = D + 8;
-  static constexpr int kStage = 2 * kBuf * 2 + 2 * 2 * 64 * 4;          // bytes: 2 buffers + lse/D
-  // dh^T tile + merge area: 4 slots (role x key half) of NCT*16 registers x 64 lanes (fp32)
-  static constexpr int kEpi = D * HP * 2 + 4 * NCT * 16 * 64 * 4;
-  static constexpr int kLds = kStage > kEpi ? kStage : kEpi;
+  static constexpr int kStage = 2 * kBuf * 2 + 2 * 2 * 64 * 4;   // bytes: 2 buffers + lse/D
+  static constexpr int kMerge = 8 * (NCT / 2) * 16 * 64 * 4;    // half of every wave's tiles (fp32)
+  static constexpr int kLoop = kStage > kMerge ? kStage : kMerge;
+  static constexpr int kKs = kLoop;                 // K_j, swizzled 64 x D
+  static constexpr int kVs = kKs + 64 * D * 2;      // V_j
+  static constexpr int kDh = kVs + 64 * D * 2;      // dh_j^T, swizzled D x D
+  static constexpr int kDz = kDh + D * D * 2;       // dz_j, 2 D floats
+  static constexpr int kLds = kDz + 2 * D * 4;
 };
 
 template <int D>
@@ -401,11 +384,15 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(
     const uint16_t* __restrict__ dh, const float* __restrict__ dz, bool linear,
     float* __restrict__ dk, float* __restrict__ dv, int N, int L, int T, float scale) {
   using C = BkvCfg<D>;
-  constexpr int RP = C::RP, HP = C::HP;
+  constexpr int RP = C::RP;
   __shared__ __attribute__((aligned(16))) uint8_t smem_raw[C::kLds];
   uint16_t* smem = reinterpret_cast<uint16_t*>(smem_raw);
   float* lses = reinterpret_cast<float*>(smem_raw + 2 * C::kBuf * 2);   // [buf][64]
   float* dss = lses + 128;                                              // [buf][64]
+  uint16_t* ksw = reinterpret_cast<uint16_t*>(smem_raw + C::kKs);
+  uint16_t* vsw = reinterpret_cast<uint16_t*>(smem_raw + C::kVs);
+  uint16_t* dhs = reinterpret_cast<uint16_t*>(smem_raw + C::kDh);
+  float* dzs = reinterpret_cast<float*>(smem_raw + C::kDz);
 
   const uint32_t wg = xcd_remap(blockIdx.x, gridDim.x);
   const int j = wg % T;
@@ -415,20 +402,18 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(
   const int kh = wave & 1, qh = (wave >> 1) & 1;
   const int n32 = lane & 31, hl = lane >> 5;
   const size_t head = static_cast<size_t>(bh) * N * D;
-  const int key = j * kBlock + 32 * kh + n32;   // this lane's key (B operand column)
+  const int kloc = 32 * kh + n32;               // this lane's key within the block
+  const int key = j * kBlock + kloc;
+  const bool kv_ok = key < L;                   // padded keys: zero operands (their P is masked too)
   const float sl2 = scale * kLog2e;
 
-  // K_j (and V_j for the dK role) as B operands (k = head-dim index 16 cc + 8 hl + s)
-  bf16x8 kf[C::NCC], vf[C::NCC];
-  {
-    const uint16_t* kr = k + head + static_cast<size_t>(key) * D + 8 * hl;
-    const uint16_t* vr = v + head + static_cast<size_t>(key) * D + 8 * hl;
-    const bool kv_ok = key < L;   // padded keys: zero operands (their P is masked too)
-#pragma unroll
-    for (int cc = 0; cc < C::NCC; ++cc) {
-      kf[cc] = kv_ok ? as_bf16x8(ld16(kr + 16 * cc)) : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
-      vf[cc] = (role_dk && kv_ok) ? as_bf16x8(ld16(vr + 16 * cc)) : kf[cc];
-    }
+  // asynchronous copies of K_j, V_j (rows past valid_len are never used
+  // unmasked), dh_j^T and dz_j
+  copy_swz<D>(k + head + static_cast<size_t>(j) * kBlock * D, ksw, 64, wave, 8, lane);
+  copy_swz<D>(v + head + static_cast<size_t>(j) * kBlock * D, vsw, 64, wave, 8, lane);
+  if (linear) {
+    copy_swz<D>(dh + (static_cast<size_t>(bh) * T + j) * D * D, dhs, D, wave, 8, lane);
+    if (wave == 7 && lane < D / 2) gl_to_lds16(dz + (static_cast<size_t>(bh) * T + j) * 2 * D + 4 * lane, dzs);
   }
   const int cnt = col_cnt[bh * T + j];
   const int32_t* crow = col + (bh * T + j) * static_cast<long long>(T);
@@ -471,11 +456,21 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(
     }
   };
 
-  if (cnt > 0) {
-    load(crow[0]);
-    store(0, crow[0]);
-    __syncthreads();
+  if (cnt > 0) load(crow[0]);
+  __builtin_amdgcn_s_waitcnt(0);   // this wave's copies have landed
+  if (cnt > 0) store(0, crow[0]);
+  __syncthreads();
+
+  // K_j (and V_j for the dK role) as B operands (k = head-dim index 16 cc + 8 hl + s)
+  bf16x8 kf[C::NCC], vf[C::NCC];
+#pragma unroll
+  for (int cc = 0; cc < C::NCC; ++cc) {
+    const u32x4 kz = ld16(ksw + swz_off<D>(kloc, 16 * cc + 8 * hl));
+    const u32x4 vz = ld16(vsw + swz_off<D>(kloc, 16 * cc + 8 * hl));
+    kf[cc] = kv_ok ? as_bf16x8(kz) : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+    vf[cc] = (role_dk && kv_ok) ? as_bf16x8(vz) : kf[cc];
   }
+
   const bool tail_key = key >= L;
   const bool tail_blk = (j + 1) * kBlock > L;   // uniform: the padded last key block
   for (int n = 0; n < cnt; ++n) {
@@ -524,86 +519,86 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(
     __syncthreads();
   }
 
-  // ---- merge the query halves; lane holds X[key = 32 kh + 8 (e/4) + 4 hl + e%4][c = 32 ct + n32]
-  __syncthreads();
-  float* ex = reinterpret_cast<float*>(smem_raw + D * HP * 2);   // [role][kh][NCT*16][64]
-  constexpr int NACC = C::NCT * 16;
-  const int slot = (role_dk ? 2 : 0) + kh;
-  if (qh == 1) {
+  // ---- merge the query halves: wave (role, qh, kh) finishes the tiles
+  // ct = 2 qh, 2 qh + 1 and hands the other two to its partner (other qh).
+  // lane holds X[key = 32 kh + 8 (e/4) + 4 hl + e%4][c = 32 ct + n32]
+  constexpr int NH = C::NCT / 2;
+  float* ex = reinterpret_cast<float*>(smem_raw);   // [wave][NH][16][64]
+  // (qh is uniform per wave; both branches index acc statically)
+  f32x16 fin[NH];
+  if (qh == 0) {
 #pragma unroll
-    for (int ct = 0; ct < C::NCT; ++ct)
+    for (int x = 0; x < NH; ++x) {
+      fin[x] = acc[x];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) ex[(slot * NACC + ct * 16 + e) * 64 + lane] = acc[ct][e];
-  }
-  // stage dh^T[c][a] of this key block for the linear part
-  uint16_t* dhs = smem;
-  if (linear) {
-    const uint16_t* src = dh + (static_cast<size_t>(bh) * T + j) * D * D;
-    for (int e = tid; e < D * D / 8; e += 512) {
-      const int c = e / (D / 8), a8 = e % (D / 8);
-      st16(&dhs[c * HP + 8 * a8], ld16(src + static_cast<size_t>(c) * D + 8 * a8));
+      for (int e = 0; e < 16; ++e) ex[((wave * NH + x) * 16 + e) * 64 + lane] = acc[NH + x][e];
+    }
+  } else {
+#pragma unroll
+    for (int x = 0; x < NH; ++x) {
+      fin[x] = acc[NH + x];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) ex[((wave * NH + x) * 16 + e) * 64 + lane] = acc[x][e];
     }
   }
   __syncthreads();
-  if (qh == 1) return;
+  const int partner = wave ^ 2;
 #pragma unroll
-  for (int ct = 0; ct < C::NCT; ++ct)
+  for (int x = 0; x < NH; ++x)
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const float sum = acc[ct][e] + ex[(slot * NACC + ct * 16 + e) * 64 + lane];
-      acc[ct][e] = role_dk ? scale * sum : sum;
+      const float sum = fin[x][e] + ex[((partner * NH + x) * 16 + e) * 64 + lane];
+      fin[x][e] = role_dk ? scale * sum : sum;
     }
-  const float* dzr = dz + (static_cast<size_t>(bh) * T + j) * 2 * D;
   if (linear) {
-    // rows t of this wave: A operand phi(K_j)[t][a] (dV role) or V_j[t][c] (dK role)
-    const int t = j * kBlock + 32 * kh + n32;
-    const bool tv = t < L;
-    const uint16_t* xr = (role_dk ? v : k) + head + static_cast<size_t>(t) * D + 8 * hl;
+    // A operand rows t = key: phi(K_j)[t][a] (dV role) or V_j[t][c] (dK role), from registers
     bf16x8 af[C::NCC];
 #pragma unroll
     for (int cc = 0; cc < C::NCC; ++cc) {
-      const u32x4 xv = tv ? ld16(xr + 16 * cc) : u32x4{0u, 0u, 0u, 0u};
       if (role_dk) {
-        af[cc] = as_bf16x8(xv);
+        af[cc] = vf[cc];
       } else {
 #pragma unroll
         for (int s2 = 0; s2 < 8; ++s2)
-          af[cc][s2] = static_cast<__bf16>(tv ? phi(bf16_to_f32(static_cast<uint16_t>(u4_elem(xv, s2)))) : 0.f);
+          af[cc][s2] = static_cast<__bf16>(kv_ok ? phi(static_cast<float>(kf[cc][s2])) : 0.f);
       }
     }
 #pragma unroll
-    for (int ct = 0; ct < C::NCT; ++ct) {
+    for (int x = 0; x < NH; ++x) {
+      const int ct = NH * qh + x;
       f32x16 lin = {};
 #pragma unroll
       for (int cc = 0; cc < C::NCC; ++cc) {
         // dV role: dV_lin[t][c] = sum_a phi(K)[t][a] dh[a][c], B = dh^T[c][a .. a + 7] (row)
         // dK role: dphi(K)[t][a] = sum_c V[t][c] dh[a][c],     B = dh^T[c .. c + 7][a] (transpose read)
-        const bf16x8 b = role_dk ? lds_op32_tr<false>(dhs, HP, 16 * cc, 32 * ct, lane)
-                                 : as_bf16x8(ld16(&dhs[(32 * ct + n32) * HP + 16 * cc + 8 * hl]));
+        const bf16x8 b = role_dk ? swz_op32_tr<D>(dhs, 16 * cc, 32 * ct, lane)
+                                 : as_bf16x8(ld16(dhs + swz_off<D>(32 * ct + n32, 16 * cc + 8 * hl)));
         lin = mfma32(af[cc], b, lin);
       }
       // lane holds X[t = 32 kh + 8 (e/4) + 4 hl + e%4][n = 32 ct + n32]
       const int a = 32 * ct + n32;
-      const float dza = role_dk ? dzr[a] + dzr[D + a] : 0.f;
+      if (role_dk) {
+        const float dza = dzs[a] + dzs[D + a];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        if (role_dk) {
-          const int tt = j * kBlock + 32 * kh + 8 * (e / 4) + 4 * hl + (e % 4);
-          const float kv = tt < L ? bf16_to_f32(k[head + static_cast<size_t>(tt) * D + a]) : 0.f;
-          acc[ct][e] += (lin[e] + dza) * phi_prime(kv);
-        } else {
-          acc[ct][e] += lin[e];
+        for (int e4 = 0; e4 < 4; ++e4) {
+          const u32x2 k4 = swz_col4<D>(ksw, 32 * kh + 8 * e4, 32 * ct, lane);   // K[t .. t + 3][a]
+#pragma unroll
+          for (int x4 = 0; x4 < 4; ++x4)
+            fin[x][4 * e4 + x4] += (lin[4 * e4 + x4] + dza) * phi_prime(bf16_to_f32(u4_half(k4, x4)));
         }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) fin[x][e] += lin[e];
       }
     }
   }
   float* out = role_dk ? dk : dv;
 #pragma unroll
-  for (int ct = 0; ct < C::NCT; ++ct)
+  for (int x = 0; x < NH; ++x)
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int tt = j * kBlock + 32 * kh + 8 * (e / 4) + 4 * hl + (e % 4);
-      out[head + static_cast<size_t>(tt) * D + 32 * ct + n32] = tt < L ? acc[ct][e] : 0.f;
+      out[head + static_cast<size_t>(tt) * D + 32 * (NH * qh + x) + n32] = tt < L ? fin[x][e] : 0.f;
     }
 }
 

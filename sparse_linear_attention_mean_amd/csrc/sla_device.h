@@ -157,6 +157,51 @@ __device__ __forceinline__ void gl_to_lds16(const void* gsrc, void* lds_base) {
       (__attribute__((address_space(3))) void*)(lds_base), 16, 0, 0);
 }
 
+// ---------------------------------------------------------------------------
+// Unpadded row-major bf16 tiles in LDS (row length D) whose 16-byte chunks are
+// XOR-swizzled per row: chunk k of row r sits in slot k ^ swz<D>(r).  Such a
+// tile can be filled by the asynchronous global->LDS copy (which writes whole
+// 1 KB runs), and both 16-byte row reads (16 lanes on 16 different rows) and
+// transpose reads (4 rows x 32 bytes per 16 lanes) spread over the banks.
+// ---------------------------------------------------------------------------
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  return D == 128 ? (((r & 7) << 1) | ((r >> 3) & 1)) : ((((r >> 1) & 3) << 1) | ((r >> 3) & 1));
+}
+template <int D>
+__device__ __forceinline__ int swz_off(int r, int col) {
+  return r * D + ((((col >> 3) ^ swz<D>(r))) << 3) + (col & 7);
+}
+// rows [0, rows) of a row-major global tile into a swizzled LDS tile; the
+// calling workgroup's waves w = 0 .. nw-1 share the copies; completion is
+// tracked by vmcnt
+template <int D>
+__device__ __forceinline__ void copy_swz(const uint16_t* src, uint16_t* dst, int rows, int w,
+                                         int nw, int lane) {
+  const int copies = rows * (D / 8) / 64;
+  for (int it = w; it < copies; it += nw) {
+    const int p = it * 64 + lane;
+    const int r = p / (D / 8), sl = p % (D / 8);
+    gl_to_lds16(src + r * D + 8 * (sl ^ swz<D>(r)), dst + it * 512);
+  }
+}
+// lds_op32_tr<false> on a swizzled tile: lane gets M[kb + 8 (l/32) + s][n0 + l%32] (s < 4)
+// and M[kb + 8 (l/32) + 4 + s][...] as the 32x32x16 operand layout
+template <int D>
+__device__ __forceinline__ bf16x8 swz_op32_tr(const uint16_t* m, int kb, int n0, int lane) {
+  const int g = lane >> 4, c = lane & 15, h = lane >> 5;
+  const int col = n0 + 16 * (g & 1) + 4 * (c & 3);
+  const int r0 = kb + 8 * h + (c >> 2);
+  return as_bf16x8(lds_tr4(m + swz_off<D>(r0, col)), lds_tr4(m + swz_off<D>(r0 + 4, col)));
+}
+// four consecutive rows of one column: lane gets M[kb + 4 (l/32) + s][n0 + l%32], s < 4
+template <int D>
+__device__ __forceinline__ u32x2 swz_col4(const uint16_t* m, int kb, int n0, int lane) {
+  const int g = lane >> 4, c = lane & 15, h = lane >> 5;
+  const int col = n0 + 16 * (g & 1) + 4 * (c & 3);
+  return lds_tr4(m + swz_off<D>(kb + 4 * h + (c >> 2), col));
+}
+
 __device__ __forceinline__ uint32_t xcd_remap(uint32_t bid, uint32_t total) {
   if (total % 8u != 0u) return bid;
   return (bid % 8u) * (total / 8u) + bid / 8u;
