@@ -22,7 +22,10 @@
 // Both tiles are double-buffered with the next block's global loads in flight
 // during the current block's MFMAs; the row pitch keeps the 16-byte operand
 // reads and the transpose reads free of LDS bank conflicts.
-// The two key halves are merged at the end like split-K partial softmaxes.
+// The two key halves are merged at the end like split-K partial softmaxes,
+// each wave finishing half of the output tiles.  H_i and Z_i for the linear
+// branch are copied asynchronously into the staging buffer the last critical
+// block leaves free, while that block is processed.
 #include <type_traits>
 
 #include "sla_device.h"
@@ -131,12 +134,29 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs args) {
 
   // One key block: S^T = K Q^T, online softmax (base 2, lazy rescale), O^T += V^T P^T.
   // MASKED is used only for the padded last key block.
+  // The buffer the last key block leaves free receives H_i^T (swizzled tile)
+  // and Z_i through asynchronous copies, so the linear epilogue reads LDS.
+  const int hbuf = cnt > 0 ? (((cnt - 1) & 1) ^ 1) : 1;
+  uint16_t* hsw = smem + hbuf * C::kBuf;
+  float* zsw = reinterpret_cast<float*>(hsw + D * D);
+  auto copy_hz = [&]() {
+    if constexpr (LINEAR) {
+      copy_swz<D>(args.hst + (static_cast<size_t>(bh) * T + i) * D * D, hsw, D, wave, 4, lane);
+      if (wave == 3 && lane < D / 2)
+        gl_to_lds16(args.zst + (static_cast<size_t>(bh) * T + i) * 2 * D + 4 * lane, zsw);
+    }
+  };
+  if (cnt == 0) copy_hz();
+
   auto step = [&](int n, auto masked_tag) {
     constexpr bool MASKED = decltype(masked_tag)::value;
     const int j = DENSE ? n : lrow[n];
     const int buf = n & 1;
     const bool more = n + 1 < cnt;
-    if (more) load_block(DENSE ? n + 1 : lrow[n + 1]);
+    if (more)
+      load_block(DENSE ? n + 1 : lrow[n + 1]);
+    else
+      copy_hz();   // buffer buf ^ 1 is no longer read
     const uint16_t* ks = smem + buf * C::kBuf;
     const uint16_t* vt = ks + 64 * KP;
     f32x16 st = {};
@@ -203,25 +223,37 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs args) {
 #undef SLA_LOAD_BLOCK
 #undef SLA_STORE_BLOCK
 
-  // ---- merge the two key halves (split-K style) ----
-  constexpr int NACC = C::NCT * 16;
-  float* ex = reinterpret_cast<float*>(smem);              // [qh][NACC][64]
-  float* exm = ex + 2 * NACC * 64;                         // [qh][64]
-  float* exl = exm + 128;                                  // [qh][64]
-  float* osl = exl + 128;                                  // [D][64] fp32 O_s^T (linear path)
+  // ---- merge the two key halves (split-K style): wave (kh, qh) finishes the
+  // O_s^T tiles ct = NH kh .. NH kh + NH - 1 and hands the others to its partner.
+  constexpr int NH = C::NCT / 2;
+  float* ex = reinterpret_cast<float*>(smem + (hbuf ^ 1) * C::kBuf);   // [wave][NH][16][64]
+  float* exm = ex + 4 * NH * 16 * 64;                                    // [wave][64]
+  float* exl = exm + 4 * 64;                                             // [wave][64]
   __syncthreads();
-  if (kh == 1) {
+  f32x16 fin[NH];
+  if (kh == 0) {
 #pragma unroll
-    for (int ct = 0; ct < C::NCT; ++ct)
+    for (int x = 0; x < NH; ++x) {
+      fin[x] = acc[x];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) ex[(qh * NACC + ct * 16 + e) * 64 + lane] = acc[ct][e];
-    exm[qh * 64 + lane] = m_run;
-    exl[qh * 64 + lane] = l_run;
+      for (int e = 0; e < 16; ++e) ex[((wave * NH + x) * 16 + e) * 64 + lane] = acc[NH + x][e];
+    }
+  } else {
+#pragma unroll
+    for (int x = 0; x < NH; ++x) {
+      fin[x] = acc[NH + x];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) ex[((wave * NH + x) * 16 + e) * 64 + lane] = acc[x][e];
+    }
   }
+  exm[wave * 64 + lane] = m_run;
+  exl[wave * 64 + lane] = l_run;
+  __builtin_amdgcn_s_waitcnt(0);   // this wave's H / Z copies have landed
   __syncthreads();
   const bool valid_row = row < L;
-  if (kh == 0) {
-    const float m2 = exm[qh * 64 + lane], l2 = exl[qh * 64 + lane];
+  const int partner = wave ^ 1;
+  {
+    const float m2 = exm[partner * 64 + lane], l2 = exl[partner * 64 + lane];
     const float ms = fmaxf(m_run, m2);
     float a1 = 0.f, a2 = 0.f, inv = 0.f, lse_v = -INFINITY;
     if (ms != -INFINITY) {
@@ -234,49 +266,34 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs args) {
       }
     }
 #pragma unroll
-    for (int ct = 0; ct < C::NCT; ++ct)
+    for (int x = 0; x < NH; ++x)
 #pragma unroll
       for (int e = 0; e < 16; ++e)
-        acc[ct][e] = (a1 * acc[ct][e] + a2 * ex[(qh * NACC + ct * 16 + e) * 64 + lane]) * inv;
-    if (hl == 0) args.lse[bh * N + row] = valid_row ? lse_v : -INFINITY;
-    if constexpr (!LINEAR) {
-      // O = O_s; lane holds O^T[c = 32 ct + 8 (e/4) + 4 hl + e%4][row]
-      uint16_t* orow = args.o + head + static_cast<size_t>(row) * D;
-#pragma unroll
-      for (int ct = 0; ct < C::NCT; ++ct)
-#pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4) {
-          const int c = 32 * ct + 8 * e4 + 4 * hl;
-          u32x2 v = {0u, 0u};
-          if (valid_row)
-            v = u32x2{pack_bf16x2(acc[ct][4 * e4], acc[ct][4 * e4 + 1]),
-                      pack_bf16x2(acc[ct][4 * e4 + 2], acc[ct][4 * e4 + 3])};
-          st8(orow + c, v);
-        }
-    } else {
-#pragma unroll
-      for (int ct = 0; ct < C::NCT; ++ct)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int c = 32 * ct + 8 * (e / 4) + 4 * hl + (e % 4);
-          osl[c * 64 + 32 * qh + n32] = acc[ct][e];
-        }
-    }
+        fin[x][e] = (a1 * fin[x][e] + a2 * ex[((partner * NH + x) * 16 + e) * 64 + lane]) * inv;
+    if (kh == 0 && hl == 0) args.lse[bh * N + row] = valid_row ? lse_v : -INFINITY;
   }
-
+  // lane holds O_s^T[c = 32 (NH kh + x) + 8 (e/4) + 4 hl + e%4][row]
+  uint16_t* orow = args.o + head + static_cast<size_t>(row) * D;
   if constexpr (!LINEAR) {
-    // no marginal blocks: Y = 0, den = 0
-    if (kh == 1) {
-      uint16_t* yrow = args.y + head + static_cast<size_t>(row) * D;
+    // O = O_s; no marginal blocks: Y = 0, den = 0
 #pragma unroll
-      for (int c = 8 * hl; c < D; c += 16) st16(yrow + c, u32x4{0u, 0u, 0u, 0u});
-      if (hl == 0) args.den[bh * N + row] = 0.f;
-    }
+    for (int x = 0; x < NH; ++x)
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const int c = 32 * (NH * kh + x) + 8 * e4 + 4 * hl;
+        u32x2 v = {0u, 0u};
+        if (valid_row)
+          v = u32x2{pack_bf16x2(fin[x][4 * e4], fin[x][4 * e4 + 1]),
+                    pack_bf16x2(fin[x][4 * e4 + 2], fin[x][4 * e4 + 3])};
+        st8(orow + c, v);
+      }
+    uint16_t* yrow = args.y + head + static_cast<size_t>(row) * D;
+#pragma unroll
+    for (int c = (D / 2) * kh + 8 * hl; c < (D / 2) * (kh + 1); c += 16) st16(yrow + c, u32x4{0u, 0u, 0u, 0u});
+    if (kh == 0 && hl == 0) args.den[bh * N + row] = 0.f;
     return;
   } else {
-    // ---- linear branch: Y^T = (H_i^T phi(Q)^T) / den ----
-    const uint16_t* hrow = args.hst + (static_cast<size_t>(bh) * T + i) * D * D;
-    const float* zrow = args.zst + (static_cast<size_t>(bh) * T + i) * 2 * D;
+    // ---- linear branch: Y^T = (H_i^T phi(Q)^T) / den, wave (kh = c half, qh) ----
     bf16x8 pq[C::NCC];
     float dpart = 0.f;
 #pragma unroll
@@ -286,7 +303,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs args) {
         const __bf16 r = static_cast<__bf16>(phi(static_cast<float>(qf[cc][s])));
         pq[cc][s] = r;
         const int a = 16 * cc + 8 * hl + s;
-        dpart += static_cast<float>(r) * (zrow[a] + zrow[D + a]);
+        dpart += static_cast<float>(r) * (zsw[a] + zsw[D + a]);
       }
     }
     const float den_v = dpart + __shfl_xor(dpart, 32);
@@ -296,15 +313,15 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs args) {
 #pragma unroll
     for (int ct = 0; ct < NCL; ++ct) {
       lin[ct] = f32x16{};
-      const uint16_t* hr = hrow + static_cast<size_t>((D / 2) * kh + 32 * ct + n32) * D + 8 * hl;
+      const int c = (D / 2) * kh + 32 * ct + n32;
 #pragma unroll
       for (int cc = 0; cc < C::NCC; ++cc)
-        lin[ct] = mfma32(as_bf16x8(ld16(hr + 16 * cc)), pq[cc], lin[ct]);
+        lin[ct] = mfma32(as_bf16x8(ld16(hsw + swz_off<D>(c, 16 * cc + 8 * hl))), pq[cc], lin[ct]);
     }
     if (kh == 0 && hl == 0) args.den[bh * N + row] = valid_row ? den_v : 0.f;
     __syncthreads();   // exchange area free again: reuse it for Y (bf16 [64][D + 8])
     constexpr int YP = D + 8;
-    uint16_t* ysl = smem;
+    uint16_t* ysl = reinterpret_cast<uint16_t*>(ex);
     uint16_t* yrow = args.y + head + static_cast<size_t>(row) * D;
 #pragma unroll
     for (int ct = 0; ct < NCL; ++ct)
@@ -319,7 +336,6 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs args) {
     __syncthreads();
     // ---- fusion: O^T = O_s^T + W Y^T, wave (kh = o half, qh) ----
     const uint16_t* ys = ysl + (32 * qh + n32) * YP + 8 * hl;
-    uint16_t* orow = args.o + head + static_cast<size_t>(row) * D;
 #pragma unroll
     for (int ot = 0; ot < NCL; ++ot) {
       const int obase = (D / 2) * kh + 32 * ot;
@@ -333,7 +349,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs args) {
         const int o0 = obase + 8 * e4 + 4 * hl;
         float r[4];
 #pragma unroll
-        for (int x = 0; x < 4; ++x) r[x] = out[4 * e4 + x] + osl[(o0 + x) * 64 + 32 * qh + n32];
+        for (int x = 0; x < 4; ++x) r[x] = out[4 * e4 + x] + fin[ot][4 * e4 + x];
         st8(orow + o0, valid_row ? u32x2{pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3])}
                                  : u32x2{0u, 0u});
       }

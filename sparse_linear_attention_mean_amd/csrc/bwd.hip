@@ -276,16 +276,31 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(
     }
   };
 
+  // The buffer the last key block leaves free receives this block's dQ rows
+  // (the linear part written by the preparation kernel, fp32 64 x D) through
+  // asynchronous copies, so the final read-modify-write reads LDS.
+  const int dqbuf = cnt > 0 ? (((cnt - 1) & 1) ^ 1) : 1;
+  float* dqs = reinterpret_cast<float*>(smem + dqbuf * C::kBuf);
+  auto copy_dq = [&]() {
+    const float* src = dq + head + static_cast<size_t>(i) * kBlock * D;
+    constexpr int kCopies = 64 * D / 4 / 64;   // 16-byte chunks / 64 per copy
+    for (int it = wave; it < kCopies; it += 4) gl_to_lds16(src + 4 * (it * 64 + lane), dqs + it * 256);
+  };
   if (cnt > 0) {
     load(lrow[0]);
     store(0, lrow[0]);
     __syncthreads();
+  } else {
+    copy_dq();
   }
   for (int n = 0; n < cnt; ++n) {
     const int j = lrow[n];
     const int buf = n & 1;
     const int jn = n + 1 < cnt ? lrow[n + 1] : 0;
-    if (n + 1 < cnt) load(jn);
+    if (n + 1 < cnt)
+      load(jn);
+    else
+      copy_dq();   // buffer buf ^ 1 is no longer read
     const uint16_t* ks = smem + buf * C::kBuf;
     const uint16_t* vs = ks + 64 * KP;
     f32x16 st = {}, dpt = {};
@@ -316,29 +331,41 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(
     if (n + 1 < cnt) store(buf ^ 1, jn);
     __syncthreads();
   }
-  // merge the key halves and add the linear part
+  // merge the key halves: wave (kh, qh) finishes the tiles at = NH kh .. NH kh + NH - 1
+  // and hands the others to its partner (other kh); then add the linear part
+  constexpr int NH = C::NAT / 2;
+  float* ex = reinterpret_cast<float*>(smem + (dqbuf ^ 1) * C::kBuf);   // [wave][NH][16][64]
   __syncthreads();
-  float* ex = reinterpret_cast<float*>(smem);   // [qh][NAT*16][64]
-  constexpr int NACC = C::NAT * 16;
-  if (kh == 1) {
-#pragma unroll
-    for (int at = 0; at < C::NAT; ++at)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) ex[(qh * NACC + at * 16 + e) * 64 + lane] = acc[at][e];
-  }
-  __syncthreads();
+  f32x16 fin[NH];
   if (kh == 0) {
-    // lane holds dQ[q = 32 qh + 8 (e/4) + 4 hl + e%4][a = 32 at + n32]
 #pragma unroll
-    for (int at = 0; at < C::NAT; ++at)
+    for (int x = 0; x < NH; ++x) {
+      fin[x] = acc[x];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int qr = i * kBlock + 32 * qh + 8 * (e / 4) + 4 * hl + (e % 4);
-        float* p = dq + head + static_cast<size_t>(qr) * D + 32 * at + n32;
-        const float sparse = scale * (acc[at][e] + ex[(qh * NACC + at * 16 + e) * 64 + lane]);
-        *p = qr < L ? *p + sparse : 0.f;
-      }
+      for (int e = 0; e < 16; ++e) ex[((wave * NH + x) * 16 + e) * 64 + lane] = acc[NH + x][e];
+    }
+  } else {
+#pragma unroll
+    for (int x = 0; x < NH; ++x) {
+      fin[x] = acc[NH + x];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) ex[((wave * NH + x) * 16 + e) * 64 + lane] = acc[x][e];
+    }
   }
+  __builtin_amdgcn_s_waitcnt(0);   // this wave's dQ copies have landed
+  __syncthreads();
+  const int partner = wave ^ 1;
+  // lane holds dQ[q = 32 qh + 8 (e/4) + 4 hl + e%4][a = 32 at + n32]
+#pragma unroll
+  for (int x = 0; x < NH; ++x)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int ql = 32 * qh + 8 * (e / 4) + 4 * hl + (e % 4);
+      const int a = 32 * (NH * kh + x) + n32;
+      const float sparse = scale * (fin[x][e] + ex[((partner * NH + x) * 16 + e) * 64 + lane]);
+      const int qr = i * kBlock + ql;
+      dq[head + static_cast<size_t>(qr) * D + a] = qr < L ? dqs[ql * D + a] + sparse : 0.f;
+    }
 }
 
 // ---------------------------------------------------------------------------
