@@ -7,7 +7,8 @@ backward) on one batch of seeded synthetic input already resident in HBM.
 Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--mode fwd|fwdbwd] [--no-cpu-baseline]
+                    [--mode fwd|fwdbwd] [--no-cpu-baseline] [--no-side-runs]
+                    [--traffic-probe]
 """
 from __future__ import annotations
 
@@ -40,6 +41,11 @@ def parse():
     ap.add_argument("--mode", choices=("fwd", "fwdbwd"), default="fwdbwd")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-side-runs", action="store_true",
+                    help="skip the linear-branch and dense-baseline side measurements")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="after the timed region, run one device copy of 256 MiB (known bytes) "
+                         "to calibrate hardware traffic counters")
     ap.add_argument("--dense", action="store_true",
                     help="time the same library as dense attention (all blocks critical)")
     return ap.parse_args()
@@ -135,6 +141,73 @@ def cpu_baseline(inp, wl, k_c, k_n):
                    f"forward of all {len(blocks)} query blocks ({t_fwd:.1f} s); backward of the "
                    f"same head ({t_bwd:.1f} s)"),
     }
+
+
+def _timed(fn, warmup, steps):
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
+def linear_branch_rate(wl, inp, q, k, v, w, dev):
+    """Forward with no critical blocks (same negligible fraction): the linear
+    branch alone.  Algorithmic bytes: K, V read, the per-block states h, z
+    written and read once (bf16 as stored), Q read, O written."""
+    import torch
+
+    from sparse_linear_attention_mean_amd.attention import SlaProblem
+
+    prob = SlaProblem.create(wl.batch, wl.heads, wl.seq_len, wl.head_dim, 0.0,
+                             wl.frac_negligible, valid_len=wl.valid_len, device=dev)
+    o = torch.empty(prob.shape(), dtype=torch.bfloat16, device=dev)
+    mask = prob.new_mask()
+    ms = _timed(lambda: prob.forward(q, k, v, w, o=o, mask=mask), 2, 5)
+    bh, n, d, t = wl.batch * wl.heads, wl.seq_len, wl.head_dim, wl.num_blocks
+    tok = 2 * bh * n * d                         # one bf16 [B,H,N,d] tensor
+    states = bh * t * (d * d + 2 * d) * 2        # h (d x d) and z (two bf16 parts) per block
+    nbytes = 2 * tok + 2 * states + tok + tok
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"ms": round(ms, 4), "bytes": nbytes, "GB/s": round(gbs, 1),
+            "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
+            "note": "sla_forward with frac_critical = 0 and the same frac_negligible"}
+
+
+def dense_ratio(wl, q, k, v, w, do, dev, with_bwd, sla_ms):
+    """The same library and kernels with every block critical (frac_critical
+    = 1, frac_negligible = 0): the dense attention baseline of the same shape."""
+    import torch
+
+    from sparse_linear_attention_mean_amd.attention import SlaProblem
+
+    prob = SlaProblem.create(wl.batch, wl.heads, wl.seq_len, wl.head_dim, 1.0, 0.0,
+                             valid_len=wl.valid_len, device=dev)
+    o = torch.empty(prob.shape(), dtype=torch.bfloat16, device=dev)
+    mask = prob.new_mask()
+    grads = None
+    if with_bwd:
+        shp = prob.shape()
+        grads = tuple(torch.empty(shp, dtype=torch.float32, device=dev) for _ in range(3)) + (
+            torch.empty((wl.head_dim, wl.head_dim), dtype=torch.float32, device=dev),)
+
+    def step():
+        prob.forward(q, k, v, w, o=o, mask=mask)
+        if with_bwd:
+            prob.backward(q, k, v, w, o, do, mask, grads=grads)
+
+    ms = _timed(step, 1, 2)
+    return {"dense_ms_per_step": round(ms, 3), "sla_ms_per_step": round(sla_ms, 4),
+            "speedup": round(ms / sla_ms, 2),
+            "note": "frac_critical = 1, frac_negligible = 0 through the same entry points"}
 
 
 def main():
@@ -256,6 +329,16 @@ def main():
             rec["fwd_tflops"] = round(flops_fwd_crit / (fwd_ms * 1e-3) / 1e12, 2)
         if bwd_ms > 0:
             rec["bwd_tflops"] = round(flops_bwd_crit / (bwd_ms * 1e-3) / 1e12, 2)
+    if not args.no_side_runs and not args.dense:
+        rec["linear_branch"] = linear_branch_rate(wl, inp, q, k, v, w, dev)
+        rec["vs_dense"] = dense_ratio(wl, q, k, v, w, do, dev, with_bwd, ms)
+    if args.traffic_probe:
+        src = torch.empty(128 << 20, dtype=torch.bfloat16, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)   # reads and writes 256 MiB each
+        torch.cuda.synchronize()
+        rec["traffic_probe_bytes"] = 2 * src.numel()
     if not args.no_cpu_baseline:
         sys.path.insert(0, ROOT)
         rec["cpu_baseline"] = cpu_baseline(inp, wl, k_c, k_n)
