@@ -10,8 +10,8 @@
 // The same kernel serves the backward with the transposed marginal matrix
 // (dh_j = sum_{i : j marginal for i} dH_i).
 //
-// Operands: S in the K-tiled layout states[bh][j / 8][n][j % 8] (bf16), so
-// that one 16-byte load gives a lane the 8 consecutive key blocks an MFMA A
+// Operands: S in the K-tiled layout states[bh][j / 4][n][j % 4] (bf16), so
+// that two 8-byte reads give a lane the 8 consecutive key blocks an MFMA A
 // operand needs; M0 as 32-bit words of marginal bits, stored word-major
 // (word w of every row contiguous), expanded to bf16 through a 256-entry LDS
 // table.  C^T[n][i] = sum_j S[j][n] M0[i][j] is
@@ -27,10 +27,14 @@ constexpr int kAggNTile = 64;    // state columns per workgroup
 constexpr int kAggIWave = 128;   // query rows per wave
 constexpr int kAggIChunk = 512;  // query rows per workgroup (4 waves)
 constexpr int kAggKChunk = 512;  // key blocks of the state strip staged in LDS per pass
+// LDS strip: pairs of 4-block planes, 2 x 64 columns x 4 blocks (1 KB, one
+// copy instruction) plus 128 bytes of padding, so the four lane groups of an
+// A-operand read (planes 2 g apart) fall on different banks
+constexpr int kAggPair = 2 * kAggNTile * 4 + 64;   // bf16 elements per plane pair
 
 // One workgroup owns a 64-column strip of S and 512 rows of C.  The strip is
 // shared by the four waves (each owns 128 rows), so it is copied once into
-// LDS with asynchronous global->LDS loads (64 KB per pass of 512 key blocks)
+// LDS with asynchronous global->LDS loads (72 KB per pass of 512 key blocks)
 // instead of being fetched by every wave; the marginal words stream from
 // global memory (they are small and stay in L2) two k-steps ahead, 32
 // contiguous bytes per lane and k-step.
@@ -41,7 +45,7 @@ __global__ __launch_bounds__(256, 2) void aggregate_kernel(const uint32_t* __res
                                                           int NB, int DD, int ntiles,
                                                           int ichunks) {
   __shared__ u32x4 table[256];
-  __shared__ __attribute__((aligned(16))) uint16_t strip[kAggKChunk / 8 * kAggNTile * 8];
+  __shared__ __attribute__((aligned(16))) uint16_t strip[kAggKChunk / 8 * kAggPair];
   const int tid = threadIdx.x;
   {
     uint32_t w[4];
@@ -74,7 +78,7 @@ __global__ __launch_bounds__(256, 2) void aggregate_kernel(const uint32_t* __res
 #pragma unroll
     for (int q = 0; q < 8; ++q) acc[m][q] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const uint16_t* sbase = states + static_cast<size_t>(bh) * (Tp / 8) * NB * 8;
+  const uint16_t* sbase = states + static_cast<size_t>(bh) * Tp * NB;
   const int ksteps = Tp / 32;
   const uint32_t* bcol = bits + static_cast<size_t>(bh) * ksteps * Tp + (rows_ok ? rbase : 0);
   struct Words {
@@ -90,7 +94,11 @@ __global__ __launch_bounds__(256, 2) void aggregate_kernel(const uint32_t* __res
   auto step = [&](const Words& w, int kl) {
     bf16x8 a[4], b[8];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) a[m] = as_bf16x8(ld16(strip + ((4 * kl + g) * kAggNTile + 16 * m + r16) * 8));
+    for (int m = 0; m < 4; ++m) {
+      // planes 8 kl + 2 g and 8 kl + 2 g + 1 = pair 4 kl + g, halves 0 and 1
+      const uint16_t* pr = strip + (4 * kl + g) * kAggPair + (16 * m + r16) * 4;
+      a[m] = as_bf16x8(ld8(pr), ld8(pr + kAggNTile * 4));
+    }
 #pragma unroll
     for (int q = 0; q < 8; ++q)
       b[q] = as_bf16x8(table[((q < 4 ? w.lo[q & 3] : w.hi[q & 3]) >> (8 * g)) & 0xffu]);
@@ -105,9 +113,9 @@ __global__ __launch_bounds__(256, 2) void aggregate_kernel(const uint32_t* __res
   for (int kc0 = 0; kc0 < Tp; kc0 += kAggKChunk) {
     const int kn = Tp - kc0 < kAggKChunk ? Tp - kc0 : kAggKChunk;   // multiple of 32
     __syncthreads();   // table ready / previous pass fully consumed
-    for (int gi = wave; gi < kn / 8; gi += 4)
-      gl_to_lds16(sbase + ((static_cast<size_t>(kc0 / 8 + gi)) * NB + n0 + lane) * 8,
-                  strip + gi * kAggNTile * 8);
+    for (int gi = wave; gi < kn / 8; gi += 4)   // plane pair gi: lanes 0-31 plane 2 gi, 32-63 plane 2 gi + 1
+      gl_to_lds16(sbase + (static_cast<size_t>(kc0 / 4 + 2 * gi + (lane >> 5)) * NB + n0 + 2 * (lane & 31)) * 4,
+                  strip + gi * kAggPair);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     const int k0 = kc0 / 32;

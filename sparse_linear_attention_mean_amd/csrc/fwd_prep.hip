@@ -39,10 +39,11 @@ __device__ __forceinline__ float tree16(const float* p, int stride) {
 //   h_j^T[c][a] = sum_t v_t[c] * phi(k_t)[a],  z_j[a] = sum_t phi(k_t)[a],
 //   kbar_j[a]   = mean_t k_t[a]            (valid tokens t only)
 // h^T and z are written as bf16 in the "K-tiled" layout the aggregation GEMM
-// reads as its A operand: states[bh][j / 8][n][j % 8], n = c*D + a for h^T,
+// reads as its A operand: states[bh][j / 4][n][j % 4], n = c*D + a for h^T,
 // n = D*D + a for bf16(z), n = D*D + D + a for bf16(z - bf16(z)).  One
-// workgroup handles 8 consecutive key blocks; every lane writes the block
-// values of one state entry as two 8-byte stores (blocks 0-3, 4-7); it has one
+// workgroup handles 8 consecutive key blocks (two planes of 4); every lane
+// writes the 4 block values of one state entry of a plane as one 8-byte
+// store, so a wave writes whole 512-byte runs; it has one
 // wave per 32x32 tile of h^T (16 waves for D = 128), so K and V are read
 // once.  The tiles are staged row-major (a plain copy, phi applied on the
 // way) and both MFMA operands, which run over tokens, come from LDS
@@ -112,7 +113,7 @@ __global__ __launch_bounds__(KvCfg<D>::kThreads) void kv_state_kernel(
   const int sa = tid % D, sl = tid / D;                     // column-sum unit: column, slice
   // bf16 pairs of (block 2p, block 2p+1) per result entry, four blocks at a time
   uint32_t stash[16][2];
-  uint16_t* out = states + (static_cast<size_t>(bh) * groups + g) * NB * 8;
+  uint16_t* out = states + (static_cast<size_t>(bh) * groups + g) * NB * 8;   // planes 2g, 2g + 1
   load(g * 8);
 #pragma unroll
   for (int jj = 0; jj < 8; ++jj) {
@@ -160,7 +161,8 @@ __global__ __launch_bounds__(KvCfg<D>::kThreads) void kv_state_kernel(
         for (int i = 0; i < 16; ++i) {
           const int c = 32 * ct + 8 * (i / 4) + 4 * hl + (i % 4);
           const int a = 32 * at + n32;
-          st8(out + (static_cast<size_t>(c) * D + a) * 8 + 4 * (jj >> 2), u32x2{stash[i][0], stash[i][1]});
+          st8(out + static_cast<size_t>(jj >> 2) * NB * 4 + (static_cast<size_t>(c) * D + a) * 4,
+              u32x2{stash[i][0], stash[i][1]});
         }
       }
     }
@@ -199,8 +201,11 @@ __global__ __launch_bounds__(KvCfg<D>::kThreads) void kv_state_kernel(
   }
 
   __syncthreads();   // zst complete
-  for (int e = tid; e < 2 * D; e += C::kThreads)
-    st16(out + (static_cast<size_t>(D) * D + e) * 8, ld16(&zst[e * 8]));
+  for (int e = tid; e < 2 * D; e += C::kThreads) {
+    const u32x4 zz = ld16(&zst[e * 8]);
+    st8(out + (static_cast<size_t>(D) * D + e) * 4, u32x2{zz[0], zz[1]});
+    st8(out + static_cast<size_t>(NB) * 4 + (static_cast<size_t>(D) * D + e) * 4, u32x2{zz[2], zz[3]});
+  }
 }
 
 // ---------------------------------------------------------------------------

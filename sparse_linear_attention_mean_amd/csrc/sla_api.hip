@@ -139,7 +139,7 @@ WorkspaceLayout workspace_layout(const Dims& d) {
   w.col_cnt = take(BH * d.T * 4);
   w.rbits = take(BH * d.Tp * (d.Tp / 32) * 4);
   w.cbits = take(BH * d.Tp * (d.Tp / 32) * 4);
-  w.states = take(BH * (d.Tp / 8) * d.NB * 8 * 2);
+  w.states = take(BH * d.Tp * d.NB * 2);
   w.dstate = take(BH * d.T * d.D * d.D * 2);
   w.dstate_z = take(BH * d.T * 2 * d.D * 4);
   w.dsum = take(BH * d.N * 4);

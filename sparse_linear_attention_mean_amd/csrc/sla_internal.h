@@ -29,7 +29,7 @@ struct WorkspaceLayout {
   size_t col, col_cnt;      // int32 [BH, T, T] critical query blocks per column, int32 [BH, T]
   size_t rbits, cbits;      // uint32 [BH, Tp/32, Tp] marginal bits by row / by column, word-major:
                             // bit b of word w of row x is entry (x, 32 w + b)
-  size_t states;            // bf16 [BH, Tp/8, NB, 8]  (forward h/z states; backward dH/dZ)
+  size_t states;            // bf16 [BH, Tp/4, NB, 4]  (forward h/z states; backward dH/dZ)
   size_t dstate;            // bf16 [BH, T, D*D] + fp32 [BH, T, 2, D] aggregated backward states
   size_t dstate_z;
   size_t dsum;              // fp32 [BH, N]  D_r of the backward
