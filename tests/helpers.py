@@ -43,6 +43,7 @@ def assert_close(name, got, ref, rel=REL_L2, atol=MAX_ABS):
 def to_np(t):
     import torch
 
+    t = t.detach()
     if t.dtype == torch.bfloat16:
         return t.float().cpu().numpy().astype(np.float64)
     return t.cpu().numpy()

@@ -1,0 +1,81 @@
+"""GPU tests of the autograd wrapper and of mask reuse across calls.
+
+The wrapper calls the same two entry points as the other parity tests, so its
+output and gradients are compared with the oracle (fp64, the GPU's own mask
+injected) to the same tolerance; mask reuse is checked for byte-identical
+output against a fresh computed-mask call and for parity with the oracle
+under the cached mask when the inputs change."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as orc
+from helpers import assert_close, decoded, device_inputs, to_np
+from sparse_linear_attention_mean_amd.inputs import make_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    global SparseLinearAttention
+    from sparse_linear_attention_mean_amd.autograd import SparseLinearAttention  # noqa: F811
+
+
+@pytest.mark.parametrize("d,grid,vl", [(64, (8, 8, 16), 1000), (128, (4, 8, 32), 1024)])
+def test_autograd_gradients_match_oracle(d, grid, vl):
+    b, h, n, fc, fn = 1, 2, 1024, 0.125, 0.25
+    inp = make_inputs(b, h, n, d, grid, vl, seed=11, with_grad=True)
+    dev = device_inputs(inp)
+    q, k, v = (dev[x].clone().requires_grad_(True) for x in ("q", "k", "v"))
+    w0 = dev["w"].float()
+    mod = SparseLinearAttention(d, fc, fn, valid_len=vl, weight=w0, reuse_mask=True)
+    o = mod(q, k, v)
+    o.backward(dev["do"])
+    torch.cuda.synchronize()
+
+    # parity protocol: the GPU's mask is injected into the oracle
+    x = decoded(inp)
+    mask = mod.cached_mask.cpu().numpy()
+    ref = orc.forward(x["q"], x["k"], x["v"], x["w"], 0.0, 0.0, valid_len=vl, mask=mask)
+    assert_close("o", to_np(o), ref["o"])
+    g = orc.backward(x["q"], x["k"], x["v"], x["w"], x["do"], mask, valid_len=vl)
+    for name, t in (("dq", q.grad), ("dk", k.grad), ("dv", v.grad)):
+        assert t.dtype == torch.bfloat16
+        r = g[name]
+        assert_close(name, to_np(t), r, atol=2e-2 * float(np.abs(r).max()))
+    assert mod.weight.grad.dtype == torch.float32
+    assert_close("dw", to_np(mod.weight.grad), g["dw"], atol=2e-2 * float(np.abs(g["dw"]).max()))
+
+
+def test_mask_reuse_is_exact_and_skips_classification():
+    b, h, n, d, vl, fc, fn = 1, 2, 1024, 64, 1024, 0.125, 0.25
+    inp = make_inputs(b, h, n, d, (8, 8, 16), vl, seed=5)
+    dev = device_inputs(inp)
+    mod = SparseLinearAttention(d, fc, fn, valid_len=vl, reuse_mask=True, weight=dev["w"].float())
+    with torch.no_grad():
+        o1 = mod(dev["q"], dev["k"], dev["v"])        # computes and caches the mask
+        m1 = mod.cached_mask.clone()
+        o2 = mod(dev["q"], dev["k"], dev["v"])        # same inputs, cached mask
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)), "reused mask changed the output"
+
+    # new inputs: the cached mask is used as given, not recomputed
+    inp2 = make_inputs(b, h, n, d, (8, 8, 16), vl, seed=6)
+    dev2 = device_inputs(inp2)
+    with torch.no_grad():
+        o3 = mod(dev2["q"], dev2["k"], dev2["v"])
+    torch.cuda.synchronize()
+    assert torch.equal(mod.cached_mask, m1)
+    x = decoded(inp2)
+    x["w"] = decoded(inp)["w"]
+    ref = orc.forward(x["q"], x["k"], x["v"], x["w"], 0.0, 0.0, valid_len=vl,
+                      mask=m1.cpu().numpy())
+    assert_close("o (cached mask)", to_np(o3), ref["o"])
+    own = orc.forward(x["q"], x["k"], x["v"], x["w"], fc, fn, valid_len=vl)["mask"]
+    assert not np.array_equal(own, m1.cpu().numpy()), "inputs too similar to tell the masks apart"
+
+    mod.reset_mask()
+    assert mod.cached_mask is None
