@@ -29,6 +29,15 @@ that the rest supports (each marked "reading"):
 * tokens at or past ``valid_len`` are padding: excluded from pooling,
   softmax and states; padded rows output zero and get zero gradients.
 
+A variant from the pages on SALAD ("Achieve High-Sparsity Attention via
+Efficient Linear Attention Tuning for Video Diffusion Transformer", method:
+parallel architecture and the static-dynamic scaling) runs the linear branch
+next to the sparse one over every token instead of the marginal blocks only,
+and scales the projected linear output by a scalar gate in [0, 1] (reading:
+the layer's static projection is W, the input- and timestep-dependent factor
+is supplied as the number ``gate``).  ``linear="global"`` selects it; the SLA
+default is ``linear="marginal"`` with no gate.
+
 Everything is written out directly: two-pass softmax, direct sums over the
 marginal blocks, no online rescaling, no complement tricks.  Inputs are fp64
 arrays (decode bf16 bits with ``decode_bf16``).  The one rounding the method
@@ -164,14 +173,25 @@ def _valid_keys(blocks, valid_len: int, block: int = BLOCK) -> np.ndarray:
     return keys[keys < valid_len]
 
 
+def _linear_blocks(mask_row, linear: str):
+    """Key blocks whose states feed the linear branch of one query block."""
+    if linear == "marginal":
+        return np.flatnonzero(mask_row == 0)
+    if linear == "global":
+        return np.arange(mask_row.size)
+    raise ValueError(f"unknown linear branch {linear!r}")
+
+
 def forward_head(q, k, v, w, mask, valid_len, scale, blocks=None, block: int = BLOCK,
-                 states=None):
+                 states=None, linear: str = "marginal", gate: float = 1.0):
     """SLA forward for one (batch, head) with a given three-way block mask.
 
     q, k, v: [N, d] fp64; w: [d, d]; mask: [T, T] int8.  ``blocks`` limits the
-    query blocks computed (default all).  Returns a dict of [N, ...] arrays
-    (rows of blocks not computed are left zero): o, o_sparse, y, lse, den;
-    and the per-query-block H [T, d, d], Z [T, d] that were used."""
+    query blocks computed (default all).  ``linear``: "marginal" (SLA) or
+    "global" (every key block, SALAD-style), with O = O_s + gate * Y W^T.
+    Returns a dict of [N, ...] arrays (rows of blocks not computed are left
+    zero): o, o_sparse, y (ungated), lse, den; and the per-query-block H
+    [T, d, d], Z [T, d] that were used."""
     n, d = q.shape
     t = n // block
     if blocks is None:
@@ -198,8 +218,8 @@ def forward_head(q, k, v, w, mask, valid_len, scale, blocks=None, block: int = B
             l = p.sum(axis=1, keepdims=True)
             o_s[lo:hi] = (p @ v[keys]) / l
             lse[lo:hi] = (m + np.log(l))[:, 0]
-        # linear branch: states summed over the marginal blocks
-        marg = np.flatnonzero(mask[i] == 0)
+        # linear branch: states summed over the marginal (or all) blocks
+        marg = _linear_blocks(mask[i], linear)
         hi_state = h[marg].sum(axis=0) if marg.size else np.zeros((d, d))
         zi_state = z[marg].sum(axis=0) if marg.size else np.zeros(d)
         big_h[i], big_z[i] = hi_state, zi_state
@@ -211,29 +231,31 @@ def forward_head(q, k, v, w, mask, valid_len, scale, blocks=None, block: int = B
         yi[pos] = num[pos] / dn[pos, None]
         y[lo:hi] = yi
         den[lo:hi] = dn
-        # fusion: sparse output plus the projected linear output
-        o[lo:hi] = o_s[lo:hi] + yi @ w.T
+        # fusion: sparse output plus the (gated) projected linear output
+        o[lo:hi] = o_s[lo:hi] + gate * (yi @ w.T)
     return dict(o=o, o_sparse=o_s, y=y, lse=lse, den=den, H=big_h, Z=big_z)
 
 
 # ----------------------------------------------------------------------------
 # backward, one head (mask held fixed: no gradient through the classifier)
 # ----------------------------------------------------------------------------
-def backward_head(q, k, v, w, do, mask, valid_len, scale, block: int = BLOCK, fwd=None):
+def backward_head(q, k, v, w, do, mask, valid_len, scale, block: int = BLOCK, fwd=None,
+                  linear: str = "marginal", gate: float = 1.0):
     """Gradients of sum(dO * O) for one head with a fixed mask.
 
     Returns dq, dk, dv [N, d] and this head's contribution to dw [d, d]."""
     n, d = q.shape
     t = n // block
     if fwd is None:
-        fwd = forward_head(q, k, v, w, mask, valid_len, scale, block=block)
+        fwd = forward_head(q, k, v, w, mask, valid_len, scale, block=block, linear=linear,
+                           gate=gate)
     o_s, y, lse, den = fwd["o_sparse"], fwd["y"], fwd["lse"], fwd["den"]
     big_h, big_z = fwd["H"], fwd["Z"]
     valid = np.arange(n) < valid_len
     dov = np.where(valid[:, None], do, 0.0)
-    # projection: O = O_s + Y W^T
-    dy = dov @ w
-    dw = dov.T @ y
+    # projection: O = O_s + gate * Y W^T
+    dy = gate * (dov @ w)
+    dw = gate * (dov.T @ y)
     dq = np.zeros((n, d))
     dk = np.zeros((n, d))
     dv = np.zeros((n, d))
@@ -276,12 +298,12 @@ def backward_head(q, k, v, w, do, mask, valid_len, scale, block: int = BLOCK, fw
         pq = phi(qi)
         d_big_h[i] = pq.T @ d_num
         d_big_z[i] = pq.T @ d_den
-    # linear branch, key/value side: through H_i = sum over marginal j of h_j
+    # linear branch, key/value side: through H_i = sum over marginal (or all) j of h_j
     for j in range(t):
         lo, hi = j * block, min((j + 1) * block, valid_len)
         if hi <= lo:
             continue
-        rows_marg = np.flatnonzero(mask[:, j] == 0)
+        rows_marg = np.flatnonzero(mask[:, j] == 0) if linear == "marginal" else np.arange(t)
         if rows_marg.size == 0:
             continue
         dh = d_big_h[rows_marg].sum(axis=0)
@@ -300,12 +322,13 @@ def backward_head(q, k, v, w, do, mask, valid_len, scale, block: int = BLOCK, fw
 # whole problems [B, H, N, d]
 # ----------------------------------------------------------------------------
 def forward(q, k, v, w, frac_critical, frac_negligible, valid_len=None, scale=None,
-            mask=None, block: int = BLOCK):
+            mask=None, block: int = BLOCK, linear: str = "marginal", gate: float = 1.0):
     """Full SLA forward.  q, k, v: [B, H, N, d] fp64; w: [d, d].
 
     If ``mask`` ([B, H, T, T] int8) is given it is used as is; otherwise it is
-    built by the classifier.  Returns o, o_sparse, y, lse, den, mask, scores
-    (scores only when the mask was built here)."""
+    built by the classifier.  ``linear`` / ``gate`` as in ``forward_head``.
+    Returns o, o_sparse, y, lse, den, mask, scores (scores only when the mask
+    was built here)."""
     bsz, nh, n, d = q.shape
     if n % block:
         raise ValueError("sequence length must be a multiple of the block size")
@@ -327,7 +350,7 @@ def forward(q, k, v, w, frac_critical, frac_negligible, valid_len=None, scale=No
     for b in range(bsz):
         for h in range(nh):
             r = forward_head(q[b, h], k[b, h], v[b, h], w, mask[b, h], valid_len, scale,
-                             block=block)
+                             block=block, linear=linear, gate=gate)
             for name in ("o", "o_sparse", "y", "lse", "den"):
                 out[name][b, h] = r[name]
     out["mask"] = mask
@@ -335,7 +358,8 @@ def forward(q, k, v, w, frac_critical, frac_negligible, valid_len=None, scale=No
     return out
 
 
-def backward(q, k, v, w, do, mask, valid_len=None, scale=None, block: int = BLOCK):
+def backward(q, k, v, w, do, mask, valid_len=None, scale=None, block: int = BLOCK,
+             linear: str = "marginal", gate: float = 1.0):
     """Full SLA backward with a fixed mask.  Returns dq, dk, dv, dw."""
     bsz, nh, n, d = q.shape
     valid_len = n if valid_len is None else valid_len
@@ -345,7 +369,7 @@ def backward(q, k, v, w, do, mask, valid_len=None, scale=None, block: int = BLOC
     for b in range(bsz):
         for h in range(nh):
             r = backward_head(q[b, h], k[b, h], v[b, h], w, do[b, h], mask[b, h],
-                              valid_len, scale, block=block)
+                              valid_len, scale, block=block, linear=linear, gate=gate)
             for name in ("dq", "dk", "dv"):
                 out[name][b, h] = r[name]
             out["dw"] += r["dw"]

@@ -449,3 +449,79 @@ def test_generator_is_seeded_and_grid_structured():
     near = np.mean([q[i] @ k[i + 1] for i in range(0, 400)])
     far = np.mean([q[i] @ k[(i + 250) % 500] for i in range(0, 400)])
     assert near > far
+
+
+# ---------------------------------------------------------------------------
+# global linear branch with a gate (SALAD-style variant)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("valid_len,gate", [(256, 0.37), (201, 1.0)])
+def test_global_linear_branch_closed_form(valid_len, gate):
+    """No critical block: the output is gate * (plain linear attention over every
+    valid token) W^T, written independently of the block states."""
+    bsz, nh, n, d = 1, 2, 256, 8
+    q, k, v = (_rand((bsz, nh, n, d), 90 + s) for s in (1, 2, 3))
+    w = _rand((d, d), 94, std=0.3)
+    mask = _random_mask(bsz, nh, n // B, 9, p=(0.0, 0.6, 0.4))   # marginal / negligible only
+    out = orc.forward(q, k, v, w, 0, 0, valid_len=valid_len, mask=mask, linear="global", gate=gate)
+    fq = np.where(q > 0, q + 1, np.exp(np.minimum(q, 0)))
+    fk = np.where(k > 0, k + 1, np.exp(np.minimum(k, 0)))[:, :, :valid_len]
+    a = np.einsum("bhna,bhta->bhnt", fq, fk)
+    y = np.einsum("bhnt,bhtc->bhnc", a, v[:, :, :valid_len]) / a.sum(-1)[..., None]
+    y[:, :, valid_len:] = 0.0
+    np.testing.assert_allclose(out["y"], y, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(out["o"], gate * (y @ w.T), rtol=1e-12, atol=1e-12)
+
+
+def test_global_linear_branch_special_cases():
+    """gate = 0 leaves the sparse output alone; with every block marginal the
+    global branch is the SLA linear branch; with critical blocks the global
+    branch still covers them (differs from the marginal-only branch)."""
+    q, k, v, w, _, vl = _problem(95, valid_len=180)
+    t = q.shape[2] // B
+    mask = _random_mask(1, 2, t, 3)
+    mask[0, 0, 0] = [1, 0, -1]
+    g0 = orc.forward(q, k, v, w, 0, 0, valid_len=vl, mask=mask, linear="global", gate=0.0)
+    np.testing.assert_array_equal(g0["o"], g0["o_sparse"])
+    allm = np.zeros_like(mask)
+    a = orc.forward(q, k, v, w, 0, 0, valid_len=vl, mask=allm, linear="global", gate=1.0)
+    b = orc.forward(q, k, v, w, 0, 0, valid_len=vl, mask=allm)
+    np.testing.assert_allclose(a["o"], b["o"], rtol=1e-12, atol=1e-13)
+    c = orc.forward(q, k, v, w, 0, 0, valid_len=vl, mask=mask, linear="global")
+    d = orc.forward(q, k, v, w, 0, 0, valid_len=vl, mask=mask)
+    assert np.abs(c["y"] - d["y"]).max() > 1e-3
+
+
+def test_global_linear_backward_matches_central_differences():
+    nh, n, d, vl = 1, 128, 4, 111
+    q, k, v = (_rand((1, nh, n, d), 100 + s) for s in (1, 2, 3))
+    w = _rand((d, d), 104, std=0.4)
+    do = _rand((1, nh, n, d), 105)
+    mask = np.array([[[[1, -1], [0, 1]]]], np.int8)
+    scale, gate = 0.55, 0.6
+    g = orc.backward(q, k, v, w, do, mask, valid_len=vl, scale=scale, linear="global", gate=gate)
+
+    def loss(q_, k_, v_, w_):
+        out = orc.forward(q_, k_, v_, w_, 0, 0, valid_len=vl, scale=scale, mask=mask,
+                          linear="global", gate=gate)
+        return float((out["o"] * do).sum())
+
+    eps = 1e-6
+    rng = np.random.default_rng(1)
+    for name, pos in (("dq", 0), ("dk", 1), ("dv", 2)):
+        for _ in range(25):
+            idx = (0, 0, int(rng.integers(0, vl)), int(rng.integers(0, d)))
+            args = [q, k, v]
+            plus, minus = args[pos].copy(), args[pos].copy()
+            plus[idx] += eps
+            minus[idx] -= eps
+            ap, am = list(args), list(args)
+            ap[pos], am[pos] = plus, minus
+            fd = (loss(*ap, w) - loss(*am, w)) / (2 * eps)
+            assert abs(fd - g[name][idx]) < 1e-6 * max(1.0, abs(fd))
+    for _ in range(8):
+        a_, b_ = (int(x) for x in rng.integers(0, d, 2))
+        wp, wm = w.copy(), w.copy()
+        wp[a_, b_] += eps
+        wm[a_, b_] -= eps
+        fd = (loss(q, k, v, wp) - loss(q, k, v, wm)) / (2 * eps)
+        assert abs(fd - g["dw"][a_, b_]) < 1e-6 * max(1.0, abs(fd))
