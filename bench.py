@@ -210,6 +210,54 @@ def dense_ratio(wl, q, k, v, w, do, dev, with_bwd, sla_ms):
             "note": "frac_critical = 1, frac_negligible = 0 through the same entry points"}
 
 
+def mask_reuse_rate(wl, q, k, v, w, dev, mask):
+    """Forward with the mask of the timed run passed back in (given-mask mode:
+    no pooling, scores or classification) against the computed-mask forward."""
+    import torch
+
+    from sparse_linear_attention_mean_amd import _binding as B
+    from sparse_linear_attention_mean_amd.attention import SlaProblem
+
+    out = {}
+    for name, mode in (("fwd_ms_computed_mask", B.SLA_MASK_COMPUTE),
+                       ("fwd_ms_given_mask", B.SLA_MASK_GIVEN)):
+        prob = SlaProblem.create(wl.batch, wl.heads, wl.seq_len, wl.head_dim, wl.frac_critical,
+                                 wl.frac_negligible, valid_len=wl.valid_len, mask_mode=mode,
+                                 device=dev)
+        o = torch.empty(prob.shape(), dtype=torch.bfloat16, device=dev)
+        m = mask.clone() if mode == B.SLA_MASK_GIVEN else prob.new_mask()
+        out[name] = round(_timed(lambda: prob.forward(q, k, v, w, o=o, mask=m), 2, 5), 4)
+    return out
+
+
+def global_linear_rate(wl, q, k, v, w, do, dev, with_bwd, gate=0.5):
+    """The SALAD-style variant: linear branch over every key block (one state
+    sum per head instead of the per-row marginal aggregation), gated output."""
+    import torch
+
+    from sparse_linear_attention_mean_amd import _binding as B
+    from sparse_linear_attention_mean_amd.attention import SlaProblem
+
+    prob = SlaProblem.create(wl.batch, wl.heads, wl.seq_len, wl.head_dim, wl.frac_critical,
+                             wl.frac_negligible, valid_len=wl.valid_len, device=dev,
+                             linear_mode=B.SLA_LINEAR_GLOBAL, linear_gate=gate)
+    o = torch.empty(prob.shape(), dtype=torch.bfloat16, device=dev)
+    mask = prob.new_mask()
+    grads = None
+    if with_bwd:
+        shp = prob.shape()
+        grads = tuple(torch.empty(shp, dtype=torch.float32, device=dev) for _ in range(3)) + (
+            torch.empty((wl.head_dim, wl.head_dim), dtype=torch.float32, device=dev),)
+
+    def step():
+        prob.forward(q, k, v, w, o=o, mask=mask)
+        if with_bwd:
+            prob.backward(q, k, v, w, o, do, mask, grads=grads)
+
+    return {"ms_per_step": round(_timed(step, 2, 5), 4), "gate": gate,
+            "note": "linear_mode = SLA_LINEAR_GLOBAL, same fractions"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -332,6 +380,8 @@ def main():
     if not args.no_side_runs and not args.dense:
         rec["linear_branch"] = linear_branch_rate(wl, inp, q, k, v, w, dev)
         rec["vs_dense"] = dense_ratio(wl, q, k, v, w, do, dev, with_bwd, ms)
+        rec["mask_reuse"] = mask_reuse_rate(wl, q, k, v, w, dev, mask)
+        rec["global_linear"] = global_linear_rate(wl, q, k, v, w, do, dev, with_bwd)
     if args.traffic_probe:
         src = torch.empty(128 << 20, dtype=torch.bfloat16, device=dev).fill_(1.0)
         dst = torch.empty_like(src)

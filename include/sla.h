@@ -32,6 +32,14 @@
  * T + 1e-6) (computed in double from the float fractions).  The backward holds
  * the mask fixed (no gradient through the classifier).
  *
+ * Variant (linear_mode = SLA_LINEAR_GLOBAL), after "SALAD: Achieve
+ * High-Sparsity Attention via Efficient Linear Attention Tuning for Video
+ * Diffusion Transformer" (method: parallel architecture; static-dynamic
+ * scaling): the linear branch runs beside the sparse one over every key block,
+ * H_i = sum_j h_j and Z_i = sum_j z_j for all i, and its projected output is
+ * scaled by a gate g in [0, 1]: O[r] = O_s[r] + g Y[r] W^T.  The mask still
+ * selects the critical blocks of the sparse branch.
+ *
  * Conventions for every entry point below:
  *  - Tensors are contiguous, row-major.  Q, K, V, O, dO are bf16 [B, H, N, d]
  *    ("BHND"); W is bf16 [d, d]; dQ, dK, dV, dW are fp32.  Device pointers must
@@ -75,13 +83,19 @@ enum {
   SLA_MASK_GIVEN = 1    /* forward reads a caller-supplied ``mask`` (fixed mask) */
 };
 
+/* linear_mode */
+enum {
+  SLA_LINEAR_MARGINAL = 0, /* the method: linear branch over the marginal blocks of each row */
+  SLA_LINEAR_GLOBAL = 1    /* variant: linear branch over every key block, output gated */
+};
+
 /* Number of timed stages in stage_events (see sla_config). */
 #define SLA_NUM_STAGES 8
 enum {
   SLA_STAGE_KV_STATE = 0,   /* forward: per-key-block states and pooled K   */
   SLA_STAGE_POOL_Q = 1,     /* forward: pooled Q                            */
   SLA_STAGE_CLASSIFY = 2,   /* forward: compressed scores + classification  */
-  SLA_STAGE_AGGREGATE = 3,  /* forward: marginal sums H_i, Z_i              */
+  SLA_STAGE_AGGREGATE = 3,  /* forward: marginal sums H_i, Z_i (or totals)  */
   SLA_STAGE_ATTENTION = 4,  /* forward: fused sparse + linear + projection  */
   SLA_STAGE_BWD_PRE = 5,    /* backward: mask lists, D, dY, linear dQ, dH   */
   SLA_STAGE_BWD_KV = 6,     /* backward: transposed sums, dK and dV         */
@@ -104,6 +118,8 @@ typedef struct sla_config {
      library records event [2 s] before and [2 s + 1] after stage s on
      ``stream`` (stages a call does not run are left unrecorded). */
   void* stage_events;
+  int32_t linear_mode;     /* SLA_LINEAR_MARGINAL (0) or SLA_LINEAR_GLOBAL */
+  float linear_gate;       /* SLA_LINEAR_GLOBAL only: g in [0, 1]; ignored otherwise */
 } sla_config;
 
 /* k_c, k_n, k_m (= T - k_c - k_n) for the configuration.  Host only. */
@@ -119,7 +135,9 @@ size_t sla_workspace_size(const sla_config* cfg);
      den  fp32 [B,H,N]     linear denominator phi(q) . Z_i
      y    bf16 [B,H,N,d]   normalised linear output Y (before W)
      hst  bf16 [B,H,T,d,d] H_i stored transposed: element (c, a) at c*d + a
-     zst  fp32 [B,H,T,2,d] Z_i as two fp32 parts whose sum is Z_i           */
+     zst  fp32 [B,H,T,2,d] Z_i as two fp32 parts whose sum is Z_i
+   (SLA_LINEAR_GLOBAL: H and Z are the same for every i and only i = 0 is
+   written).                                                                 */
 size_t sla_saved_size(const sla_config* cfg);
 sla_status sla_saved_offsets(const sla_config* cfg, size_t* lse, size_t* den, size_t* y,
                              size_t* hst, size_t* zst);

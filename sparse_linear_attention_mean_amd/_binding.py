@@ -22,6 +22,8 @@ SLA_ERR_WORKSPACE = 3
 SLA_ERR_DEVICE = 4
 SLA_MASK_COMPUTE = 0
 SLA_MASK_GIVEN = 1
+SLA_LINEAR_MARGINAL = 0
+SLA_LINEAR_GLOBAL = 1
 SLA_NUM_STAGES = 8
 STAGES = ("kv_state", "pool_q", "classify", "aggregate", "attention", "bwd_pre", "bwd_kv", "bwd_q")
 
@@ -45,6 +47,8 @@ class SlaConfig(ctypes.Structure):
         ("softmax_scale", ctypes.c_float),
         ("mask_mode", ctypes.c_int32),
         ("stage_events", ctypes.c_void_p),
+        ("linear_mode", ctypes.c_int32),
+        ("linear_gate", ctypes.c_float),
     ]
 
 
@@ -85,9 +89,11 @@ lib = _load()
 
 
 def make_config(batch, heads, seq_len, head_dim, frac_critical, frac_negligible, valid_len=0,
-                softmax_scale=0.0, mask_mode=SLA_MASK_COMPUTE, stage_events=None) -> SlaConfig:
+                softmax_scale=0.0, mask_mode=SLA_MASK_COMPUTE, stage_events=None,
+                linear_mode=SLA_LINEAR_MARGINAL, linear_gate=1.0) -> SlaConfig:
     return SlaConfig(batch, heads, seq_len, head_dim, valid_len, 64, frac_critical,
-                     frac_negligible, softmax_scale, mask_mode, stage_events)
+                     frac_negligible, softmax_scale, mask_mode, stage_events, linear_mode,
+                     linear_gate)
 
 
 def _check(status: int) -> None:

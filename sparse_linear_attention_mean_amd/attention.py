@@ -30,9 +30,11 @@ class SlaProblem:
 
     @classmethod
     def create(cls, batch, heads, seq_len, head_dim, frac_critical, frac_negligible,
-               valid_len=0, softmax_scale=0.0, mask_mode=B.SLA_MASK_COMPUTE, device="cuda"):
+               valid_len=0, softmax_scale=0.0, mask_mode=B.SLA_MASK_COMPUTE, device="cuda",
+               linear_mode=B.SLA_LINEAR_MARGINAL, linear_gate=1.0):
         cfg = B.make_config(batch, heads, seq_len, head_dim, frac_critical, frac_negligible,
-                            valid_len, softmax_scale, mask_mode)
+                            valid_len, softmax_scale, mask_mode, linear_mode=linear_mode,
+                            linear_gate=linear_gate)
         ws = B.sla_workspace_size(cfg)
         sv = B.sla_saved_size(cfg)
         if ws == 0 or sv == 0:

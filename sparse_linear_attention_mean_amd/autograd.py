@@ -5,7 +5,9 @@ Attention" (English abstract): the method is meant to be fine-tuned in place of
 full attention, so it needs a forward and a backward that autograd can chain.
 The projection weight of the linear branch (O = O_s + Y W^T) is the only
 parameter; the block mask is piecewise constant in Q and K and gets no
-gradient (the backward runs with the mask held fixed).
+gradient (the backward runs with the mask held fixed).  ``global_linear=True``
+selects the SALAD-style variant: a linear branch over every key block and
+O = O_s + gate Y W^T.
 
 Mask reuse across calls (denoising steps): with ``reuse_mask=True`` the module
 keeps the mask of its first call and passes it back to the library in the
@@ -116,7 +118,8 @@ class SparseLinearAttention(torch.nn.Module):
 
     def __init__(self, head_dim: int, frac_critical: float, frac_negligible: float,
                  valid_len: int = 0, softmax_scale: float = 0.0, reuse_mask: bool = False,
-                 weight: torch.Tensor | None = None, device=None):
+                 weight: torch.Tensor | None = None, device=None, global_linear: bool = False,
+                 gate: float = 1.0):
         super().__init__()
         if head_dim not in (64, 128):
             raise ValueError("head_dim must be 64 or 128")
@@ -126,6 +129,8 @@ class SparseLinearAttention(torch.nn.Module):
         self.valid_len = int(valid_len)
         self.softmax_scale = float(softmax_scale)
         self.reuse_mask = bool(reuse_mask)
+        self.global_linear = bool(global_linear)   # SALAD-style linear branch over every block
+        self.gate = float(gate)                     # its output scale (global_linear only)
         if weight is None:
             weight = torch.randn(head_dim, head_dim, device=device) / math.sqrt(head_dim)
         self.weight = torch.nn.Parameter(weight.clone())
@@ -147,7 +152,9 @@ class SparseLinearAttention(torch.nn.Module):
         key = (b, h, n, d, str(q.device))
         given = self.reuse_mask and self._mask is not None and self._mask_key == key
         cfg = B.make_config(b, h, n, d, self.frac_critical, self.frac_negligible, self.valid_len,
-                            self.softmax_scale, B.SLA_MASK_GIVEN if given else B.SLA_MASK_COMPUTE)
+                            self.softmax_scale, B.SLA_MASK_GIVEN if given else B.SLA_MASK_COMPUTE,
+                            linear_mode=B.SLA_LINEAR_GLOBAL if self.global_linear
+                            else B.SLA_LINEAR_MARGINAL, linear_gate=self.gate)
         B.sla_block_counts(cfg)   # validates the configuration, raises SlaError
         w = self.weight.to(torch.bfloat16)
         o, mask = SlaFunction.apply(q, k, v, w, cfg, self._mask if given else None)

@@ -161,6 +161,46 @@ __global__ __launch_bounds__(256, 2) void aggregate_kernel(const uint32_t* __res
   }
 }
 
+// ---------------------------------------------------------------------------
+// state_total: the global linear branch (every key block in every row) needs
+// one sum per head instead of one per query block, H = sum_j h_j and
+// Z = sum_j z_j: a column sum of the state matrix, fp32 in block order, one
+// thread per state entry (8-byte loads of the 4-block planes, consecutive
+// threads on consecutive entries).  Written like the aggregation output, to
+// query-block slot 0 of the head.  Blocks j >= T hold zero states.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void state_total_kernel(const uint16_t* __restrict__ states,
+                                                          uint16_t* __restrict__ hout,
+                                                          float* __restrict__ zout, int T, int Tp,
+                                                          int NB, int DD) {
+  const long long bh = blockIdx.y;
+  const int n = blockIdx.x * 256 + threadIdx.x;
+  if (n >= NB) return;
+  const uint16_t* src = states + static_cast<size_t>(bh) * Tp * NB + static_cast<size_t>(n) * 4;
+  float acc = 0.f;
+  for (int p = 0; p < Tp / 4; p += 8) {   // Tp / 4 is a multiple of 8
+    u32x2 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = ld8(src + static_cast<size_t>(p + u) * NB * 4);
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc += bf16_to_f32(u4_half(v[u], e));
+  }
+  if (n < DD)
+    hout[static_cast<size_t>(bh) * T * DD + n] = f32_to_bf16(acc);
+  else
+    zout[static_cast<size_t>(bh) * T * (NB - DD) + (n - DD)] = acc;
+}
+
+hipError_t launch_state_total(const Dims& d, const uint16_t* states, uint16_t* hout, float* zout,
+                              hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>((d.NB + 255) / 256), static_cast<unsigned>(d.BH()));
+  hipLaunchKernelGGL(state_total_kernel, grid, dim3(256), 0, s, states, hout, zout, d.T, d.Tp, d.NB,
+                     d.D * d.D);
+  return hipGetLastError();
+}
+
 hipError_t launch_aggregate(const Dims& d, const uint32_t* bits, const uint16_t* states,
                             uint16_t* hout, float* zout, hipStream_t s) {
   const int ntiles = d.NB / kAggNTile;

@@ -48,6 +48,8 @@ struct AttnArgs {
   uint16_t* y;
   int N, L, T;
   float scale_log2;
+  int hglobal;   // H, Z shared by every query block (slot 0 of the head)
+  float gate;    // O = O_s + gate * Y W^T
 };
 
 template <int D>
@@ -141,9 +143,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs args) {
   float* zsw = reinterpret_cast<float*>(hsw + D * D);
   auto copy_hz = [&]() {
     if constexpr (LINEAR) {
-      copy_swz<D>(args.hst + (static_cast<size_t>(bh) * T + i) * D * D, hsw, D, wave, 4, lane);
-      if (wave == 3 && lane < D / 2)
-        gl_to_lds16(args.zst + (static_cast<size_t>(bh) * T + i) * 2 * D + 4 * lane, zsw);
+      const size_t hslot = static_cast<size_t>(bh) * T + (args.hglobal ? 0 : i);
+      copy_swz<D>(args.hst + hslot * D * D, hsw, D, wave, 4, lane);
+      if (wave == 3 && lane < D / 2) gl_to_lds16(args.zst + hslot * 2 * D + 4 * lane, zsw);
     }
   };
   if (cnt == 0) copy_hz();
@@ -349,7 +351,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs args) {
         const int o0 = obase + 8 * e4 + 4 * hl;
         float r[4];
 #pragma unroll
-        for (int x = 0; x < 4; ++x) r[x] = out[4 * e4 + x] + fin[ot][4 * e4 + x];
+        for (int x = 0; x < 4; ++x) r[x] = out[4 * e4 + x] * args.gate + fin[ot][4 * e4 + x];
         st8(orow + o0, valid_row ? u32x2{pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3])}
                                  : u32x2{0u, 0u});
       }
@@ -380,7 +382,7 @@ hipError_t launch_attn_fwd(const Dims& d, const uint16_t* q, const uint16_t* k,
                            const uint16_t* hst, const float* zst, uint16_t* o, float* lse,
                            float* den, uint16_t* y, hipStream_t s) {
   AttnArgs a{q, k, v, w, lut, lut_cnt, hst, zst, o, lse, den, y, d.N, d.L, d.T,
-             d.scale * kLog2e};
+             d.scale * kLog2e, d.global ? 1 : 0, d.gate};
   const unsigned grid = static_cast<unsigned>(d.BH() * d.T);
   if (d.D == 128) return launch_attn_t<128>(a, grid, dense, linear, s);
   return launch_attn_t<64>(a, grid, dense, linear, s);

@@ -53,7 +53,7 @@ __global__ __launch_bounds__(256, 2) void bwd_prep_kernel(
     const float* __restrict__ den, const uint16_t* __restrict__ y,
     const uint16_t* __restrict__ hst, const float* __restrict__ zst, float* __restrict__ dsum,
     float* __restrict__ ddel, uint16_t* __restrict__ dn, float* __restrict__ dq, int N, int L,
-    int T, bool linear) {
+    int T, bool linear, bool hglobal, float gate) {
   constexpr int HP = D + 8;    // dN row pitch
   constexpr int NCC = D / 16;
   constexpr int NT = D / 64;   // 32-wide tiles per wave in each half
@@ -76,9 +76,9 @@ __global__ __launch_bounds__(256, 2) void bwd_prep_kernel(
 
   // asynchronous copies of H_i^T and Z_i
   if (linear) {
-    copy_swz<D>(hst + (static_cast<size_t>(bh) * T + i) * D * D, hs, D, wave, 4, lane);
-    if (wave == 0 && lane < D / 2)
-      gl_to_lds16(zst + (static_cast<size_t>(bh) * T + i) * 2 * D + 4 * lane, zs);
+    const size_t hslot = static_cast<size_t>(bh) * T + (hglobal ? 0 : i);
+    copy_swz<D>(hst + hslot * D * D, hs, D, wave, 4, lane);
+    if (wave == 0 && lane < D / 2) gl_to_lds16(zst + hslot * 2 * D + 4 * lane, zs);
   }
 
   // dO fragments for dY, and the row pieces of O, Y, dO and Q that match the
@@ -112,6 +112,8 @@ __global__ __launch_bounds__(256, 2) void bwd_prep_kernel(
     const uint16_t* wr = wT + static_cast<size_t>((D / 2) * ch + 32 * ct + n32) * D + 8 * hl;
 #pragma unroll
     for (int cc = 0; cc < NCC; ++cc) dyt[ct] = mfma32(as_bf16x8(ld16(wr + 16 * cc)), dof[cc], dyt[ct]);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) dyt[ct][e] *= gate;   // dY of the ungated Y (gate 1: exact)
   }
   // partial row dots over this lane's c values
   float p_oo = 0.f, p_yy = 0.f;
@@ -408,7 +410,7 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dO,
     const float* __restrict__ lse, const float* __restrict__ dsum,
     const int32_t* __restrict__ col, const int32_t* __restrict__ col_cnt,
-    const uint16_t* __restrict__ dh, const float* __restrict__ dz, bool linear,
+    const uint16_t* __restrict__ dh, const float* __restrict__ dz, bool linear, bool hglobal,
     float* __restrict__ dk, float* __restrict__ dv, int N, int L, int T, float scale) {
   using C = BkvCfg<D>;
   constexpr int RP = C::RP;
@@ -439,8 +441,9 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(
   copy_swz<D>(k + head + static_cast<size_t>(j) * kBlock * D, ksw, 64, wave, 8, lane);
   copy_swz<D>(v + head + static_cast<size_t>(j) * kBlock * D, vsw, 64, wave, 8, lane);
   if (linear) {
-    copy_swz<D>(dh + (static_cast<size_t>(bh) * T + j) * D * D, dhs, D, wave, 8, lane);
-    if (wave == 7 && lane < D / 2) gl_to_lds16(dz + (static_cast<size_t>(bh) * T + j) * 2 * D + 4 * lane, dzs);
+    const size_t hslot = static_cast<size_t>(bh) * T + (hglobal ? 0 : j);
+    copy_swz<D>(dh + hslot * D * D, dhs, D, wave, 8, lane);
+    if (wave == 7 && lane < D / 2) gl_to_lds16(dz + hslot * 2 * D + 4 * lane, dzs);
   }
   const int cnt = col_cnt[bh * T + j];
   const int32_t* crow = col + (bh * T + j) * static_cast<long long>(T);
@@ -710,9 +713,10 @@ __global__ __launch_bounds__(256) void dw_part_kernel(const uint16_t* __restrict
 
 // Fixed-order reduction of the partials: workgroup of 256 threads per 64
 // entries; thread group g (of 4) sums partials g, g + 4, ... in order, and the
-// four group sums are added in order.
+// four group sums are added in order; times the linear-output gate (1 for SLA).
 __global__ __launch_bounds__(256) void dw_reduce_kernel(const float* __restrict__ part,
-                                                        float* __restrict__ dw, int DD, int parts) {
+                                                        float* __restrict__ dw, int DD, int parts,
+                                                        float gate) {
   __shared__ float red[4][64];
   const int tid = threadIdx.x, g = tid >> 6;
   const int e = blockIdx.x * 64 + (tid & 63);
@@ -730,7 +734,7 @@ __global__ __launch_bounds__(256) void dw_reduce_kernel(const float* __restrict_
   }
   red[g][tid & 63] = s;
   __syncthreads();
-  if (g == 0 && e < DD) dw[e] = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
+  if (g == 0 && e < DD) dw[e] = gate * (((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid]);
 }
 
 // ---------------------------------------------------------------------------
@@ -748,10 +752,10 @@ hipError_t launch_bwd_prep(const Dims& d, const uint16_t* q, const uint16_t* o,
   const dim3 grid(static_cast<unsigned>(d.BH() * d.T));
   if (d.D == 128)
     hipLaunchKernelGGL(bwd_prep_kernel<128>, grid, dim3(256), 0, s, q, o, dO, wT, den, y, hst, zst,
-                       dsum, ddel, dn, dq, d.N, d.L, d.T, linear);
+                       dsum, ddel, dn, dq, d.N, d.L, d.T, linear, d.global, d.gate);
   else
     hipLaunchKernelGGL(bwd_prep_kernel<64>, grid, dim3(256), 0, s, q, o, dO, wT, den, y, hst, zst,
-                       dsum, ddel, dn, dq, d.N, d.L, d.T, linear);
+                       dsum, ddel, dn, dq, d.N, d.L, d.T, linear, d.global, d.gate);
   return hipGetLastError();
 }
 
@@ -775,10 +779,10 @@ hipError_t launch_bwd_kv(const Dims& d, const uint16_t* q, const uint16_t* k, co
   const dim3 grid(static_cast<unsigned>(d.BH() * d.T));
   if (d.D == 128)
     hipLaunchKernelGGL(bwd_kv_kernel<128>, grid, dim3(512), 0, s, q, k, v, dO, lse, dsum, col,
-                       col_cnt, dh, dz, linear, dk, dv, d.N, d.L, d.T, d.scale);
+                       col_cnt, dh, dz, linear, d.global, dk, dv, d.N, d.L, d.T, d.scale);
   else
     hipLaunchKernelGGL(bwd_kv_kernel<64>, grid, dim3(512), 0, s, q, k, v, dO, lse, dsum, col,
-                       col_cnt, dh, dz, linear, dk, dv, d.N, d.L, d.T, d.scale);
+                       col_cnt, dh, dz, linear, d.global, dk, dv, d.N, d.L, d.T, d.scale);
   return hipGetLastError();
 }
 
@@ -795,7 +799,8 @@ hipError_t launch_dw(const Dims& d, const uint16_t* y, const uint16_t* dO, float
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int dd = d.D * d.D;
-  hipLaunchKernelGGL(dw_reduce_kernel, dim3((dd + 63) / 64), dim3(256), 0, s, part, dw, dd, parts);
+  hipLaunchKernelGGL(dw_reduce_kernel, dim3((dd + 63) / 64), dim3(256), 0, s, part, dw, dd, parts,
+                     d.gate);
   return hipGetLastError();
 }
 

@@ -63,6 +63,11 @@ sla_status make_dims(const sla_config* cfg, Dims* d) {
     return fail(SLA_ERR_INVALID_ARGUMENT, "unknown mask_mode %d", cfg->mask_mode);
   if (!isfinite(cfg->softmax_scale))
     return fail(SLA_ERR_INVALID_ARGUMENT, "softmax_scale must be finite");
+  if (cfg->linear_mode != SLA_LINEAR_MARGINAL && cfg->linear_mode != SLA_LINEAR_GLOBAL)
+    return fail(SLA_ERR_INVALID_ARGUMENT, "unknown linear_mode %d", cfg->linear_mode);
+  const bool global = cfg->linear_mode == SLA_LINEAR_GLOBAL;
+  if (global && !(cfg->linear_gate >= 0.f && cfg->linear_gate <= 1.f))
+    return fail(SLA_ERR_INVALID_ARGUMENT, "linear_gate must lie in [0, 1] (got %g)", cfg->linear_gate);
   const long long elems = static_cast<long long>(cfg->batch) * cfg->heads * N;
   if (elems > (1LL << 40)) return fail(SLA_ERR_UNSUPPORTED, "problem too large");
   int kc = 0, kn = 0;
@@ -81,6 +86,8 @@ sla_status make_dims(const sla_config* cfg, Dims* d) {
   d->km = T - kc - kn;
   d->scale = cfg->softmax_scale > 0.f ? cfg->softmax_scale : 1.0f / sqrtf(static_cast<float>(d->D));
   d->mask_mode = cfg->mask_mode;
+  d->global = global;
+  d->gate = global ? cfg->linear_gate : 1.0f;
   return SLA_OK;
 }
 
@@ -243,8 +250,9 @@ sla_status sla_forward(const sla_config* cfg, const void* q, const void* k, cons
 
   const bool given = d.mask_mode == SLA_MASK_GIVEN;
   // all blocks critical: plain dense attention, no classification, no linear branch
-  const bool dense = !given && d.kc == d.T;
-  const bool linear = given || d.km > 0;
+  const bool dense = !given && d.kc == d.T && !d.global;
+  const bool linear = d.global || given || d.km > 0;
+  uint32_t* bits = d.global ? nullptr : rbits;   // the global branch needs no marginal bits
 
   if (dense) {
     SLA_CHECK(launched(launch_fill_mask(d, mask, 1, s), "fill_mask"));
@@ -265,18 +273,21 @@ sla_status sla_forward(const sla_config* cfg, const void* q, const void* k, cons
                                        reinterpret_cast<float*>(ws + wl.scores), s),
                          "scores"));
       SLA_CHECK(launched(launch_classify(d, reinterpret_cast<float*>(ws + wl.scores), mask, lut,
-                                         lut_cnt, rbits, s),
+                                         lut_cnt, bits, s),
                          "classify"));
       SLA_CHECK(stg.end(SLA_STAGE_CLASSIFY));
     } else {
       SLA_CHECK(stg.begin(SLA_STAGE_CLASSIFY));
-      SLA_CHECK(launched(launch_mask_lists(d, mask, lut, lut_cnt, rbits, nullptr, nullptr, nullptr, s),
+      SLA_CHECK(launched(launch_mask_lists(d, mask, lut, lut_cnt, bits, nullptr, nullptr, nullptr, s),
                          "mask_lists"));
       SLA_CHECK(stg.end(SLA_STAGE_CLASSIFY));
     }
     if (linear) {
       SLA_CHECK(stg.begin(SLA_STAGE_AGGREGATE));
-      SLA_CHECK(launched(launch_aggregate(d, rbits, states, hst, zst, s), "aggregate"));
+      if (d.global)
+        SLA_CHECK(launched(launch_state_total(d, states, hst, zst, s), "state_total"));
+      else
+        SLA_CHECK(launched(launch_aggregate(d, rbits, states, hst, zst, s), "aggregate"));
       SLA_CHECK(stg.end(SLA_STAGE_AGGREGATE));
     }
   }
@@ -345,7 +356,7 @@ sla_status sla_backward(const sla_config* cfg, const void* q, const void* k, con
   const auto* zst = reinterpret_cast<const float*>(sv + sl.zst);
   // the forward ran its linear branch exactly when this holds (same config)
   const bool given = d.mask_mode == SLA_MASK_GIVEN;
-  const bool linear = given || (d.km > 0 && d.kc < d.T);
+  const bool linear = d.global || given || (d.km > 0 && d.kc < d.T);
 
   SLA_CHECK(stg.begin(SLA_STAGE_BWD_PRE));
   SLA_CHECK(launched(launch_mask_lists(d, mask, lut, lut_cnt, rbits, col, col_cnt, cbits, s),
@@ -356,7 +367,10 @@ sla_status sla_backward(const sla_config* cfg, const void* q, const void* k, con
                      "bwd_prep"));
   if (linear) {
     SLA_CHECK(launched(launch_dstate(d, q16, dn, ddel, states, s), "dstate"));
-    SLA_CHECK(launched(launch_aggregate(d, cbits, states, dh, dz, s), "aggregate_t"));
+    if (d.global)
+      SLA_CHECK(launched(launch_state_total(d, states, dh, dz, s), "state_total"));
+    else
+      SLA_CHECK(launched(launch_aggregate(d, cbits, states, dh, dz, s), "aggregate_t"));
   }
   SLA_CHECK(stg.end(SLA_STAGE_BWD_PRE));
   SLA_CHECK(stg.begin(SLA_STAGE_BWD_KV));

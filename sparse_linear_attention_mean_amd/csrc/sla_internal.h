@@ -18,6 +18,8 @@ struct Dims {
   int kc, kn, km;      // per-row counts (compute mode)
   float scale;         // softmax scale
   int mask_mode;
+  bool global;         // linear branch over every key block (H_i, Z_i the same for all i)
+  float gate;          // scale of the projected linear output (1 unless global)
   long long BH() const { return static_cast<long long>(B) * H; }
 };
 
@@ -65,6 +67,10 @@ hipError_t launch_mask_lists(const Dims& d, const int8_t* mask, int32_t* lut, in
 hipError_t launch_fill_mask(const Dims& d, int8_t* mask, int8_t value, hipStream_t s);
 hipError_t launch_aggregate(const Dims& d, const uint32_t* bits, const uint16_t* states,
                             uint16_t* hout, float* zout, hipStream_t s);
+// column sums of the states over every key block, written to slot i = 0 of
+// each head of hout [BH, T, D*D] / zout [BH, T, 2D]
+hipError_t launch_state_total(const Dims& d, const uint16_t* states, uint16_t* hout, float* zout,
+                              hipStream_t s);
 hipError_t launch_attn_fwd(const Dims& d, const uint16_t* q, const uint16_t* k,
                            const uint16_t* v, const uint16_t* w, const int32_t* lut,
                            const int32_t* lut_cnt, bool dense, bool linear,

@@ -101,3 +101,18 @@ def test_status_strings_and_sizes(B):
     assert all(v % 256 == 0 for v in off.values())
     assert B.sla_saved_size(cfg) >= off["zst"] + 2 * 12 * 512 * 2 * 128 * 4
     assert B.sla_workspace_size(cfg) > 0
+
+
+def test_linear_mode_and_gate_are_validated_on_the_host():
+    from sparse_linear_attention_mean_amd import _binding as B
+
+    ok = B.make_config(1, 2, 1024, 64, 0.1, 0.2, linear_mode=B.SLA_LINEAR_GLOBAL, linear_gate=0.5)
+    assert B.sla_block_counts(ok) == (2, 3, 11)
+    for mode, gate in ((2, 0.5), (B.SLA_LINEAR_GLOBAL, 1.5), (B.SLA_LINEAR_GLOBAL, -0.1),
+                       (B.SLA_LINEAR_GLOBAL, float("nan"))):
+        bad = B.make_config(1, 2, 1024, 64, 0.1, 0.2, linear_mode=mode, linear_gate=gate)
+        with pytest.raises(B.SlaError):
+            B.sla_block_counts(bad)
+    # the gate is ignored by the method's own (marginal) linear branch
+    plain = B.make_config(1, 2, 1024, 64, 0.1, 0.2, linear_gate=7.0)
+    assert B.sla_block_counts(plain) == (2, 3, 11)
