@@ -12,8 +12,9 @@ O = O_s + gate Y W^T.
 Mask reuse across calls (denoising steps): with ``reuse_mask=True`` the module
 keeps the mask of its first call and passes it back to the library in the
 ``SLA_MASK_GIVEN`` mode, which skips block pooling, the score map and the
-classifier.  The pages on mixture-of-sparse-attention for video models describe
-reusing selection metadata across steps; ``reset_mask()`` forgets the cache.
+classifier.  The page on Meta-Cached Sparse Attention (MC-Sparse; its key
+facts and "how to apply" sections) describes caching sparse-attention metadata
+between denoising steps; ``reset_mask()`` forgets the cache.
 
 Every computation runs in ``libsla.so``; this file only allocates buffers,
 checks arguments and wires the two entry points into ``torch.autograd``.
