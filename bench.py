@@ -74,6 +74,7 @@ class HipEvents:
     def elapsed_ms(self, a, b):
         out = ctypes.c_float()
         if self.hip.hipEventElapsedTime(ctypes.byref(out), a, b) != 0:
+            self.hip.hipGetLastError()   # a stage the call did not run: clear the sticky error
             return None
         return out.value
 
@@ -313,6 +314,8 @@ def main():
 
     stage_ms = {}
     for si, name in enumerate(B.STAGES):
+        if not with_bwd and si >= 5:   # backward stages are not recorded in forward-only runs
+            continue
         vals = [hip.elapsed_ms(ev_sets[s][2 * si], ev_sets[s][2 * si + 1]) for s in range(args.steps)]
         vals = [x for x in vals if x is not None]
         if vals:

@@ -17,11 +17,12 @@
 // then the S^T result tile, converted to bf16, is directly the B operand of
 // the P V product (k index permuted identically in the V^T operand), each
 // lane owns one query row, and row statistics need a single xor-32 exchange.
-// K_j and V_j are staged to LDS row-major (a plain 16-byte copy); the V^T
+// K_j and V_j arrive in LDS through asynchronous buffer->LDS copies into
+// XOR-swizzled row-major tiles (no staging registers, no LDS stores); the V^T
 // operand of the P V product is read from the V tile with LDS transpose reads.
-// Both tiles are double-buffered with the next block's global loads in flight
-// during the current block's MFMAs; the row pitch keeps the 16-byte operand
-// reads and the transpose reads free of LDS bank conflicts.
+// Both tiles are double-buffered: the next block's copies are in flight during
+// the current block's MFMAs; the swizzle keeps the 16-byte operand reads and
+// the transpose reads spread over the LDS banks.
 // The two key halves are merged at the end like split-K partial softmaxes,
 // each wave finishing half of the output tiles.  H_i and Z_i for the linear
 // branch are copied asynchronously into the staging buffer the last critical
@@ -54,11 +55,9 @@ struct AttnArgs {
 
 template <int D>
 struct AttnCfg {
-  static constexpr int KP = D == 128 ? 152 : 72;   // K and V row pitch in LDS (bf16)
-  static constexpr int VP = KP;
-  static constexpr int kBuf = 2 * 64 * KP;         // one K + V buffer (bf16 elements)
-  static constexpr int kLds = 2 * kBuf * 2;        // bytes, double buffered
-  static constexpr int KCH = D / 32;               // 16-byte K chunks per thread
+  static constexpr int kBuf = 2 * 64 * D;          // one K + V buffer (bf16 elements), swizzled tiles
+  static constexpr int kExtra = 4096;              // bytes: Z_i and the merge statistics
+  static constexpr int kLds = 2 * kBuf * 2 + kExtra;
   static constexpr int NCT = D / 32;               // 32-row tiles of O^T per wave
   static constexpr int NCC = D / 16;               // 16-wide k chunks over the head dim
 };
@@ -66,8 +65,8 @@ struct AttnCfg {
 template <int D, bool DENSE, bool LINEAR>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs args) {
   using C = AttnCfg<D>;
-  constexpr int KP = C::KP, VP = C::VP;
   __shared__ __attribute__((aligned(16))) uint16_t smem[C::kLds / 2];
+  float* extra = reinterpret_cast<float*>(smem + 2 * C::kBuf);
 
   const int T = args.T, N = args.N, L = args.L;
   const uint32_t wg = xcd_remap(blockIdx.x, gridDim.x);
@@ -94,37 +93,15 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs args) {
   const int cnt = DENSE ? T : args.lut_cnt[bh * T + i];
   const int32_t* lrow = DENSE ? nullptr : args.lut + (bh * T + i) * static_cast<long long>(T);
 
-  // staging: 8 D chunks of 16 bytes each for K and V (row t, 8 columns);
-  // chunk e = tid + 256 u.  Loads go through buffer resources of this head
-  // (block offset in an SGPR, lane offset in a VGPR).
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(args.k + head, static_cast<uint32_t>(N) * D * 2);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(args.v + head, static_cast<uint32_t>(N) * D * 2);
-  u32x4 rk[C::KCH], rv[C::KCH];
-  // chunk e = tid + 256 u: global byte offset 16 e; row e / (D / 8) = row0 + u (256 / (D / 8))
-  const uint32_t gbase = 16u * tid;
-  const int kst0 = (tid / (D / 8)) * KP + 8 * (tid % (D / 8));
-  constexpr int kRowsPerU = 256 / (D / 8);
-  auto load_block = [&](int jb) {
-    const uint32_t soff = static_cast<uint32_t>(jb) * kBlock * D * 2;
-#pragma unroll
-    for (int u = 0; u < C::KCH; ++u) {
-      rk[u] = buf_ld16(krs, gbase, soff + 4096u * u);
-      rv[u] = buf_ld16(vrs, gbase, soff + 4096u * u);
-    }
-    if ((jb + 1) * kBlock > L) {   // padded last block: zero V rows (their P is masked too)
-#pragma unroll
-      for (int u = 0; u < C::KCH; ++u)
-        if (jb * kBlock + (tid / (D / 8)) + u * kRowsPerU >= L) rv[u] = u32x4{0u, 0u, 0u, 0u};
-    }
-  };
-  auto store_block = [&](int bufidx) {
+  // K_j and V_j arrive through asynchronous buffer->LDS copies into swizzled
+  // tiles (no staging registers).  The resources end at valid_len, so the
+  // rows of the padded last block past it arrive as zeros.
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(args.k + head, static_cast<uint32_t>(L) * D * 2);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(args.v + head, static_cast<uint32_t>(L) * D * 2);
+  auto copy_block = [&](int jb, int bufidx) {
     uint16_t* ks_ = smem + bufidx * C::kBuf;
-    uint16_t* vt_ = ks_ + 64 * KP;
-#pragma unroll
-    for (int u = 0; u < C::KCH; ++u) {
-      st16(ks_ + kst0 + u * kRowsPerU * KP, rk[u]);
-      st16(vt_ + kst0 + u * kRowsPerU * KP, rv[u]);
-    }
+    copy_swz_buf<D, 4>(krs, jb * kBlock, ks_, wave, lane);
+    copy_swz_buf<D, 4>(vrs, jb * kBlock, ks_ + 64 * D, wave, lane);
   };
 
   f32x16 acc[C::NCT];
@@ -132,7 +109,6 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs args) {
   for (int ct = 0; ct < C::NCT; ++ct) acc[ct] = f32x16{};
   float m_run = -INFINITY;   // running max (log2 units) of this lane's query
   float l_run = 0.f;         // partial row sum over this lane's keys
-  const int kread = (32 * kh + n32) * KP + 8 * hl;          // S^T A operand (row of K)
 
   // One key block: S^T = K Q^T, online softmax (base 2, lazy rescale), O^T += V^T P^T.
   // MASKED is used only for the padded last key block.
@@ -140,7 +116,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs args) {
   // and Z_i through asynchronous copies, so the linear epilogue reads LDS.
   const int hbuf = cnt > 0 ? (((cnt - 1) & 1) ^ 1) : 1;
   uint16_t* hsw = smem + hbuf * C::kBuf;
-  float* zsw = reinterpret_cast<float*>(hsw + D * D);
+  float* zsw = extra;                       // 2 D floats
   auto copy_hz = [&]() {
     if constexpr (LINEAR) {
       const size_t hslot = static_cast<size_t>(bh) * T + (args.hglobal ? 0 : i);
@@ -156,21 +132,24 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs args) {
     const int buf = n & 1;
     const bool more = n + 1 < cnt;
     if (more)
-      load_block(DENSE ? n + 1 : lrow[n + 1]);
+      copy_block(DENSE ? n + 1 : lrow[n + 1], buf ^ 1);
     else
       copy_hz();   // buffer buf ^ 1 is no longer read
     const uint16_t* ks = smem + buf * C::kBuf;
-    const uint16_t* vt = ks + 64 * KP;
+    const uint16_t* vt = ks + 64 * D;
+    // S^T = K Q^T: K operand rows read four chunks ahead of the MFMA chain
+    constexpr int KA = C::NCC < 4 ? C::NCC : 4;
+    bf16x8 ka[KA];
+#pragma unroll
+    for (int cc = 0; cc < KA; ++cc)
+      ka[cc] = as_bf16x8(ld16(ks + swz_off<D>(32 * kh + n32, 16 * cc + 8 * hl)));
     f32x16 st = {};
 #pragma unroll
-    for (int cc = 0; cc < C::NCC; ++cc) st = mfma32(as_bf16x8(ld16(ks + kread + 16 * cc)), qf[cc], st);
-    // V^T operands of this block (transpose reads of the V tile, keys in the
-    // permuted order of the S^T tile), read ahead of the softmax arithmetic
-    bf16x8 va[C::NCT][2];
-#pragma unroll
-    for (int ct = 0; ct < C::NCT; ++ct)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) va[ct][h] = lds_op32_tr<true>(vt, VP, 32 * kh + 16 * h, 32 * ct, lane);
+    for (int cc = 0; cc < C::NCC; ++cc) {
+      const bf16x8 a = ka[cc % KA];
+      if (cc + KA < C::NCC) ka[cc % KA] = as_bf16x8(ld16(ks + swz_off<D>(32 * kh + n32, 16 * (cc + KA) + 8 * hl)));
+      st = mfma32(a, qf[cc], st);
+    }
     if constexpr (MASKED) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
@@ -201,18 +180,21 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs args) {
       l_run += p[e];
     }
     const bf16x8 pb[2] = {cvt_bf16x8(p), cvt_bf16x8(p + 8)};
-    // O^T += V^T P^T; k index of chunk h: keys 16 h + {4 hl .. 4 hl + 3, 8 + 4 hl .. 8 + 4 hl + 3}
+    // O^T += V^T P^T; the V^T operands come from transpose reads of the V tile
+    // (keys in the permuted order of the S^T tile: k index of chunk h is keys
+    // 16 h + {4 hl .. 4 hl + 3, 8 + 4 hl .. 8 + 4 hl + 3})
 #pragma unroll
     for (int ct = 0; ct < C::NCT; ++ct)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) acc[ct] = mfma32(va[ct][h], pb[h], acc[ct]);
-    if (more) store_block(buf ^ 1);
+      for (int h = 0; h < 2; ++h)
+        acc[ct] = mfma32(swz_op32_tr_perm<D>(vt, 32 * kh + 16 * h, 32 * ct, lane), pb[h], acc[ct]);
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's copies into buffer buf ^ 1 have landed
     __syncthreads();
   };
 
   if (cnt > 0) {
-    load_block(DENSE ? 0 : lrow[0]);
-    store_block(0);
+    copy_block(DENSE ? 0 : lrow[0], 0);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (int n = 0; n + 1 < cnt; ++n) step(n, std::false_type{});
     const int jl = DENSE ? cnt - 1 : lrow[cnt - 1];   // ascending lists: only the last can be padded
@@ -222,14 +204,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs args) {
       step(cnt - 1, std::false_type{});
   }
   l_run += __shfl_xor(l_run, 32);
-#undef SLA_LOAD_BLOCK
-#undef SLA_STORE_BLOCK
 
   // ---- merge the two key halves (split-K style): wave (kh, qh) finishes the
   // O_s^T tiles ct = NH kh .. NH kh + NH - 1 and hands the others to its partner.
   constexpr int NH = C::NCT / 2;
   float* ex = reinterpret_cast<float*>(smem + (hbuf ^ 1) * C::kBuf);   // [wave][NH][16][64]
-  float* exm = ex + 4 * NH * 16 * 64;                                    // [wave][64]
+  float* exm = extra + 2 * D;                                            // [wave][64]
   float* exl = exm + 4 * 64;                                             // [wave][64]
   __syncthreads();
   f32x16 fin[NH];

@@ -194,6 +194,32 @@ __device__ __forceinline__ bf16x8 swz_op32_tr(const uint16_t* m, int kb, int n0,
   const int r0 = kb + 8 * h + (c >> 2);
   return as_bf16x8(lds_tr4(m + swz_off<D>(r0, col)), lds_tr4(m + swz_off<D>(r0 + 4, col)));
 }
+// lds_op32_tr<true> (permuted k order) on a swizzled tile
+template <int D>
+__device__ __forceinline__ bf16x8 swz_op32_tr_perm(const uint16_t* m, int kb, int n0, int lane) {
+  const int g = lane >> 4, c = lane & 15, h = lane >> 5;
+  const int col = n0 + 16 * (g & 1) + 4 * (c & 3);
+  const int r0 = kb + 4 * h + (c >> 2);
+  return as_bf16x8(lds_tr4(m + swz_off<D>(r0, col)), lds_tr4(m + swz_off<D>(r0 + 8, col)));
+}
+// rows [row0, row0 + 64) of a row-major tile behind a buffer resource into a
+// swizzled LDS tile (asynchronous buffer->LDS copies; bytes past the
+// resource's size arrive as zero); the workgroup's waves share the copies
+template <int D, int NW>
+__device__ __forceinline__ void copy_swz_buf(__amdgpu_buffer_rsrc_t rs, int row0, uint16_t* dst,
+                                             int w, int lane) {
+  constexpr int kCopies = 64 * (D / 8) / 64;
+  static_assert(kCopies % NW == 0, "copies split evenly over the waves");
+#pragma unroll
+  for (int u = 0; u < kCopies / NW; ++u) {
+    const int it = w + NW * u;
+    const int p = it * 64 + lane;
+    const int r = p / (D / 8), sl = p % (D / 8);
+    const int voff = ((row0 + r) * D + 8 * (sl ^ swz<D>(r))) * 2;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + it * 512),
+                                             16, voff, 0, 0, 0);
+  }
+}
 // four consecutive rows of one column: lane gets M[kb + 4 (l/32) + s][n0 + l%32], s < 4
 template <int D>
 __device__ __forceinline__ u32x2 swz_col4(const uint16_t* m, int kb, int n0, int lane) {
