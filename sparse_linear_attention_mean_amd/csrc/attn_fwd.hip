@@ -16,19 +16,21 @@
 // computed transposed (S^T = K Q^T, O^T = V^T P^T) with v_mfma_f32_32x32x16:
 // then the S^T result tile, converted to bf16, is directly the B operand of
 // the P V product (k index permuted identically in the V^T operand), each
-// lane owns one query row, and row statistics need a single xor-32 exchange.
-// K_j and V_j arrive in LDS through asynchronous buffer->LDS copies into
-// XOR-swizzled row-major tiles (no staging registers, no LDS stores); the V^T
-// operand of the P V product is read from the V tile with LDS transpose reads.
-// Both tiles are double-buffered: the next block's copies are in flight during
-// the current block's MFMAs; the swizzle keeps the 16-byte operand reads and
-// the transpose reads spread over the LDS banks.
+// lane owns one query row, and row statistics need a single exchange between
+// the two 32-lane halves.
+// The loop is software-pipelined by one block: iteration n issues the S^T
+// MFMAs of block n and, while they run, does the online softmax of block
+// n - 1 and its P V product, so the matrix cores and the vector ALUs work at
+// the same time within each wave.  K_j and V_j arrive in LDS through
+// asynchronous buffer->LDS copies into XOR-swizzled row-major tiles (no
+// staging registers, no LDS stores), K one iteration ahead of its use and V
+// two (K tiles and V tiles have two buffers each); the V^T operand is read
+// from the V tile with LDS transpose reads.  The swizzle keeps the 16-byte
+// operand reads and the transpose reads spread over the LDS banks.
 // The two key halves are merged at the end like split-K partial softmaxes,
 // each wave finishing half of the output tiles.  H_i and Z_i for the linear
-// branch are copied asynchronously into the staging buffer the last critical
-// block leaves free, while that block is processed.
-#include <type_traits>
-
+// branch are copied asynchronously into the K buffers once the last S^T tile
+// has been computed.
 #include "sla_device.h"
 #include "sla_internal.h"
 
@@ -55,9 +57,8 @@ struct AttnArgs {
 
 template <int D>
 struct AttnCfg {
-  static constexpr int kBuf = 2 * 64 * D;          // one K + V buffer (bf16 elements), swizzled tiles
+  static constexpr int kTile = 64 * D;             // one K or V tile (bf16 elements), swizzled
   static constexpr int kExtra = 4096;              // bytes: Z_i and the merge statistics
-  static constexpr int kLds = 2 * kBuf * 2 + kExtra;
   static constexpr int NCT = D / 32;               // 32-row tiles of O^T per wave
   static constexpr int NCC = D / 16;               // 16-wide k chunks over the head dim
 };
@@ -65,8 +66,14 @@ struct AttnCfg {
 template <int D, bool DENSE, bool LINEAR>
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs args) {
   using C = AttnCfg<D>;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[C::kLds / 2];
-  float* extra = reinterpret_cast<float*>(smem + 2 * C::kBuf);
+  // Every buffer is its own array and every access names its array
+  // statically, so the compiler can tell the LDS reads from the copies in
+  // flight and does not hold the reads back until the copies land.
+  __shared__ __attribute__((aligned(16))) uint16_t kb0[C::kTile];
+  __shared__ __attribute__((aligned(16))) uint16_t kb1[C::kTile];
+  __shared__ __attribute__((aligned(16))) uint16_t vb0[C::kTile];
+  __shared__ __attribute__((aligned(16))) uint16_t vb1[C::kTile];
+  __shared__ __attribute__((aligned(16))) float extra[C::kExtra / 4];
 
   const int T = args.T, N = args.N, L = args.L;
   const uint32_t wg = xcd_remap(blockIdx.x, gridDim.x);
@@ -74,7 +81,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs args) {
   const long long bh = wg / T;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kh = wave & 1, qh = wave >> 1;
   const int n32 = lane & 31, hl = lane >> 5;
   const size_t head = static_cast<size_t>(bh) * N * D;
@@ -92,16 +99,37 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs args) {
 
   const int cnt = DENSE ? T : args.lut_cnt[bh * T + i];
   const int32_t* lrow = DENSE ? nullptr : args.lut + (bh * T + i) * static_cast<long long>(T);
+  // the list is held in a register, entry 64 g + l in lane l (g = n / 64): the
+  // loop takes its block indices with readlane instead of a memory load
+  int lutv = 0;
+  if (!DENSE && lane < cnt) lutv = lrow[lane];
+  auto block_at = [&](int n) { return DENSE ? n : __builtin_amdgcn_readlane(lutv, n & 63); };
+  // ascending lists: only the last block can be the padded one
+  const int jl = cnt == 0 ? 0 : DENSE ? cnt - 1 : lrow[cnt - 1];
+  const bool mlast = (jl + 1) * kBlock > L;
 
   // K_j and V_j arrive through asynchronous buffer->LDS copies into swizzled
   // tiles (no staging registers).  The resources end at valid_len, so the
   // rows of the padded last block past it arrive as zeros.
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(args.k + head, static_cast<uint32_t>(L) * D * 2);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(args.v + head, static_cast<uint32_t>(L) * D * 2);
-  auto copy_block = [&](int jb, int bufidx) {
-    uint16_t* ks_ = smem + bufidx * C::kBuf;
-    copy_swz_buf<D, 4>(krs, jb * kBlock, ks_, wave, lane);
-    copy_swz_buf<D, 4>(vrs, jb * kBlock, ks_ + 64 * D, wave, lane);
+  auto copy_k = [&](int n, uint16_t* dst) __attribute__((always_inline)) {
+    if (n < cnt) copy_swz_buf<D, 4>(krs, block_at(n) * kBlock, dst, wave, lane);
+  };
+  auto copy_v = [&](int n, uint16_t* dst) __attribute__((always_inline)) {
+    copy_swz_buf<D, 4>(vrs, block_at(n) * kBlock, dst, wave, lane);
+  };
+  // H_i^T (swizzled, rows 0..63 into kb0 and 64..127 into kb1) and Z_i, once
+  // the K buffers are no longer read
+  float* zsw = extra;   // 2 D floats
+  auto copy_hz = [&]() __attribute__((always_inline)) {
+    if constexpr (LINEAR) {
+      const size_t hslot = static_cast<size_t>(bh) * T + (args.hglobal ? 0 : i);
+      const uint16_t* hsrc = args.hst + hslot * D * D;
+      copy_swz<D>(hsrc, kb0, 64, wave, 4, lane);
+      if constexpr (D == 128) copy_swz<D>(hsrc + 64 * D, kb1, 64, wave, 4, lane);
+      if (wave == 3 && lane < D / 2) gl_to_lds16(args.zst + hslot * 2 * D + 4 * lane, zsw);
+    }
   };
 
   f32x16 acc[C::NCT];
@@ -110,57 +138,42 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs args) {
   float m_run = -INFINITY;   // running max (log2 units) of this lane's query
   float l_run = 0.f;         // partial row sum over this lane's keys
 
-  // One key block: S^T = K Q^T, online softmax (base 2, lazy rescale), O^T += V^T P^T.
-  // MASKED is used only for the padded last key block.
-  // The buffer the last key block leaves free receives H_i^T (swizzled tile)
-  // and Z_i through asynchronous copies, so the linear epilogue reads LDS.
-  const int hbuf = cnt > 0 ? (((cnt - 1) & 1) ^ 1) : 1;
-  uint16_t* hsw = smem + hbuf * C::kBuf;
-  float* zsw = extra;                       // 2 D floats
-  auto copy_hz = [&]() {
-    if constexpr (LINEAR) {
-      const size_t hslot = static_cast<size_t>(bh) * T + (args.hglobal ? 0 : i);
-      copy_swz<D>(args.hst + hslot * D * D, hsw, D, wave, 4, lane);
-      if (wave == 3 && lane < D / 2) gl_to_lds16(args.zst + hslot * 2 * D + 4 * lane, zsw);
-    }
-  };
-  if (cnt == 0) copy_hz();
-
-  auto step = [&](int n, auto masked_tag) {
-    constexpr bool MASKED = decltype(masked_tag)::value;
-    const int j = DENSE ? n : lrow[n];
-    const int buf = n & 1;
-    const bool more = n + 1 < cnt;
-    if (more)
-      copy_block(DENSE ? n + 1 : lrow[n + 1], buf ^ 1);
-    else
-      copy_hz();   // buffer buf ^ 1 is no longer read
-    const uint16_t* ks = smem + buf * C::kBuf;
-    const uint16_t* vt = ks + 64 * D;
-    // S^T = K Q^T: K operand rows read four chunks ahead of the MFMA chain
+  // S^T = K Q^T for the K tile kt; K operand rows read four chunks ahead
+  auto s_tile = [&](const uint16_t* kt) __attribute__((always_inline)) {
     constexpr int KA = C::NCC < 4 ? C::NCC : 4;
     bf16x8 ka[KA];
 #pragma unroll
     for (int cc = 0; cc < KA; ++cc)
-      ka[cc] = as_bf16x8(ld16(ks + swz_off<D>(32 * kh + n32, 16 * cc + 8 * hl)));
+      ka[cc] = as_bf16x8(ld16(kt + swz_off<D>(32 * kh + n32, 16 * cc + 8 * hl)));
     f32x16 st = {};
 #pragma unroll
     for (int cc = 0; cc < C::NCC; ++cc) {
       const bf16x8 a = ka[cc % KA];
-      if (cc + KA < C::NCC) ka[cc % KA] = as_bf16x8(ld16(ks + swz_off<D>(32 * kh + n32, 16 * (cc + KA) + 8 * hl)));
+      if (cc + KA < C::NCC)
+        ka[cc % KA] = as_bf16x8(ld16(kt + swz_off<D>(32 * kh + n32, 16 * (cc + KA) + 8 * hl)));
       st = mfma32(a, qf[cc], st);
     }
-    if constexpr (MASKED) {
+    return st;
+  };
+  // online softmax of one S^T tile (base 2, lazy rescale) and O^T += V^T P^T
+  // with the V tile vt; masked: the tile of the padded last key block jl
+  auto soft_pv = [&](f32x16 st, const uint16_t* vt,
+                     bool masked) __attribute__((always_inline)) {
+    if (masked) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int key = j * kBlock + 32 * kh + 8 * (e / 4) + 4 * hl + (e % 4);
+        const int key = jl * kBlock + 32 * kh + 8 * (e / 4) + 4 * hl + (e % 4);
         if (key >= L) st[e] = -INFINITY;
       }
     }
-    float mraw = st[0];
+    float mraw = fmaxf(st[0], st[1]);
 #pragma unroll
-    for (int e = 1; e < 16; ++e) mraw = fmaxf(mraw, st[e]);
-    mraw = fmaxf(mraw, __shfl_xor(mraw, 32));
+    for (int e = 2; e < 16; e += 2) mraw = fmaxf(mraw, fmaxf(st[e], st[e + 1]));
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mraw), __float_as_uint(mraw),
+                                                       false, false);
+      mraw = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));   // max over both lane halves
+    }
     const float m_new = fmaxf(m_run, mraw * sl2);
     const bool need = m_new > m_run + 8.0f;
     if (__any(need)) {
@@ -188,27 +201,59 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs args) {
 #pragma unroll
       for (int h = 0; h < 2; ++h)
         acc[ct] = mfma32(swz_op32_tr_perm<D>(vt, 32 * kh + 16 * h, 32 * ct, lane), pb[h], acc[ct]);
-    __builtin_amdgcn_s_waitcnt(0);   // this wave's copies into buffer buf ^ 1 have landed
+  };
+  auto sync = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's copies have landed
     __syncthreads();
   };
 
-  if (cnt > 0) {
-    copy_block(DENSE ? 0 : lrow[0], 0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    for (int n = 0; n + 1 < cnt; ++n) step(n, std::false_type{});
-    const int jl = DENSE ? cnt - 1 : lrow[cnt - 1];   // ascending lists: only the last can be padded
-    if ((jl + 1) * kBlock > L)
-      step(cnt - 1, std::true_type{});
+  // Iteration n (1 <= n < cnt): K_n is in kc, V_{n-1} in vp, S^T of block
+  // n - 1 in sp; K_{n+1} is copied into kn (the buffer of K_{n-1}) and V_n
+  // into vn (the buffer of V_{n-2}).
+  f32x16 sp;
+  auto iter = [&](int n, const uint16_t* kc, uint16_t* kn, uint16_t* vn,
+                  const uint16_t* vp) __attribute__((always_inline)) {
+    copy_k(n + 1, kn);
+    copy_v(n, vn);
+    const f32x16 sn = s_tile(kc);
+    soft_pv(sp, vp, false);
+    sp = sn;
+    sync();
+  };
+
+  if (cnt == 0) {
+    copy_hz();
+  } else {
+    copy_k(0, kb0);
+    sync();
+    copy_k(1, kb1);
+    copy_v(0, vb0);
+    sp = s_tile(kb0);
+    sync();
+    int n = 1;
+    for (; n + 1 < cnt; n += 2) {
+      iter(n, kb1, kb0, vb1, vb0);
+      iter(n + 1, kb0, kb1, vb0, vb1);
+    }
+    if (n < cnt) iter(n, kb1, kb0, vb1, vb0);
+    // last block cnt - 1: its V tile is in vb0 when cnt is odd
+    copy_hz();
+    if (cnt & 1)
+      soft_pv(sp, vb0, mlast);
     else
-      step(cnt - 1, std::false_type{});
+      soft_pv(sp, vb1, mlast);
   }
   l_run += __shfl_xor(l_run, 32);
 
   // ---- merge the two key halves (split-K style): wave (kh, qh) finishes the
   // O_s^T tiles ct = NH kh .. NH kh + NH - 1 and hands the others to its partner.
   constexpr int NH = C::NCT / 2;
-  float* ex = reinterpret_cast<float*>(smem + (hbuf ^ 1) * C::kBuf);   // [wave][NH][16][64]
+  // exchange area [wave][NH][16][64] floats: waves 0, 1 in vb0, waves 2, 3 in vb1
+  auto exw = [&](int w) {
+    return reinterpret_cast<float*>(w >> 1 ? vb1 : vb0) + (w & 1) * NH * 16 * 64;
+  };
+  float* exo = exw(wave);
+  const float* exp_ = exw(wave ^ 1);
   float* exm = extra + 2 * D;                                            // [wave][64]
   float* exl = exm + 4 * 64;                                             // [wave][64]
   __syncthreads();
@@ -218,14 +263,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs args) {
     for (int x = 0; x < NH; ++x) {
       fin[x] = acc[x];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) ex[((wave * NH + x) * 16 + e) * 64 + lane] = acc[NH + x][e];
+      for (int e = 0; e < 16; ++e) exo[(x * 16 + e) * 64 + lane] = acc[NH + x][e];
     }
   } else {
 #pragma unroll
     for (int x = 0; x < NH; ++x) {
       fin[x] = acc[NH + x];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) ex[((wave * NH + x) * 16 + e) * 64 + lane] = acc[x][e];
+      for (int e = 0; e < 16; ++e) exo[(x * 16 + e) * 64 + lane] = acc[x][e];
     }
   }
   exm[wave * 64 + lane] = m_run;
@@ -251,7 +296,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs args) {
     for (int x = 0; x < NH; ++x)
 #pragma unroll
       for (int e = 0; e < 16; ++e)
-        fin[x][e] = (a1 * fin[x][e] + a2 * ex[((partner * NH + x) * 16 + e) * 64 + lane]) * inv;
+        fin[x][e] = (a1 * fin[x][e] + a2 * exp_[(x * 16 + e) * 64 + lane]) * inv;
     if (kh == 0 && hl == 0) args.lse[bh * N + row] = valid_row ? lse_v : -INFINITY;
   }
   // lane holds O_s^T[c = 32 (NH kh + x) + 8 (e/4) + 4 hl + e%4][row]
@@ -291,11 +336,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs args) {
     const float den_v = dpart + __shfl_xor(dpart, 32);
     const float rden = den_v > 0.f ? 1.0f / den_v : 0.f;
     constexpr int NCL = D / 64;   // 32-row tiles of Y^T per wave (c half kh)
+    // H^T row c: rows 0 .. 63 are in kb0, rows 64 .. 127 (D = 128) in kb1
+    const uint16_t* hsw = (D == 128 && kh) ? kb1 : kb0;
+    const int hrow0 = D == 128 ? 0 : (D / 2) * kh;
     f32x16 lin[NCL];
 #pragma unroll
     for (int ct = 0; ct < NCL; ++ct) {
       lin[ct] = f32x16{};
-      const int c = (D / 2) * kh + 32 * ct + n32;
+      const int c = hrow0 + 32 * ct + n32;
 #pragma unroll
       for (int cc = 0; cc < C::NCC; ++cc)
         lin[ct] = mfma32(as_bf16x8(ld16(hsw + swz_off<D>(c, 16 * cc + 8 * hl))), pq[cc], lin[ct]);
@@ -303,7 +351,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs args) {
     if (kh == 0 && hl == 0) args.den[bh * N + row] = valid_row ? den_v : 0.f;
     __syncthreads();   // exchange area free again: reuse it for Y (bf16 [64][D + 8])
     constexpr int YP = D + 8;
-    uint16_t* ysl = reinterpret_cast<uint16_t*>(ex);
+    uint16_t* ysl = reinterpret_cast<uint16_t*>(qh ? vb1 : vb0);   // rows 32 qh .. 32 qh + 31
     uint16_t* yrow = args.y + head + static_cast<size_t>(row) * D;
 #pragma unroll
     for (int ct = 0; ct < NCL; ++ct)
@@ -312,12 +360,12 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs args) {
         const int c = (D / 2) * kh + 32 * ct + 8 * e4 + 4 * hl;
         const uint32_t w0 = pack_bf16x2(lin[ct][4 * e4] * rden, lin[ct][4 * e4 + 1] * rden);
         const uint32_t w1 = pack_bf16x2(lin[ct][4 * e4 + 2] * rden, lin[ct][4 * e4 + 3] * rden);
-        st8(ysl + (32 * qh + n32) * YP + c, u32x2{w0, w1});
+        st8(ysl + n32 * YP + c, u32x2{w0, w1});
         st8(yrow + c, valid_row ? u32x2{w0, w1} : u32x2{0u, 0u});
       }
     __syncthreads();
     // ---- fusion: O^T = O_s^T + W Y^T, wave (kh = o half, qh) ----
-    const uint16_t* ys = ysl + (32 * qh + n32) * YP + 8 * hl;
+    const uint16_t* ys = ysl + n32 * YP + 8 * hl;
 #pragma unroll
     for (int ot = 0; ot < NCL; ++ot) {
       const int obase = (D / 2) * kh + 32 * ot;
