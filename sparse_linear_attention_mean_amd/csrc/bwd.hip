@@ -206,9 +206,7 @@ __global__ __launch_bounds__(256, 2) void bwd_prep_kernel(
 // ---------------------------------------------------------------------------
 template <int D>
 struct BqCfg {
-  static constexpr int KP = D == 128 ? 152 : 72;      // row pitch (bf16)
-  static constexpr int kBuf = 2 * 64 * KP;             // K and V rows
-  static constexpr int KCH = D / 32;                   // 16-byte chunks per thread per tensor
+  static constexpr int kTile = 64 * D;                 // one K or V tile (bf16), swizzled
   static constexpr int NCC = D / 16, NAT = D / 32;
 };
 
@@ -220,13 +218,18 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(
     const int32_t* __restrict__ lut, const int32_t* __restrict__ lut_cnt,
     float* __restrict__ dq, int N, int L, int T, float scale) {
   using C = BqCfg<D>;
-  constexpr int KP = C::KP;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * C::kBuf];
+  // separate arrays, named statically by every access: the compiler can tell
+  // the LDS reads from the copies in flight
+  __shared__ __attribute__((aligned(16))) uint16_t kb0[C::kTile];
+  __shared__ __attribute__((aligned(16))) uint16_t kb1[C::kTile];
+  __shared__ __attribute__((aligned(16))) uint16_t vb0[C::kTile];
+  __shared__ __attribute__((aligned(16))) uint16_t vb1[C::kTile];
 
   const uint32_t wg = xcd_remap(blockIdx.x, gridDim.x);
   const int i = wg % T;
   const long long bh = wg / T;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kh = wave & 1, qh = wave >> 1;
   const int n32 = lane & 31, hl = lane >> 5;
   const size_t head = static_cast<size_t>(bh) * N * D;
@@ -249,94 +252,103 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(
   const float dsv = valid ? dsum[bh * N + row] : 0.f;
   const int cnt = lut_cnt[bh * T + i];
   const int32_t* lrow = lut + (bh * T + i) * static_cast<long long>(T);
+  // the list in a register (entry 64 g + l in lane l), read with readlane
+  int lutv = lane < cnt ? lrow[lane] : 0;
+  auto block_at = [&](int n) { return __builtin_amdgcn_readlane(lutv, n & 63); };
+  // ascending lists: only the last block can be the padded one
+  const int jl = cnt == 0 ? 0 : lrow[cnt - 1];
+  const bool mlast = (jl + 1) * kBlock > L;
 
   f32x16 acc[C::NAT];
 #pragma unroll
   for (int at = 0; at < C::NAT; ++at) acc[at] = f32x16{};
 
-  u32x4 rk[C::KCH], rv[C::KCH];
-  auto load = [&](int j) {
-    const size_t off = head + static_cast<size_t>(j) * kBlock * D;
-#pragma unroll
-    for (int u = 0; u < C::KCH; ++u) {
-      const int e = tid + 256 * u;
-      rk[u] = ld16(k + off + 8 * e);
-      rv[u] = ld16(v + off + 8 * e);
-    }
+  // K_j, V_j by asynchronous buffer->LDS copies into swizzled tiles; the
+  // resources end at valid_len, so rows of the padded block past it are zero
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(k + head, static_cast<uint32_t>(L) * D * 2);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(v + head, static_cast<uint32_t>(L) * D * 2);
+  auto copy_kv = [&](int n, uint16_t* kd, uint16_t* vd) __attribute__((always_inline)) {
+    const int jb = block_at(n);
+    copy_swz_buf<D, 4>(krs, jb * kBlock, kd, wave, lane);
+    copy_swz_buf<D, 4>(vrs, jb * kBlock, vd, wave, lane);
   };
-  auto store = [&](int buf, int j) {
-    uint16_t* ks = smem + buf * C::kBuf;
-    uint16_t* vs = ks + 64 * KP;
-    const int nvalid = L - j * kBlock;   // < 64 only for the last (padded) key block
+  // This block's dQ rows (the linear part written by the preparation kernel,
+  // fp32 64 x D) are copied into the buffers the last key block leaves free:
+  // rows 0..31 into its K buffer, rows 32..63 into its V buffer.
+  auto copy_dq = [&](float* r0, float* r1) __attribute__((always_inline)) {
+    const float* src = dq + head + static_cast<size_t>(i) * kBlock * D;
+    constexpr int kCopies = 32 * D / 4 / 64;   // 16-byte chunks / 64 per copy, per half
 #pragma unroll
-    for (int u = 0; u < C::KCH; ++u) {
-      const int e = tid + 256 * u;
-      const int t = e / (D / 8);
-      const bool ok = t < nvalid;        // padded keys: zero K and V rows
-      st16(ks + t * KP + 8 * (e % (D / 8)), ok ? rk[u] : u32x4{0u, 0u, 0u, 0u});
-      st16(vs + t * KP + 8 * (e % (D / 8)), ok ? rv[u] : u32x4{0u, 0u, 0u, 0u});
+    for (int it = wave; it < kCopies; it += 4) {
+      gl_to_lds16(src + 4 * (it * 64 + lane), r0 + it * 256);
+      gl_to_lds16(src + 32 * D + 4 * (it * 64 + lane), r1 + it * 256);
     }
   };
 
-  // The buffer the last key block leaves free receives this block's dQ rows
-  // (the linear part written by the preparation kernel, fp32 64 x D) through
-  // asynchronous copies, so the final read-modify-write reads LDS.
-  const int dqbuf = cnt > 0 ? (((cnt - 1) & 1) ^ 1) : 1;
-  float* dqs = reinterpret_cast<float*>(smem + dqbuf * C::kBuf);
-  auto copy_dq = [&]() {
-    const float* src = dq + head + static_cast<size_t>(i) * kBlock * D;
-    constexpr int kCopies = 64 * D / 4 / 64;   // 16-byte chunks / 64 per copy
-    for (int it = wave; it < kCopies; it += 4) gl_to_lds16(src + 4 * (it * 64 + lane), dqs + it * 256);
-  };
-  if (cnt > 0) {
-    load(lrow[0]);
-    store(0, lrow[0]);
-    __syncthreads();
-  } else {
-    copy_dq();
-  }
-  for (int n = 0; n < cnt; ++n) {
-    const int j = lrow[n];
-    const int buf = n & 1;
-    const int jn = n + 1 < cnt ? lrow[n + 1] : 0;
+  // one key block from (kt, vt); the next one is copied into (kn, vn), or
+  // this block's dQ rows after the last one
+  auto step = [&](int n, const uint16_t* kt, const uint16_t* vt, uint16_t* kn, uint16_t* vn,
+                  bool masked) __attribute__((always_inline)) {
+    if (((n + 1) & 63) == 0 && n + 1 < cnt) {
+      const int e = n + 1 + lane;   // the next 64 entries of the list
+      lutv = e < cnt ? lrow[e] : 0;
+    }
     if (n + 1 < cnt)
-      load(jn);
+      copy_kv(n + 1, kn, vn);
     else
-      copy_dq();   // buffer buf ^ 1 is no longer read
-    const uint16_t* ks = smem + buf * C::kBuf;
-    const uint16_t* vs = ks + 64 * KP;
+      copy_dq(reinterpret_cast<float*>(kn), reinterpret_cast<float*>(vn));
     f32x16 st = {}, dpt = {};
 #pragma unroll
     for (int cc = 0; cc < C::NCC; ++cc) {
-      st = mfma32(as_bf16x8(ld16(ks + (32 * kh + n32) * KP + 16 * cc + 8 * hl)), qf[cc], st);
-      dpt = mfma32(as_bf16x8(ld16(vs + (32 * kh + n32) * KP + 16 * cc + 8 * hl)), dof[cc], dpt);
+      st = mfma32(as_bf16x8(ld16(kt + swz_off<D>(32 * kh + n32, 16 * cc + 8 * hl))), qf[cc], st);
+      dpt = mfma32(as_bf16x8(ld16(vt + swz_off<D>(32 * kh + n32, 16 * cc + 8 * hl))), dof[cc], dpt);
     }
     float dsf[16];
 #pragma unroll
     for (int e = 0; e < 16; ++e) dsf[e] = __builtin_amdgcn_exp2f(__fmaf_rn(st[e], sl2, -lse2));
-    if ((j + 1) * kBlock > L) {   // uniform: only the padded last key block
+    if (masked) {   // keys of the padded last block past valid_len
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int key = j * kBlock + 32 * kh + 8 * (e / 4) + 4 * hl + (e % 4);
+        const int key = jl * kBlock + 32 * kh + 8 * (e / 4) + 4 * hl + (e % 4);
         if (key >= L) dsf[e] = 0.f;
       }
     }
 #pragma unroll
     for (int e = 0; e < 16; ++e) dsf[e] *= dpt[e] - dsv;
     const bf16x8 ds[2] = {cvt_bf16x8(dsf), cvt_bf16x8(dsf + 8)};
-    // dQ[q][a] += dS[q][keys] K[keys][a]: B operand K[keys of chunk h][a] by transpose reads
+    // dQ[q][a] += dS[q][keys] K[keys][a]: B operand K[keys of chunk h][a] by
+    // transpose reads, keys in the permuted order of the S^T tile
 #pragma unroll
     for (int at = 0; at < C::NAT; ++at)
 #pragma unroll
       for (int h = 0; h < 2; ++h)
-        acc[at] = mfma32(ds[h], lds_op32_tr<true>(ks, KP, 32 * kh + 16 * h, 32 * at, lane), acc[at]);
-    if (n + 1 < cnt) store(buf ^ 1, jn);
+        acc[at] = mfma32(ds[h], swz_op32_tr_perm<D>(kt, 32 * kh + 16 * h, 32 * at, lane), acc[at]);
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's copies have landed
     __syncthreads();
+  };
+
+  if (cnt == 0) {
+    copy_dq(reinterpret_cast<float*>(kb0), reinterpret_cast<float*>(vb0));
+  } else {
+    copy_kv(0, kb0, vb0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int n = 0; n < cnt; n += 2) {
+      step(n, kb0, vb0, kb1, vb1, mlast && n + 1 == cnt);
+      if (n + 1 < cnt) step(n + 1, kb1, vb1, kb0, vb0, mlast && n + 2 == cnt);
+    }
   }
   // merge the key halves: wave (kh, qh) finishes the tiles at = NH kh .. NH kh + NH - 1
-  // and hands the others to its partner (other kh); then add the linear part
+  // and hands the others to its partner (other kh); then add the linear part.
+  // The last block's buffers hold the exchange (waves 0, 1 in its K buffer,
+  // 2, 3 in its V buffer), the other ones the dQ rows.
   constexpr int NH = C::NAT / 2;
-  float* ex = reinterpret_cast<float*>(smem + (dqbuf ^ 1) * C::kBuf);   // [wave][NH][16][64]
+  const bool odd = cnt & 1;   // the last block (cnt - 1) was read from kb0 / vb0
+                              // (cnt = 0: the dQ rows are in kb0 / vb0 as well)
+  float* exq = reinterpret_cast<float*>(qh ? (odd ? vb0 : vb1) : (odd ? kb0 : kb1));
+  const float* dqs = reinterpret_cast<const float*>(qh ? (odd ? vb1 : vb0) : (odd ? kb1 : kb0));
+  float* exo = exq + kh * NH * 16 * 64;
+  const float* exp_ = exq + (kh ^ 1) * NH * 16 * 64;
   __syncthreads();
   f32x16 fin[NH];
   if (kh == 0) {
@@ -344,29 +356,28 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(
     for (int x = 0; x < NH; ++x) {
       fin[x] = acc[x];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) ex[((wave * NH + x) * 16 + e) * 64 + lane] = acc[NH + x][e];
+      for (int e = 0; e < 16; ++e) exo[(x * 16 + e) * 64 + lane] = acc[NH + x][e];
     }
   } else {
 #pragma unroll
     for (int x = 0; x < NH; ++x) {
       fin[x] = acc[NH + x];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) ex[((wave * NH + x) * 16 + e) * 64 + lane] = acc[x][e];
+      for (int e = 0; e < 16; ++e) exo[(x * 16 + e) * 64 + lane] = acc[x][e];
     }
   }
   __builtin_amdgcn_s_waitcnt(0);   // this wave's dQ copies have landed
   __syncthreads();
-  const int partner = wave ^ 1;
   // lane holds dQ[q = 32 qh + 8 (e/4) + 4 hl + e%4][a = 32 at + n32]
 #pragma unroll
   for (int x = 0; x < NH; ++x)
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const int ql = 32 * qh + 8 * (e / 4) + 4 * hl + (e % 4);
+      const int qlh = 8 * (e / 4) + 4 * hl + (e % 4);   // row within the half
       const int a = 32 * (NH * kh + x) + n32;
-      const float sparse = scale * (fin[x][e] + ex[((partner * NH + x) * 16 + e) * 64 + lane]);
-      const int qr = i * kBlock + ql;
-      dq[head + static_cast<size_t>(qr) * D + a] = qr < L ? dqs[ql * D + a] + sparse : 0.f;
+      const float sparse = scale * (fin[x][e] + exp_[(x * 16 + e) * 64 + lane]);
+      const int qr = i * kBlock + 32 * qh + qlh;
+      dq[head + static_cast<size_t>(qr) * D + a] = qr < L ? dqs[qlh * D + a] + sparse : 0.f;
     }
 }
 
