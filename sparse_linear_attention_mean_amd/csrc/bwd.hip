@@ -391,28 +391,23 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(
 // dP = dO V^T take K_j, V_j from registers and Q_i, dO_i rows from LDS; the
 // products over queries take P or dS straight from the S / dP result tiles
 // (k index permuted) and read dO_i or Q_i from the same LDS tiles with
-// transpose reads, so only the natural tiles are staged.  The row pitch keeps
-// both kinds of LDS read free of bank conflicts.
-// Everything the block needs besides the Q_i / dO_i stream -- K_j, V_j, dh_j^T
-// and dz_j -- is copied into LDS asynchronously when the workgroup starts, so
+// transpose reads, so only the natural tiles are staged.
+// Q_i, dO_i and the rows' lse / D values arrive through asynchronous
+// buffer->LDS copies (Q_i, dO_i into XOR-swizzled tiles), double-buffered in
+// separate arrays so that the next query block's copies overlap the current
+// one's products.  The resources end at valid_len: the padded rows of the
+// last query block arrive as zeros (Q = dO = 0 and D = 0 there, so they add
+// nothing to dV and, with dP = 0, nothing to dK).
+// Everything the block needs besides that stream -- K_j, V_j, dh_j^T and
+// dz_j -- is copied into LDS asynchronously when the workgroup starts, so
 // those reads overlap the first query block and the linear epilogue reads LDS
 // only.  After the loop the two query halves are merged so that every wave
 // finishes two of the four 32-column tiles.
 // ---------------------------------------------------------------------------
 template <int D>
 struct BkvCfg {
-  static constexpr int RP = D == 128 ? 152 : 72;      // Q / dO row pitch (bf16)
-  static constexpr int kBuf = 2 * 64 * RP;              // Q and dO of one query block
-  static constexpr int KCH = D / 64;                    // 16-byte chunks per thread per tensor
+  static constexpr int kTile = 64 * D;                  // one Q or dO tile (bf16), swizzled
   static constexpr int NCC = D / 16, NCT = D / 32;
-  static constexpr int kStage = 2 * kBuf * 2 + 2 * 2 * 64 * 4;   // bytes: 2 buffers + lse/D
-  static constexpr int kMerge = 8 * (NCT / 2) * 16 * 64 * 4;    // half of every wave's tiles (fp32)
-  static constexpr int kLoop = kStage > kMerge ? kStage : kMerge;
-  static constexpr int kKs = kLoop;                 // K_j, swizzled 64 x D
-  static constexpr int kVs = kKs + 64 * D * 2;      // V_j
-  static constexpr int kDh = kVs + 64 * D * 2;      // dh_j^T, swizzled D x D
-  static constexpr int kDz = kDh + D * D * 2;       // dz_j, 2 D floats
-  static constexpr int kLds = kDz + 2 * D * 4;
 };
 
 template <int D>
@@ -424,20 +419,23 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(
     const uint16_t* __restrict__ dh, const float* __restrict__ dz, bool linear, bool hglobal,
     float* __restrict__ dk, float* __restrict__ dv, int N, int L, int T, float scale) {
   using C = BkvCfg<D>;
-  constexpr int RP = C::RP;
-  __shared__ __attribute__((aligned(16))) uint8_t smem_raw[C::kLds];
-  uint16_t* smem = reinterpret_cast<uint16_t*>(smem_raw);
-  float* lses = reinterpret_cast<float*>(smem_raw + 2 * C::kBuf * 2);   // [buf][64]
-  float* dss = lses + 128;                                              // [buf][64]
-  uint16_t* ksw = reinterpret_cast<uint16_t*>(smem_raw + C::kKs);
-  uint16_t* vsw = reinterpret_cast<uint16_t*>(smem_raw + C::kVs);
-  uint16_t* dhs = reinterpret_cast<uint16_t*>(smem_raw + C::kDh);
-  float* dzs = reinterpret_cast<float*>(smem_raw + C::kDz);
+  // the streamed buffers are separate arrays, named statically by every
+  // access, so the compiler can tell the LDS reads from the copies in flight
+  // (Q_i tile, then the dO_i tile, in one array per stage)
+  __shared__ __attribute__((aligned(16))) uint16_t qd0[2 * C::kTile];
+  __shared__ __attribute__((aligned(16))) uint16_t qd1[2 * C::kTile];
+  __shared__ __attribute__((aligned(16))) float lb0[128];   // lse [64] then D [64] of the rows
+  __shared__ __attribute__((aligned(16))) float lb1[128];
+  __shared__ __attribute__((aligned(16))) uint16_t ksw[64 * D];   // K_j, swizzled
+  __shared__ __attribute__((aligned(16))) uint16_t vsw[64 * D];   // V_j
+  __shared__ __attribute__((aligned(16))) uint16_t dhs[D * D];    // dh_j^T, swizzled
+  __shared__ __attribute__((aligned(16))) float dzs[2 * D];       // dz_j
 
   const uint32_t wg = xcd_remap(blockIdx.x, gridDim.x);
   const int j = wg % T;
   const long long bh = wg / T;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool role_dk = wave >= 4;               // uniform per wave
   const int kh = wave & 1, qh = (wave >> 1) & 1;
   const int n32 = lane & 31, hl = lane >> 5;
@@ -458,48 +456,35 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(
   }
   const int cnt = col_cnt[bh * T + j];
   const int32_t* crow = col + (bh * T + j) * static_cast<long long>(T);
+  // the list in a register (entry 64 g + l in lane l), read with readlane
+  int colv = lane < cnt ? crow[lane] : 0;
+  auto block_at = [&](int n) { return __builtin_amdgcn_readlane(colv, n & 63); };
+
+  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(q + head, static_cast<uint32_t>(L) * D * 2);
+  const __amdgpu_buffer_rsrc_t drs = make_rsrc(dO + head, static_cast<uint32_t>(L) * D * 2);
+  const __amdgpu_buffer_rsrc_t lrs = make_rsrc(lse + bh * N, static_cast<uint32_t>(L) * 4);
+  const __amdgpu_buffer_rsrc_t srs = make_rsrc(dsum + bh * N, static_cast<uint32_t>(L) * 4);
+  // Q_i, dO_i tiles into qd (8 waves share the copies) and the rows' lse / D values
+  auto copy_q = [&](int n, uint16_t* qd, float* ld) __attribute__((always_inline)) {
+    const int ib = block_at(n);
+    copy_swz_buf<D, 8>(qrs, ib * kBlock, qd, wave, lane);
+    copy_swz_buf<D, 8>(drs, ib * kBlock, qd + C::kTile, wave, lane);
+    // lane l writes base + 16 l: lse to ld[0..63] (wave 0), D to ld[64..127] (wave 1)
+    const uint32_t off = static_cast<uint32_t>(ib * kBlock + 4 * lane) * 4u;
+    if (wave == 0 && lane < 16)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(lrs, (__attribute__((address_space(3))) void*)(ld),
+                                               16, off, 0, 0, 0);
+    if (wave == 1 && lane < 16)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, (__attribute__((address_space(3))) void*)(ld + 64),
+                                               16, off, 0, 0, 0);
+  };
 
   f32x16 acc[C::NCT];   // dV (role 0) or the unscaled dK (role 1)
 #pragma unroll
   for (int ct = 0; ct < C::NCT; ++ct) acc[ct] = f32x16{};
 
-  u32x4 r_q[C::KCH], r_d[C::KCH];
-  float r_l = 0.f, r_s = 0.f;
-  auto load = [&](int ib) {
-    const size_t off = head + static_cast<size_t>(ib) * kBlock * D;
-#pragma unroll
-    for (int u = 0; u < C::KCH; ++u) {
-      const int e = tid + 512 * u;
-      r_q[u] = ld16(q + off + 8 * e);
-      r_d[u] = ld16(dO + off + 8 * e);
-    }
-    if (tid < kBlock) {
-      const int rr = ib * kBlock + tid;
-      r_l = rr < L ? lse[bh * N + rr] * kLog2e : INFINITY;
-      r_s = rr < L ? dsum[bh * N + rr] : 0.f;
-    }
-  };
-  auto store = [&](int buf, int ib) {
-    uint16_t* qs = smem + buf * C::kBuf;
-    uint16_t* ds_ = qs + 64 * RP;
-    const int nvalid = L - ib * kBlock;   // < 64 only for the last (padded) query block
-#pragma unroll
-    for (int u = 0; u < C::KCH; ++u) {
-      const int e = tid + 512 * u;
-      const int rr = e / (D / 8), cc8 = 8 * (e % (D / 8));
-      const bool ok = rr < nvalid;         // padded rows: zero Q and dO (and lse = inf)
-      st16(qs + rr * RP + cc8, ok ? r_q[u] : u32x4{0u, 0u, 0u, 0u});
-      st16(ds_ + rr * RP + cc8, ok ? r_d[u] : u32x4{0u, 0u, 0u, 0u});
-    }
-    if (tid < kBlock) {
-      lses[buf * 64 + tid] = r_l;
-      dss[buf * 64 + tid] = r_s;
-    }
-  };
-
-  if (cnt > 0) load(crow[0]);
+  if (cnt > 0) copy_q(0, qd0, lb0);
   __builtin_amdgcn_s_waitcnt(0);   // this wave's copies have landed
-  if (cnt > 0) store(0, crow[0]);
   __syncthreads();
 
   // K_j (and V_j for the dK role) as B operands (k = head-dim index 16 cc + 8 hl + s)
@@ -514,23 +499,27 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(
 
   const bool tail_key = key >= L;
   const bool tail_blk = (j + 1) * kBlock > L;   // uniform: the padded last key block
-  for (int n = 0; n < cnt; ++n) {
-    const int buf = n & 1;
-    const int inext = n + 1 < cnt ? crow[n + 1] : 0;
-    if (n + 1 < cnt) load(inext);
-    const uint16_t* qs = smem + buf * C::kBuf;
-    const uint16_t* ds_ = qs + 64 * RP;
+  // one query block from (qt: Q_i then dO_i, lt); the next one is copied into (qn, ln)
+  auto step = [&](int n, const uint16_t* qt, const float* lt, uint16_t* qn,
+                  float* ln) __attribute__((always_inline)) {
+    const uint16_t* dt = qt + C::kTile;
+    if (((n + 1) & 63) == 0 && n + 1 < cnt) {
+      const int e = n + 1 + lane;   // the next 64 entries of the list
+      colv = e < cnt ? crow[e] : 0;
+    }
+    if (n + 1 < cnt) copy_q(n + 1, qn, ln);
     f32x16 s = {};
 #pragma unroll
     for (int cc = 0; cc < C::NCC; ++cc)
-      s = mfma32(as_bf16x8(ld16(qs + (32 * qh + n32) * RP + 16 * cc + 8 * hl)), kf[cc], s);
+      s = mfma32(as_bf16x8(ld16(qt + swz_off<D>(32 * qh + n32, 16 * cc + 8 * hl))), kf[cc], s);
     // lane holds S[q = 32 qh + 8 (e/4) + 4 hl + e%4][key]: row statistics by 4
     float pf[16];
 #pragma unroll
     for (int e4 = 0; e4 < 4; ++e4) {
-      const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lses[buf * 64 + 32 * qh + 8 * e4 + 4 * hl]);
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lt[32 * qh + 8 * e4 + 4 * hl]);
 #pragma unroll
-      for (int x = 0; x < 4; ++x) pf[4 * e4 + x] = __builtin_amdgcn_exp2f(__fmaf_rn(s[4 * e4 + x], sl2, -l4[x]));
+      for (int x = 0; x < 4; ++x)
+        pf[4 * e4 + x] = __builtin_amdgcn_exp2f(__fmaf_rn(s[4 * e4 + x], sl2, -l4[x] * kLog2e));
     }
     if (tail_blk) {   // keys past valid_len: no probability mass
 #pragma unroll
@@ -540,31 +529,42 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(
       f32x16 dp = {};
 #pragma unroll
       for (int cc = 0; cc < C::NCC; ++cc)
-        dp = mfma32(as_bf16x8(ld16(ds_ + (32 * qh + n32) * RP + 16 * cc + 8 * hl)), vf[cc], dp);
+        dp = mfma32(as_bf16x8(ld16(dt + swz_off<D>(32 * qh + n32, 16 * cc + 8 * hl))), vf[cc], dp);
 #pragma unroll
       for (int e4 = 0; e4 < 4; ++e4) {
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&dss[buf * 64 + 32 * qh + 8 * e4 + 4 * hl]);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&lt[64 + 32 * qh + 8 * e4 + 4 * hl]);
 #pragma unroll
         for (int x = 0; x < 4; ++x) pf[4 * e4 + x] *= dp[4 * e4 + x] - d4[x];
       }
     }
     const bf16x8 xb[2] = {cvt_bf16x8(pf), cvt_bf16x8(pf + 8)};
-    // dV[key][c] += P^T dO  or  dK[key][a] += dS^T Q  (B operand by transpose reads)
-    const uint16_t* bsrc = role_dk ? qs : ds_;
+    // dV[key][c] += P^T dO  or  dK[key][a] += dS^T Q  (B operand by transpose
+    // reads, query index in the permuted order of the S tile)
+    const uint16_t* bsrc = qt + (role_dk ? 0 : C::kTile);
 #pragma unroll
     for (int ct = 0; ct < C::NCT; ++ct)
 #pragma unroll
       for (int h = 0; h < 2; ++h)
-        acc[ct] = mfma32(xb[h], lds_op32_tr<true>(bsrc, RP, 32 * qh + 16 * h, 32 * ct, lane), acc[ct]);
-    if (n + 1 < cnt) store(buf ^ 1, inext);
+        acc[ct] = mfma32(xb[h], swz_op32_tr_perm<D>(bsrc, 32 * qh + 16 * h, 32 * ct, lane), acc[ct]);
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's copies have landed
     __syncthreads();
+  };
+  for (int n = 0; n < cnt; n += 2) {
+    step(n, qd0, lb0, qd1, lb1);
+    if (n + 1 < cnt) step(n + 1, qd1, lb1, qd0, lb0);
   }
 
   // ---- merge the query halves: wave (role, qh, kh) finishes the tiles
   // ct = 2 qh, 2 qh + 1 and hands the other two to its partner (other qh).
   // lane holds X[key = 32 kh + 8 (e/4) + 4 hl + e%4][c = 32 ct + n32]
   constexpr int NH = C::NCT / 2;
-  float* ex = reinterpret_cast<float*>(smem_raw);   // [wave][NH][16][64]
+  // exchange area [wave][NH][16][64] floats: two waves per streamed tile
+  auto exw = [&](int w) {
+    uint16_t* b = ((w >> 2) ? qd1 : qd0) + ((w >> 1) & 1) * C::kTile;
+    return reinterpret_cast<float*>(b) + (w & 1) * NH * 16 * 64;
+  };
+  float* exo = exw(wave);
+  const float* exq = exw(wave ^ 2);
   // (qh is uniform per wave; both branches index acc statically)
   f32x16 fin[NH];
   if (qh == 0) {
@@ -572,23 +572,22 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(
     for (int x = 0; x < NH; ++x) {
       fin[x] = acc[x];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) ex[((wave * NH + x) * 16 + e) * 64 + lane] = acc[NH + x][e];
+      for (int e = 0; e < 16; ++e) exo[(x * 16 + e) * 64 + lane] = acc[NH + x][e];
     }
   } else {
 #pragma unroll
     for (int x = 0; x < NH; ++x) {
       fin[x] = acc[NH + x];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) ex[((wave * NH + x) * 16 + e) * 64 + lane] = acc[x][e];
+      for (int e = 0; e < 16; ++e) exo[(x * 16 + e) * 64 + lane] = acc[x][e];
     }
   }
   __syncthreads();
-  const int partner = wave ^ 2;
 #pragma unroll
   for (int x = 0; x < NH; ++x)
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const float sum = fin[x][e] + ex[((partner * NH + x) * 16 + e) * 64 + lane];
+      const float sum = fin[x][e] + exq[(x * 16 + e) * 64 + lane];
       fin[x][e] = role_dk ? scale * sum : sum;
     }
   if (linear) {
