@@ -430,6 +430,7 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t vsw[64 * D];   // V_j
   __shared__ __attribute__((aligned(16))) uint16_t dhs[D * D];    // dh_j^T, swizzled
   __shared__ __attribute__((aligned(16))) float dzs[2 * D];       // dz_j
+  __shared__ __attribute__((aligned(16))) float psh[4 * 16 * 64];  // P per (kh, qh)
 
   const uint32_t wg = xcd_remap(blockIdx.x, gridDim.x);
   const int j = wg % T;
@@ -508,33 +509,48 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(
       colv = e < cnt ? crow[e] : 0;
     }
     if (n + 1 < cnt) copy_q(n + 1, qn, ln);
-    f32x16 s = {};
-#pragma unroll
-    for (int cc = 0; cc < C::NCC; ++cc)
-      s = mfma32(as_bf16x8(ld16(qt + swz_off<D>(32 * qh + n32, 16 * cc + 8 * hl))), kf[cc], s);
-    // lane holds S[q = 32 qh + 8 (e/4) + 4 hl + e%4][key]: row statistics by 4
+    // dV role: S = Q K^T and P, handed to the dK wave of the same (kh, qh)
+    // through LDS; dK role meanwhile: dP = dO V^T.  Both result tiles have
+    // lane = key, element e = query 32 qh + 8 (e/4) + 4 hl + e%4.
     float pf[16];
+    f32x16 dp = {};
+    float* pw = psh + (wave & 3) * 16 * 64;   // [e / 4][lane][e % 4] of this (kh, qh)
+    if (!role_dk) {
+      f32x16 s = {};
 #pragma unroll
-    for (int e4 = 0; e4 < 4; ++e4) {
-      const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lt[32 * qh + 8 * e4 + 4 * hl]);
+      for (int cc = 0; cc < C::NCC; ++cc)
+        s = mfma32(as_bf16x8(ld16(qt + swz_off<D>(32 * qh + n32, 16 * cc + 8 * hl))), kf[cc], s);
 #pragma unroll
-      for (int x = 0; x < 4; ++x)
-        pf[4 * e4 + x] = __builtin_amdgcn_exp2f(__fmaf_rn(s[4 * e4 + x], sl2, -l4[x] * kLog2e));
-    }
-    if (tail_blk) {   // keys past valid_len: no probability mass
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lt[32 * qh + 8 * e4 + 4 * hl]);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) pf[e] = tail_key ? 0.f : pf[e];
-    }
-    if (role_dk) {
-      f32x16 dp = {};
+        for (int x = 0; x < 4; ++x)
+          pf[4 * e4 + x] = __builtin_amdgcn_exp2f(__fmaf_rn(s[4 * e4 + x], sl2, -l4[x] * kLog2e));
+      }
+      if (tail_blk) {   // keys past valid_len: no probability mass
+#pragma unroll
+        for (int e = 0; e < 16; ++e) pf[e] = tail_key ? 0.f : pf[e];
+      }
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4)
+        *reinterpret_cast<f32x4*>(&pw[(e4 * 64 + lane) * 4]) =
+            f32x4{pf[4 * e4], pf[4 * e4 + 1], pf[4 * e4 + 2], pf[4 * e4 + 3]};
+    } else {
 #pragma unroll
       for (int cc = 0; cc < C::NCC; ++cc)
         dp = mfma32(as_bf16x8(ld16(dt + swz_off<D>(32 * qh + n32, 16 * cc + 8 * hl))), vf[cc], dp);
+    }
+    // P visible to the dK waves: LDS writes done, then a barrier that does
+    // not wait for the next block's copies (the asm also keeps the compiler
+    // from moving LDS accesses across it)
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (role_dk) {
 #pragma unroll
       for (int e4 = 0; e4 < 4; ++e4) {
         const f32x4 d4 = *reinterpret_cast<const f32x4*>(&lt[64 + 32 * qh + 8 * e4 + 4 * hl]);
+        const f32x4 p4 = *reinterpret_cast<const f32x4*>(&pw[(e4 * 64 + lane) * 4]);
 #pragma unroll
-        for (int x = 0; x < 4; ++x) pf[4 * e4 + x] *= dp[4 * e4 + x] - d4[x];
+        for (int x = 0; x < 4; ++x) pf[4 * e4 + x] = p4[x] * (dp[4 * e4 + x] - d4[x]);
       }
     }
     const bf16x8 xb[2] = {cvt_bf16x8(pf), cvt_bf16x8(pf + 8)};
