@@ -148,6 +148,110 @@ def classify(scores: np.ndarray, k_c: int, k_n: int) -> np.ndarray:
 
 
 # ----------------------------------------------------------------------------
+# two-level (hierarchical) selection
+#
+# "Trainable Log-linear Sparse Attention for Efficient Diffusion Transformers"
+# (English abstract): top-k selection is done level by level, each level
+# selecting sparsely among the indices the coarser level kept, so that the
+# selection cost no longer grows with the full T x T compressed map.  The page
+# gives no further detail; the readings used here:
+#   * two levels: key blocks are grouped G at a time (the last group may hold
+#     fewer blocks); a group's coarse key is the mean of its valid tokens, the
+#     query side stays at block level;
+#   * coarse scores scale * qbar_i . kgbar_g (fp32, as the fine map);
+#   * under the total order (coarse score descending, group index ascending)
+#     the first `keep` groups are kept and the last n_g = floor(k_n / G)
+#     groups are negligible as a whole (the negligible share is never above
+#     the requested fraction, as in the flat split);
+#   * the candidates are the blocks of the kept groups; under the total order
+#     (fine score descending, block index ascending) their first k_c are
+#     critical (also when their group is among the negligible ones, which
+#     happens only when keep + n_g exceeds the number of groups);
+#   * every other block is marginal.
+# With G = 1 and keep = T this is exactly the flat split.
+# ----------------------------------------------------------------------------
+def num_groups(num_blocks: int, group: int) -> int:
+    return -(-num_blocks // group)
+
+
+def group_means(x: np.ndarray, valid_len: int, group: int, block: int = BLOCK) -> np.ndarray:
+    """Mean of the valid tokens of every group of `group` consecutive blocks.
+    x: [N, d] -> [ceil(T / group), d]."""
+    n, d = x.shape
+    t = n // block
+    tg = num_groups(t, group)
+    out = np.zeros((tg, d))
+    for g in range(tg):
+        lo, hi = g * group * block, min((g + 1) * group * block, valid_len, n)
+        out[g] = x[lo:hi].mean(axis=0)
+    return out
+
+
+def coarse_scores(q: np.ndarray, k: np.ndarray, valid_len: int, scale: float, group: int,
+                  block: int = BLOCK) -> np.ndarray:
+    """Coarse score map of one head: scale * qbar_i . kgbar_g in fp64, rounded
+    to fp32.  q, k: [N, d] -> [T, ceil(T / group)] float32."""
+    qb = block_means(q, valid_len, block)
+    kg = group_means(k, valid_len, group, block)
+    return (scale * (qb @ kg.T)).astype(np.float32)
+
+
+def hier_counts(num_blocks: int, group: int, keep: int, k_c: int, k_n: int):
+    """Checked parameters of the two-level split: returns (Tg, n_g).  The
+    smallest candidate set (the short last group among the kept ones) must
+    still hold k_c blocks; kept and negligible groups may overlap."""
+    if group < 1:
+        raise ValueError("group must be at least 1")
+    tg = num_groups(num_blocks, group)
+    n_g = k_n // group
+    last = num_blocks - (tg - 1) * group
+    if not 1 <= keep <= tg:
+        raise ValueError("keep must lie in [1, number of groups]")
+    if k_c > (keep - 1) * group + last:
+        raise ValueError("the kept groups hold fewer than k_c blocks")
+    return tg, n_g
+
+
+def _rank_desc(values: np.ndarray) -> np.ndarray:
+    """Indices sorted by value descending, index ascending; -0 equals +0; NaN
+    is an error."""
+    v = np.asarray(values, dtype=np.float32)
+    if np.isnan(v).any():
+        raise ValueError("NaN in compressed scores")
+    return np.lexsort((np.arange(v.size), -(v.astype(np.float64) + 0.0)))
+
+
+def classify_hier_row(coarse: np.ndarray, scores: np.ndarray, k_c: int, n_g: int, keep: int,
+                      group: int) -> np.ndarray:
+    """Two-level split of one row: coarse [Tg] and fine [T] fp32 scores ->
+    int8 [T] (+1 critical, 0 marginal, -1 negligible).  Only the fine scores
+    of the candidate blocks are read."""
+    t = np.asarray(scores).shape[0]
+    tg = np.asarray(coarse).shape[0]
+    order_g = _rank_desc(coarse)
+    kept = np.sort(order_g[:keep])
+    negl = order_g[tg - n_g:] if n_g > 0 else np.zeros(0, np.int64)
+    row = np.zeros(t, np.int8)
+    for g in negl:
+        row[g * group:min((g + 1) * group, t)] = -1
+    cand = np.concatenate([np.arange(g * group, min((g + 1) * group, t)) for g in kept])
+    sc = np.asarray(scores, dtype=np.float32)[cand]
+    row[cand[_rank_desc(sc)[:k_c]]] = 1
+    return row
+
+
+def classify_hier(coarse: np.ndarray, scores: np.ndarray, k_c: int, n_g: int, keep: int,
+                  group: int) -> np.ndarray:
+    """Two-level split of every row: coarse [..., T, Tg], fine [..., T, T]."""
+    c = np.asarray(coarse, dtype=np.float32)
+    s = np.asarray(scores, dtype=np.float32)
+    cf = c.reshape(-1, c.shape[-1])
+    sf = s.reshape(-1, s.shape[-1])
+    out = np.stack([classify_hier_row(a, b, k_c, n_g, keep, group) for a, b in zip(cf, sf)])
+    return out.reshape(s.shape)
+
+
+# ----------------------------------------------------------------------------
 # forward, one head
 # ----------------------------------------------------------------------------
 def key_block_states(k: np.ndarray, v: np.ndarray, valid_len: int, block: int = BLOCK):
@@ -322,13 +426,16 @@ def backward_head(q, k, v, w, do, mask, valid_len, scale, block: int = BLOCK, fw
 # whole problems [B, H, N, d]
 # ----------------------------------------------------------------------------
 def forward(q, k, v, w, frac_critical, frac_negligible, valid_len=None, scale=None,
-            mask=None, block: int = BLOCK, linear: str = "marginal", gate: float = 1.0):
+            mask=None, block: int = BLOCK, linear: str = "marginal", gate: float = 1.0,
+            select_group: int = 0, select_keep: int = 0):
     """Full SLA forward.  q, k, v: [B, H, N, d] fp64; w: [d, d].
 
     If ``mask`` ([B, H, T, T] int8) is given it is used as is; otherwise it is
-    built by the classifier.  ``linear`` / ``gate`` as in ``forward_head``.
-    Returns o, o_sparse, y, lse, den, mask, scores (scores only when the mask
-    was built here)."""
+    built by the classifier: the flat split, or with ``select_group`` > 0 the
+    two-level split (groups of ``select_group`` key blocks, ``select_keep``
+    kept per row).  ``linear`` / ``gate`` as in ``forward_head``.  Returns o,
+    o_sparse, y, lse, den, mask, scores and coarse (the maps only when the
+    mask was built here)."""
     bsz, nh, n, d = q.shape
     if n % block:
         raise ValueError("sequence length must be a multiple of the block size")
@@ -339,14 +446,23 @@ def forward(q, k, v, w, frac_critical, frac_negligible, valid_len=None, scale=No
     out = {name: np.zeros((bsz, nh, n, d)) for name in ("o", "o_sparse", "y")}
     out["lse"] = np.full((bsz, nh, n), -np.inf)
     out["den"] = np.zeros((bsz, nh, n))
-    scores = None
+    scores = coarse = None
     if mask is None:
         scores = np.zeros((bsz, nh, t, t), np.float32)
         mask = np.zeros((bsz, nh, t, t), np.int8)
+        if select_group > 0:
+            tg, n_g = hier_counts(t, select_group, select_keep, k_c, k_n)
+            coarse = np.zeros((bsz, nh, t, tg), np.float32)
         for b in range(bsz):
             for h in range(nh):
                 scores[b, h] = compressed_scores(q[b, h], k[b, h], valid_len, scale, block)
-                mask[b, h] = classify(scores[b, h], k_c, k_n)
+                if select_group > 0:
+                    coarse[b, h] = coarse_scores(q[b, h], k[b, h], valid_len, scale,
+                                                 select_group, block)
+                    mask[b, h] = classify_hier(coarse[b, h], scores[b, h], k_c, n_g,
+                                               select_keep, select_group)
+                else:
+                    mask[b, h] = classify(scores[b, h], k_c, k_n)
     for b in range(bsz):
         for h in range(nh):
             r = forward_head(q[b, h], k[b, h], v[b, h], w, mask[b, h], valid_len, scale,
@@ -355,6 +471,7 @@ def forward(q, k, v, w, frac_critical, frac_negligible, valid_len=None, scale=No
                 out[name][b, h] = r[name]
     out["mask"] = mask
     out["scores"] = scores
+    out["coarse"] = coarse
     return out
 
 

@@ -525,3 +525,140 @@ def test_global_linear_backward_matches_central_differences():
         wm[a_, b_] -= eps
         fd = (loss(q, k, v, wp) - loss(q, k, v, wm)) / (2 * eps)
         assert abs(fd - g["dw"][a_, b_]) < 1e-6 * max(1.0, abs(fd))
+
+
+# ---------------------------------------------------------------------------
+# two-level (hierarchical) selection
+# ---------------------------------------------------------------------------
+def _sorted_hier(coarse, scores, k_c, n_g, keep, group):
+    """Brute force with Python's sorted() on tuples, written independently."""
+    t, tg = len(scores), len(coarse)
+    go = sorted(range(tg), key=lambda g: (-(float(coarse[g]) + 0.0), g))
+    kept, negl = set(go[:keep]), set(go[tg - n_g:]) if n_g else set()
+    out = [0] * t
+    for j in range(t):
+        if j // group in negl:
+            out[j] = -1
+    cand = [j for j in range(t) if j // group in kept]
+    for j in sorted(cand, key=lambda j: (-(float(scores[j]) + 0.0), j))[:k_c]:
+        out[j] = 1
+    return out
+
+
+@pytest.mark.parametrize("kind", ["random", "integers", "signed_zeros"])
+@pytest.mark.parametrize("t,group", [(37, 4), (40, 8), (9, 1), (64, 16)])
+def test_hier_classifier_matches_sorted_brute_force(kind, t, group):
+    rng = np.random.default_rng(t * 31 + group)
+    tg = orc.num_groups(t, group)
+    rows = 12
+    if kind == "random":
+        s = rng.standard_normal((rows, t)).astype(np.float32)
+        c = rng.standard_normal((rows, tg)).astype(np.float32)
+    elif kind == "integers":
+        s = rng.integers(-2, 3, size=(rows, t)).astype(np.float32)
+        c = rng.integers(-2, 3, size=(rows, tg)).astype(np.float32)
+    else:
+        s = np.where(rng.random((rows, t)) < 0.5, np.float32(0.0), np.float32(-0.0))
+        c = np.where(rng.random((rows, tg)) < 0.5, np.float32(0.0), np.float32(-0.0))
+        s[:, ::5] = 1.0
+    last = t - (tg - 1) * group
+    for keep in sorted({1, max(1, tg // 3), tg}):
+        for k_n in (0, group, 3 * group + 1):
+            n_g = k_n // group
+            if n_g > tg:
+                continue
+            for k_c in (0, 1, (keep - 1) * group + last):
+                got = orc.classify_hier(c, s, k_c, n_g, keep, group)
+                for r in range(rows):
+                    assert got[r].tolist() == _sorted_hier(c[r], s[r], k_c, n_g, keep, group)
+                    assert (got[r] == 1).sum() == k_c
+
+
+def test_hier_with_unit_groups_and_all_kept_is_the_flat_split():
+    rng = np.random.default_rng(5)
+    t = 33
+    for s in (rng.standard_normal((16, t)).astype(np.float32),
+              rng.integers(-2, 3, size=(16, t)).astype(np.float32)):
+        for k_c, k_n in [(0, 0), (4, 7), (33, 0), (0, 33), (10, 23)]:
+            tg, n_g = orc.hier_counts(t, 1, t, k_c, k_n)
+            assert (tg, n_g) == (t, k_n)
+            np.testing.assert_array_equal(orc.classify_hier(s, s, k_c, n_g, t, 1),
+                                          orc.classify(s, k_c, k_n))
+
+
+def test_hier_with_all_groups_kept_picks_the_flat_critical_set():
+    rng = np.random.default_rng(6)
+    t, group = 50, 8
+    s = rng.standard_normal((10, t)).astype(np.float32)
+    c = rng.standard_normal((10, orc.num_groups(t, group))).astype(np.float32)
+    for k_c in (1, 7, 50):
+        got = orc.classify_hier(c, s, k_c, 0, orc.num_groups(t, group), group)
+        flat = orc.classify(s, k_c, 0)
+        np.testing.assert_array_equal(got == 1, flat == 1)
+
+
+def test_hier_invariants_on_workload_inputs():
+    inp = make_inputs(1, 2, 64 * 48, 64, (4, 12, 64), 64 * 48 - 10, seed=3, with_grad=False)
+    q, k = orc.decode_bf16(inp["q"]), orc.decode_bf16(inp["k"])
+    vl, t, group, keep = 64 * 48 - 10, 48, 5, 3
+    k_c, k_n, _ = orc.block_counts(t, 0.2, 0.3)
+    tg, n_g = orc.hier_counts(t, group, keep, k_c, k_n)
+    for h in range(2):
+        c = orc.coarse_scores(q[0, h], k[0, h], vl, 0.125, group)
+        s = orc.compressed_scores(q[0, h], k[0, h], vl, 0.125)
+        m = orc.classify_hier(c, s, k_c, n_g, keep, group)
+        for i in range(t):
+            row = m[i]
+            assert (row == 1).sum() == k_c
+            crit_groups = set(np.flatnonzero(row == 1) // group)
+            negl = np.flatnonzero(row == -1)
+            negl_groups = set(negl // group)
+            # negligible blocks are whole groups, n_g of them, never kept ones
+            assert len(negl_groups) == n_g
+            assert sum(min(group, t - g * group) for g in negl_groups) == negl.size
+            assert len(crit_groups) <= keep and not crit_groups & negl_groups
+            if negl_groups and crit_groups:
+                assert max(c[i][list(negl_groups)]) <= min(c[i][list(crit_groups)])
+
+
+def test_group_means_closed_forms():
+    n, d, vl, group = 64 * 10, 3, 64 * 10 - 20, 4
+    c = np.array([1.0, -2.0, 0.5])
+    x = np.arange(n, dtype=np.float64)[:, None] * c[None, :]
+    g = orc.group_means(x, vl, group)
+    assert g.shape == (3, d)
+    for i, (lo, hi) in enumerate([(0, 256), (256, 512), (512, vl)]):
+        np.testing.assert_allclose(g[i], (lo + hi - 1) / 2.0 * c, rtol=1e-15)
+    # unit groups are the block means, so the coarse map is the fine one
+    q = _rand((n, d), 41)
+    np.testing.assert_array_equal(orc.group_means(q, vl, 1), orc.block_means(q, vl))
+    np.testing.assert_array_equal(orc.coarse_scores(q, q, vl, 0.5, 1),
+                                  orc.compressed_scores(q, q, vl, 0.5))
+
+
+def test_hier_counts_rejects_impossible_splits():
+    with pytest.raises(ValueError):
+        orc.hier_counts(40, 8, 0, 1, 0)          # nothing kept
+    assert orc.hier_counts(40, 8, 4, 1, 16) == (5, 2)   # kept and negligible may overlap
+    with pytest.raises(ValueError):
+        orc.hier_counts(37, 8, 2, 14, 0)         # the short last group leaves 13 candidates
+    assert orc.hier_counts(37, 8, 2, 13, 0) == (5, 0)
+
+
+def test_forward_with_two_level_selection_uses_its_mask():
+    inp = make_inputs(1, 2, 64 * 12, 16, (3, 16, 16), 64 * 12 - 7, seed=8, with_grad=False)
+    x = {k_: orc.decode_bf16(inp[k_]) for k_ in ("q", "k", "v", "w")}
+    vl = 64 * 12 - 7
+    r = orc.forward(x["q"], x["k"], x["v"], x["w"], 0.25, 0.34, valid_len=vl,
+                    select_group=3, select_keep=2)
+    k_c, k_n, _ = orc.block_counts(12, 0.25, 0.34)
+    _, n_g = orc.hier_counts(12, 3, 2, k_c, k_n)
+    np.testing.assert_array_equal(r["mask"],
+                                  orc.classify_hier(r["coarse"], r["scores"], k_c, n_g, 2, 3))
+    ref = orc.forward(x["q"], x["k"], x["v"], x["w"], 0.0, 0.0, valid_len=vl, mask=r["mask"])
+    np.testing.assert_array_equal(r["o"], ref["o"])
+    # unit groups, everything kept: the flat forward
+    a = orc.forward(x["q"], x["k"], x["v"], x["w"], 0.25, 0.34, valid_len=vl,
+                    select_group=1, select_keep=12)
+    b = orc.forward(x["q"], x["k"], x["v"], x["w"], 0.25, 0.34, valid_len=vl)
+    np.testing.assert_array_equal(a["mask"], b["mask"])
