@@ -40,6 +40,21 @@
  * scaled by a gate g in [0, 1]: O[r] = O_s[r] + g Y[r] W^T.  The mask still
  * selects the critical blocks of the sparse branch.
  *
+ * Two-level selection (select_group = G >= 1), after the abstract of
+ * "Trainable Log-linear Sparse Attention for Efficient Diffusion Transformers"
+ * (top-k chosen level by level, each level looking only at what the coarser
+ * level kept): key blocks are grouped G at a time (Tg = ceil(T / G) groups,
+ * the last possibly shorter); a group's coarse key kgbar_g is the mean of its
+ * valid rows, and per row i, under the order (C_ig descending, g ascending)
+ * with C_ig = s * qbar_i . kgbar_g (fp32):
+ *   the first select_keep groups are kept, the last n_g = floor(k_n / G)
+ *   groups are negligible (every block in them -> -1), and among the blocks of
+ *   the kept groups, under the order (S_ij descending, j ascending), the first
+ *   k_c -> +1 critical (also inside a negligible group); the rest -> 0.
+ * Only the kept groups' fine scores are computed, so the selection costs
+ * T * (Tg + select_keep * G) scores instead of T * T.  G = 1 with
+ * select_keep = T is the flat rule above.
+ *
  * Conventions for every entry point below:
  *  - Tensors are contiguous, row-major.  Q, K, V, O, dO are bf16 [B, H, N, d]
  *    ("BHND"); W is bf16 [d, d]; dQ, dK, dV, dW are fp32.  Device pointers must
@@ -120,6 +135,11 @@ typedef struct sla_config {
   void* stage_events;
   int32_t linear_mode;     /* SLA_LINEAR_MARGINAL (0) or SLA_LINEAR_GLOBAL */
   float linear_gate;       /* SLA_LINEAR_GLOBAL only: g in [0, 1]; ignored otherwise */
+  int32_t select_group;    /* 0: flat selection; G >= 1: two-level selection with groups of
+                              G key blocks (SLA_MASK_COMPUTE only) */
+  int32_t select_keep;     /* two-level only: groups kept per query block, in [1, Tg]; the
+                              kept groups must hold k_c blocks even when the shorter last
+                              group is among them */
 } sla_config;
 
 /* k_c, k_n, k_m (= T - k_c - k_n) for the configuration.  Host only. */
@@ -174,6 +194,19 @@ sla_status sla_pool_scores(const sla_config* cfg, const void* q, const void* k, 
 /* Classification alone: scores fp32 [B,H,T,T] (in, finite) -> mask int8
    [B,H,T,T] (out), by the rule above.  Uses cfg's sizes and fractions only. */
 sla_status sla_classify(const sla_config* cfg, const float* scores, int8_t* mask, void* stream);
+
+/* Two-level selection (cfg->select_group >= 1): the coarse score map alone,
+   coarse fp32 [B,H,T,Tg] (out), bit-identical to the map the forward ranks. */
+sla_status sla_coarse_scores(const sla_config* cfg, const void* q, const void* k, float* coarse,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Two-level classification alone (cfg->select_group >= 1): coarse fp32
+   [B,H,T,Tg] and scores fp32 [B,H,T,T] (in, finite; only the entries of kept
+   groups are read) -> mask int8 [B,H,T,T] (out), by the two-level rule.  With
+   the maps of sla_coarse_scores and sla_pool_scores it reproduces the mask of
+   sla_forward exactly. */
+sla_status sla_classify_hier(const sla_config* cfg, const float* coarse, const float* scores,
+                             int8_t* mask, void* stream);
 
 /* Static description of a status code. */
 const char* sla_status_string(sla_status status);

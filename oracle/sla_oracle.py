@@ -200,8 +200,8 @@ def hier_counts(num_blocks: int, group: int, keep: int, k_c: int, k_n: int):
     """Checked parameters of the two-level split: returns (Tg, n_g).  The
     smallest candidate set (the short last group among the kept ones) must
     still hold k_c blocks; kept and negligible groups may overlap."""
-    if group < 1:
-        raise ValueError("group must be at least 1")
+    if not 1 <= group <= num_blocks:
+        raise ValueError("group must lie in [1, T]")
     tg = num_groups(num_blocks, group)
     n_g = k_n // group
     last = num_blocks - (tg - 1) * group

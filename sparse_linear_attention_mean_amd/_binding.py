@@ -29,8 +29,8 @@ STAGES = ("kv_state", "pool_q", "classify", "aggregate", "attention", "bwd_pre",
 
 EXPORTED = (
     "sla_block_counts", "sla_workspace_size", "sla_saved_size", "sla_saved_offsets",
-    "sla_forward", "sla_backward", "sla_pool_scores", "sla_classify", "sla_status_string",
-    "sla_last_error",
+    "sla_forward", "sla_backward", "sla_pool_scores", "sla_classify", "sla_coarse_scores",
+    "sla_classify_hier", "sla_status_string", "sla_last_error",
 )
 
 
@@ -49,6 +49,8 @@ class SlaConfig(ctypes.Structure):
         ("stage_events", ctypes.c_void_p),
         ("linear_mode", ctypes.c_int32),
         ("linear_gate", ctypes.c_float),
+        ("select_group", ctypes.c_int32),
+        ("select_keep", ctypes.c_int32),
     ]
 
 
@@ -75,6 +77,8 @@ def _load() -> ctypes.CDLL:
                                         sz, vp]),
         "sla_pool_scores": (ctypes.c_int, [cfgp, vp, vp, vp, vp, sz, vp]),
         "sla_classify": (ctypes.c_int, [cfgp, vp, vp, vp]),
+        "sla_coarse_scores": (ctypes.c_int, [cfgp, vp, vp, vp, vp, sz, vp]),
+        "sla_classify_hier": (ctypes.c_int, [cfgp, vp, vp, vp, vp]),
         "sla_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "sla_last_error": (ctypes.c_char_p, []),
     }
@@ -90,10 +94,11 @@ lib = _load()
 
 def make_config(batch, heads, seq_len, head_dim, frac_critical, frac_negligible, valid_len=0,
                 softmax_scale=0.0, mask_mode=SLA_MASK_COMPUTE, stage_events=None,
-                linear_mode=SLA_LINEAR_MARGINAL, linear_gate=1.0) -> SlaConfig:
+                linear_mode=SLA_LINEAR_MARGINAL, linear_gate=1.0, select_group=0,
+                select_keep=0) -> SlaConfig:
     return SlaConfig(batch, heads, seq_len, head_dim, valid_len, 64, frac_critical,
                      frac_negligible, softmax_scale, mask_mode, stage_events, linear_mode,
-                     linear_gate)
+                     linear_gate, select_group, select_keep)
 
 
 def _check(status: int) -> None:
@@ -153,6 +158,17 @@ def sla_pool_scores(cfg, q, k, scores, workspace, stream=None) -> None:
 
 def sla_classify(cfg, scores, mask, stream=None) -> None:
     _check(lib.sla_classify(ctypes.byref(cfg), _ptr(scores), _ptr(mask), _stream(stream)))
+
+
+def sla_coarse_scores(cfg, q, k, coarse, workspace, stream=None) -> None:
+    _check(lib.sla_coarse_scores(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(coarse),
+                                 _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                 _stream(stream)))
+
+
+def sla_classify_hier(cfg, coarse, scores, mask, stream=None) -> None:
+    _check(lib.sla_classify_hier(ctypes.byref(cfg), _ptr(coarse), _ptr(scores), _ptr(mask),
+                                 _stream(stream)))
 
 
 def sla_status_string(status: int) -> str:

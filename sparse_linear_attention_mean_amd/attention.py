@@ -31,10 +31,12 @@ class SlaProblem:
     @classmethod
     def create(cls, batch, heads, seq_len, head_dim, frac_critical, frac_negligible,
                valid_len=0, softmax_scale=0.0, mask_mode=B.SLA_MASK_COMPUTE, device="cuda",
-               linear_mode=B.SLA_LINEAR_MARGINAL, linear_gate=1.0):
+               linear_mode=B.SLA_LINEAR_MARGINAL, linear_gate=1.0, select_group=0,
+               select_keep=0):
         cfg = B.make_config(batch, heads, seq_len, head_dim, frac_critical, frac_negligible,
                             valid_len, softmax_scale, mask_mode, linear_mode=linear_mode,
-                            linear_gate=linear_gate)
+                            linear_gate=linear_gate, select_group=select_group,
+                            select_keep=select_keep)
         ws = B.sla_workspace_size(cfg)
         sv = B.sla_saved_size(cfg)
         if ws == 0 or sv == 0:
@@ -83,6 +85,18 @@ class SlaProblem:
         B.sla_pool_scores(self.cfg, q, k, scores, self.workspace, stream)
         return scores
 
+    def num_groups(self) -> int:
+        g = self.cfg.select_group
+        return -(-self.num_blocks // g) if g > 0 else 0
+
+    def coarse_scores(self, q, k, stream=None):
+        """Two-level selection only: the coarse map fp32 [B, H, T, Tg]."""
+        c = self.cfg
+        coarse = torch.empty((c.batch, c.heads, self.num_blocks, self.num_groups()),
+                             dtype=torch.float32, device=self.device)
+        B.sla_coarse_scores(self.cfg, q, k, coarse, self.workspace, stream)
+        return coarse
+
     def saved_views(self):
         """Views into the saved buffer: lse, den (fp32 [B,H,N]), y (bf16 [B,H,N,d])."""
         off = B.sla_saved_offsets(self.cfg)
@@ -99,4 +113,13 @@ def classify(cfg: B.SlaConfig, scores: torch.Tensor, stream=None) -> torch.Tenso
     t = cfg.seq_len // 64
     mask = torch.empty((cfg.batch, cfg.heads, t, t), dtype=torch.int8, device=scores.device)
     B.sla_classify(cfg, scores, mask, stream)
+    return mask
+
+
+def classify_hier(cfg: B.SlaConfig, coarse: torch.Tensor, scores: torch.Tensor,
+                  stream=None) -> torch.Tensor:
+    """Two-level split of given coarse [B, H, T, Tg] and fine [B, H, T, T] maps."""
+    t = cfg.seq_len // 64
+    mask = torch.empty((cfg.batch, cfg.heads, t, t), dtype=torch.int8, device=scores.device)
+    B.sla_classify_hier(cfg, coarse, scores, mask, stream)
     return mask

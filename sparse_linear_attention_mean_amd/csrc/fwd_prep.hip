@@ -310,51 +310,14 @@ __device__ __forceinline__ uint32_t descending_code(float s) {
   return ~asc;
 }
 
-__global__ __launch_bounds__(256) void classify_kernel(const float* __restrict__ scores,
-                                                       int8_t* __restrict__ mask,
-                                                       int32_t* __restrict__ lut,
-                                                       int32_t* __restrict__ lut_cnt,
-                                                       uint32_t* __restrict__ rbits, int T,
-                                                       int Tp, int kc, int kn) {
-  __shared__ unsigned long long keys[kMaxT];
-  __shared__ int8_t cls[kMaxT];
-  const int i = blockIdx.x;
-  const long long bh = blockIdx.y;
+// Writes a classified row cls[0..T) (in LDS, complete): the mask row, and
+// optionally the ascending critical list with its length and the marginal bits
+// of the row (word-major).  Called by all 256 threads of the workgroup.
+__device__ void emit_row(const int8_t* cls, int8_t* __restrict__ mask, int32_t* __restrict__ lut,
+                         int32_t* __restrict__ lut_cnt, uint32_t* __restrict__ rbits, long long bh,
+                         int i, int T, int Tp) {
   const int tid = threadIdx.x;
   const int words = Tp / 32;
-  if (i >= T) {
-    if (rbits)
-      for (int w = tid; w < words; w += 256) rbits[(bh * words + w) * Tp + i] = 0u;
-    return;
-  }
-  int n2 = 1;
-  while (n2 < T) n2 <<= 1;
-  const float* row = scores + (bh * T + i) * T;
-  for (int j = tid; j < n2; j += 256)
-    keys[j] = (j < T) ? ((static_cast<unsigned long long>(descending_code(row[j])) << 32) |
-                         static_cast<unsigned long long>(j))
-                      : ~0ull;
-  __syncthreads();
-  for (int size = 2; size <= n2; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int t = tid; t < n2 / 2; t += 256) {
-        const int lo = 2 * t - (t & (stride - 1));
-        const int hi = lo + stride;
-        const bool up = ((lo & size) == 0);
-        const unsigned long long a = keys[lo], b = keys[hi];
-        if ((a > b) == up) {
-          keys[lo] = b;
-          keys[hi] = a;
-        }
-      }
-      __syncthreads();
-    }
-  }
-  for (int p = tid; p < T; p += 256) {
-    const int j = static_cast<int>(keys[p] & 0xffffffffull);
-    cls[j] = p < kc ? 1 : (p >= T - kn ? -1 : 0);
-  }
-  __syncthreads();
   int8_t* mrow = mask + (bh * T + i) * T;
   for (int j = tid; j < T; j += 256) mrow[j] = cls[j];
   if (tid < 64) {
@@ -384,6 +347,207 @@ __global__ __launch_bounds__(256) void classify_kernel(const float* __restrict__
       }
     }
   }
+}
+
+// In-place bitonic sort (ascending) of keys[0, n2) in LDS, n2 a power of two;
+// called by all 256 threads, ends synchronised.
+__device__ void bitonic_sort(unsigned long long* keys, int n2) {
+  const int tid = threadIdx.x;
+  for (int size = 2; size <= n2; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int t = tid; t < n2 / 2; t += 256) {
+        const int lo = 2 * t - (t & (stride - 1));
+        const int hi = lo + stride;
+        const bool up = ((lo & size) == 0);
+        const unsigned long long a = keys[lo], b = keys[hi];
+        if ((a > b) == up) {
+          keys[lo] = b;
+          keys[hi] = a;
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void classify_kernel(const float* __restrict__ scores,
+                                                       int8_t* __restrict__ mask,
+                                                       int32_t* __restrict__ lut,
+                                                       int32_t* __restrict__ lut_cnt,
+                                                       uint32_t* __restrict__ rbits, int T,
+                                                       int Tp, int kc, int kn) {
+  __shared__ unsigned long long keys[kMaxT];
+  __shared__ int8_t cls[kMaxT];
+  const int i = blockIdx.x;
+  const long long bh = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int words = Tp / 32;
+  if (i >= T) {
+    if (rbits)
+      for (int w = tid; w < words; w += 256) rbits[(bh * words + w) * Tp + i] = 0u;
+    return;
+  }
+  int n2 = 1;
+  while (n2 < T) n2 <<= 1;
+  const float* row = scores + (bh * T + i) * T;
+  for (int j = tid; j < n2; j += 256)
+    keys[j] = (j < T) ? ((static_cast<unsigned long long>(descending_code(row[j])) << 32) |
+                         static_cast<unsigned long long>(j))
+                      : ~0ull;
+  __syncthreads();
+  bitonic_sort(keys, n2);
+  for (int p = tid; p < T; p += 256) {
+    const int j = static_cast<int>(keys[p] & 0xffffffffull);
+    cls[j] = p < kc ? 1 : (p >= T - kn ? -1 : 0);
+  }
+  __syncthreads();
+  emit_row(cls, mask, lut, lut_cnt, rbits, bh, i, T, Tp);
+}
+
+// ---------------------------------------------------------------------------
+// Two-level selection, after the abstract of "Trainable Log-linear Sparse
+// Attention for Efficient Diffusion Transformers": key blocks are grouped G
+// at a time, a group's coarse key is the mean of its valid rows, the first
+// `keep` groups by coarse score (descending, index ascending) are kept and the
+// last n_g negligible; only the blocks of the kept groups get fine scores, and
+// the first k_c of them (fine score descending, index ascending) are critical.
+// ---------------------------------------------------------------------------
+// kgbar[g] = sum over the blocks j of group g of n_j kbar[j] / sum n_j, with
+// n_j the valid rows of block j (blocks ascending, fp32).
+__global__ __launch_bounds__(256) void group_means_kernel(const float* __restrict__ kbar,
+                                                          float* __restrict__ kgbar, int T, int D,
+                                                          int G, int Tg, int L) {
+  const long long bh = blockIdx.y;
+  const int e = blockIdx.x * 256 + threadIdx.x;   // (group, column)
+  if (e >= Tg * D) return;
+  const int g = e / D, a = e % D;
+  const int j1 = min((g + 1) * G, T);
+  float acc = 0.f;
+  int n = 0;
+  for (int j = g * G; j < j1; ++j) {
+    const int nj = min(kBlock, L - j * kBlock);   // >= 1: only the last block is short
+    acc = __fmaf_rn(static_cast<float>(nj), kbar[(bh * T + j) * D + a], acc);
+    n += nj;
+  }
+  kgbar[(bh * Tg + g) * D + a] = __fdiv_rn(acc, static_cast<float>(n));
+}
+
+// s * (q . k) over D entries, accumulated in index order with fused
+// multiply-adds (the order of the compressed score map)
+__device__ __forceinline__ float ordered_score(const float* q, const float* __restrict__ k, int D,
+                                               float scale) {
+  float acc = 0.f;
+  for (int a = 0; a < D; a += 4) {
+    const f32x4 qv = *reinterpret_cast<const f32x4*>(q + a);
+    const f32x4 kv = *reinterpret_cast<const f32x4*>(k + a);
+    acc = __fmaf_rn(qv[0], kv[0], acc);
+    acc = __fmaf_rn(qv[1], kv[1], acc);
+    acc = __fmaf_rn(qv[2], kv[2], acc);
+    acc = __fmaf_rn(qv[3], kv[3], acc);
+  }
+  return __fmul_rn(acc, scale);
+}
+
+// coarse map alone: one workgroup per (row i, bh)
+__global__ __launch_bounds__(256) void coarse_scores_kernel(const float* __restrict__ qbar,
+                                                            const float* __restrict__ kgbar,
+                                                            float* __restrict__ coarse, int T,
+                                                            int D, int Tg, float scale) {
+  __shared__ __attribute__((aligned(16))) float qs[128];
+  const int i = blockIdx.x;
+  const long long bh = blockIdx.y;
+  for (int a = threadIdx.x; a < D; a += 256) qs[a] = qbar[(bh * T + i) * D + a];
+  __syncthreads();
+  for (int g = threadIdx.x; g < Tg; g += 256)
+    coarse[(bh * T + i) * Tg + g] = ordered_score(qs, kgbar + (bh * Tg + g) * D, D, scale);
+}
+
+// one workgroup per row (bh, i): coarse keys (computed, or read from
+// coarse_in) sorted to pick the kept and negligible groups, then the fine keys
+// of the candidate blocks (computed, or read from scores_in) sorted to pick the
+// critical ones; the row is written like the flat classifier's.
+__global__ __launch_bounds__(256) void classify_hier_kernel(
+    const float* __restrict__ qbar, const float* __restrict__ kgbar,
+    const float* __restrict__ kbar, const float* __restrict__ coarse_in,
+    const float* __restrict__ scores_in, int8_t* __restrict__ mask, int32_t* __restrict__ lut,
+    int32_t* __restrict__ lut_cnt, uint32_t* __restrict__ rbits, int T, int Tp, int D, int G,
+    int Tg, int keep, int ng, int kc, float scale) {
+  __shared__ unsigned long long keys[kMaxT];
+  __shared__ int8_t cls[kMaxT];
+  __shared__ uint8_t gflag[kMaxT];   // bit 0: kept, bit 1: negligible
+  __shared__ int kpre[kMaxT];        // kept groups before group g
+  __shared__ __attribute__((aligned(16))) float qs[128];
+  const int i = blockIdx.x;
+  const long long bh = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int words = Tp / 32;
+  if (i >= T) {
+    if (rbits)
+      for (int w = tid; w < words; w += 256) rbits[(bh * words + w) * Tp + i] = 0u;
+    return;
+  }
+  const bool given = coarse_in != nullptr;
+  if (!given)
+    for (int a = tid; a < D; a += 256) qs[a] = qbar[(bh * T + i) * D + a];
+  __syncthreads();
+  // ---- level 1: groups
+  int n2 = 1;
+  while (n2 < Tg) n2 <<= 1;
+  for (int g = tid; g < n2; g += 256) {
+    unsigned long long key = ~0ull;
+    if (g < Tg) {
+      const float c = given ? coarse_in[(bh * T + i) * Tg + g]
+                            : ordered_score(qs, kgbar + (bh * Tg + g) * D, D, scale);
+      key = (static_cast<unsigned long long>(descending_code(c)) << 32) |
+            static_cast<unsigned long long>(g);
+    }
+    keys[g] = key;
+  }
+  __syncthreads();
+  bitonic_sort(keys, n2);
+  for (int p = tid; p < Tg; p += 256) {
+    const int g = static_cast<int>(keys[p] & 0xffffffffull);
+    gflag[g] = static_cast<uint8_t>((p < keep ? 1 : 0) | (p >= Tg - ng ? 2 : 0));
+  }
+  __syncthreads();
+  // candidates in block order: kept groups ascending (only the last group can
+  // be short, so a kept group's first candidate slot is G times the kept
+  // groups before it)
+  if (tid < 64) {
+    int cnt = 0;
+    for (int base = 0; base < Tg; base += 64) {
+      const int g = base + tid;
+      const bool f = g < Tg && (gflag[g] & 1);
+      const unsigned long long bal = __ballot(f);
+      if (g < Tg) kpre[g] = cnt + __popcll(bal & ((1ull << tid) - 1ull));
+      cnt += __popcll(bal);
+    }
+  }
+  __syncthreads();
+  // ---- level 2: fine keys of the candidate blocks (keep groups of G blocks,
+  // less the missing blocks of the short last group when it is kept)
+  const int ncand = keep * G - ((gflag[Tg - 1] & 1) ? Tg * G - T : 0);
+  int m2 = 1;
+  while (m2 < ncand) m2 <<= 1;
+  for (int p = tid; p < m2; p += 256) keys[p] = ~0ull;
+  __syncthreads();
+  for (int j = tid; j < T; j += 256) {
+    const int g = j / G;
+    if (gflag[g] & 1) {
+      const float sc = given ? scores_in[(bh * T + i) * T + j]
+                             : ordered_score(qs, kbar + (bh * T + j) * D, D, scale);
+      keys[kpre[g] * G + (j - g * G)] =
+          (static_cast<unsigned long long>(descending_code(sc)) << 32) |
+          static_cast<unsigned long long>(j);
+    }
+  }
+  __syncthreads();
+  bitonic_sort(keys, m2);
+  for (int j = tid; j < T; j += 256) cls[j] = (gflag[j / G] & 2) ? -1 : 0;
+  __syncthreads();
+  for (int p = tid; p < kc; p += 256) cls[static_cast<int>(keys[p] & 0xffffffffull)] = 1;
+  __syncthreads();
+  emit_row(cls, mask, lut, lut_cnt, rbits, bh, i, T, Tp);
 }
 
 // ---------------------------------------------------------------------------
@@ -495,6 +659,31 @@ hipError_t launch_classify(const Dims& d, const float* scores, int8_t* mask, int
   const int rows = rbits ? d.Tp : d.T;
   hipLaunchKernelGGL(classify_kernel, dim3(rows, static_cast<unsigned>(d.BH())), dim3(256), 0, s,
                      scores, mask, lut, lut_cnt, rbits, d.T, d.Tp, d.kc, d.kn);
+  return hipGetLastError();
+}
+
+hipError_t launch_group_means(const Dims& d, const float* kbar, float* kgbar, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>((d.Tg * d.D + 255) / 256), static_cast<unsigned>(d.BH()));
+  hipLaunchKernelGGL(group_means_kernel, grid, dim3(256), 0, s, kbar, kgbar, d.T, d.D, d.G, d.Tg,
+                     d.L);
+  return hipGetLastError();
+}
+
+hipError_t launch_coarse_scores(const Dims& d, const float* qbar, const float* kgbar,
+                                float* coarse, hipStream_t s) {
+  hipLaunchKernelGGL(coarse_scores_kernel, dim3(d.T, static_cast<unsigned>(d.BH())), dim3(256), 0,
+                     s, qbar, kgbar, coarse, d.T, d.D, d.Tg, d.scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_classify_hier(const Dims& d, const float* qbar, const float* kgbar,
+                                const float* kbar, const float* coarse_in, const float* scores_in,
+                                int8_t* mask, int32_t* lut, int32_t* lut_cnt, uint32_t* rbits,
+                                hipStream_t s) {
+  const int rows = rbits ? d.Tp : d.T;
+  hipLaunchKernelGGL(classify_hier_kernel, dim3(rows, static_cast<unsigned>(d.BH())), dim3(256), 0,
+                     s, qbar, kgbar, kbar, coarse_in, scores_in, mask, lut, lut_cnt, rbits, d.T,
+                     d.Tp, d.D, d.G, d.Tg, d.keep, d.ng, d.kc, d.scale);
   return hipGetLastError();
 }
 

@@ -88,6 +88,28 @@ sla_status make_dims(const sla_config* cfg, Dims* d) {
   d->mask_mode = cfg->mask_mode;
   d->global = global;
   d->gate = global ? cfg->linear_gate : 1.0f;
+  // two-level selection: groups of G key blocks, `keep` kept per row, the last
+  // floor(k_n / G) negligible; the kept groups must hold k_c blocks even when
+  // the short last group is one of them
+  d->G = d->Tg = d->keep = d->ng = 0;
+  if (cfg->select_group != 0) {
+    const int G = cfg->select_group;
+    if (G < 1 || G > T)
+      return fail(SLA_ERR_INVALID_ARGUMENT, "select_group must lie in [1, T] (got %d)", G);
+    const int Tg = (T + G - 1) / G;
+    const int last = T - (Tg - 1) * G;
+    if (cfg->select_keep < 1 || cfg->select_keep > Tg)
+      return fail(SLA_ERR_INVALID_ARGUMENT, "select_keep must lie in [1, %d] (got %d)", Tg,
+                  cfg->select_keep);
+    if (kc > (cfg->select_keep - 1) * G + last)
+      return fail(SLA_ERR_INVALID_ARGUMENT,
+                  "the kept groups hold fewer than k_c = %d blocks (select_keep %d, group %d)", kc,
+                  cfg->select_keep, G);
+    d->G = G;
+    d->Tg = Tg;
+    d->keep = cfg->select_keep;
+    d->ng = kn / G;
+  }
   return SLA_OK;
 }
 
@@ -139,6 +161,7 @@ WorkspaceLayout workspace_layout(const Dims& d) {
   };
   w.qbar = take(BH * d.T * d.D * 4);
   w.kbar = take(BH * d.T * d.D * 4);
+  w.kgbar = take(BH * (d.G > 0 ? d.Tg : 1) * d.D * 4);
   w.scores = take(BH * d.T * d.T * 4);
   w.lut = take(BH * d.T * d.T * 4);
   w.lut_cnt = take(BH * d.T * 4);
@@ -251,7 +274,8 @@ sla_status sla_forward(const sla_config* cfg, const void* q, const void* k, cons
   const bool given = d.mask_mode == SLA_MASK_GIVEN;
   // all blocks critical: plain dense attention, no classification, no linear branch
   const bool dense = !given && d.kc == d.T && !d.global;
-  const bool linear = d.global || given || d.km > 0;
+  // (the two-level split can leave marginal blocks even when the flat one has none)
+  const bool linear = d.global || given || ((d.km > 0 || d.G > 0) && d.kc < d.T);
   uint32_t* bits = d.global ? nullptr : rbits;   // the global branch needs no marginal bits
 
   if (dense) {
@@ -268,13 +292,24 @@ sla_status sla_forward(const sla_config* cfg, const void* q, const void* k, cons
       SLA_CHECK(launched(launch_pool(d, q16, reinterpret_cast<float*>(ws + wl.qbar), s), "pool_q"));
       SLA_CHECK(stg.end(SLA_STAGE_POOL_Q));
       SLA_CHECK(stg.begin(SLA_STAGE_CLASSIFY));
-      SLA_CHECK(launched(launch_scores(d, reinterpret_cast<float*>(ws + wl.qbar),
-                                       reinterpret_cast<float*>(ws + wl.kbar),
-                                       reinterpret_cast<float*>(ws + wl.scores), s),
-                         "scores"));
-      SLA_CHECK(launched(launch_classify(d, reinterpret_cast<float*>(ws + wl.scores), mask, lut,
-                                         lut_cnt, bits, s),
-                         "classify"));
+      if (d.G > 0) {
+        // two-level: group means of K, then coarse and candidate scores inside the classifier
+        auto* kgbar = reinterpret_cast<float*>(ws + wl.kgbar);
+        SLA_CHECK(launched(launch_group_means(d, reinterpret_cast<float*>(ws + wl.kbar), kgbar, s),
+                           "group_means"));
+        SLA_CHECK(launched(launch_classify_hier(d, reinterpret_cast<float*>(ws + wl.qbar), kgbar,
+                                                reinterpret_cast<float*>(ws + wl.kbar), nullptr,
+                                                nullptr, mask, lut, lut_cnt, bits, s),
+                           "classify_hier"));
+      } else {
+        SLA_CHECK(launched(launch_scores(d, reinterpret_cast<float*>(ws + wl.qbar),
+                                         reinterpret_cast<float*>(ws + wl.kbar),
+                                         reinterpret_cast<float*>(ws + wl.scores), s),
+                           "scores"));
+        SLA_CHECK(launched(launch_classify(d, reinterpret_cast<float*>(ws + wl.scores), mask, lut,
+                                           lut_cnt, bits, s),
+                           "classify"));
+      }
       SLA_CHECK(stg.end(SLA_STAGE_CLASSIFY));
     } else {
       SLA_CHECK(stg.begin(SLA_STAGE_CLASSIFY));
@@ -356,7 +391,7 @@ sla_status sla_backward(const sla_config* cfg, const void* q, const void* k, con
   const auto* zst = reinterpret_cast<const float*>(sv + sl.zst);
   // the forward ran its linear branch exactly when this holds (same config)
   const bool given = d.mask_mode == SLA_MASK_GIVEN;
-  const bool linear = d.global || given || (d.km > 0 && d.kc < d.T);
+  const bool linear = d.global || given || ((d.km > 0 || d.G > 0) && d.kc < d.T);
 
   SLA_CHECK(stg.begin(SLA_STAGE_BWD_PRE));
   SLA_CHECK(launched(launch_mask_lists(d, mask, lut, lut_cnt, rbits, col, col_cnt, cbits, s),
@@ -416,6 +451,43 @@ sla_status sla_classify(const sla_config* cfg, const float* scores, int8_t* mask
   return launched(launch_classify(d, scores, mask, nullptr, nullptr, nullptr,
                                   static_cast<hipStream_t>(stream)),
                   "classify");
+}
+
+sla_status sla_coarse_scores(const sla_config* cfg, const void* q, const void* k, float* coarse,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  Dims d;
+  SLA_CHECK(make_dims(cfg, &d));
+  if (d.G == 0) return fail(SLA_ERR_INVALID_ARGUMENT, "select_group is 0 (flat selection)");
+  SLA_CHECK(check_ptr(q, "q"));
+  SLA_CHECK(check_ptr(k, "k"));
+  SLA_CHECK(check_ptr(coarse, "coarse"));
+  SLA_CHECK(check_ptr(workspace, "workspace"));
+  const WorkspaceLayout wl = workspace_layout(d);
+  if (workspace_bytes < wl.total)
+    return fail(SLA_ERR_WORKSPACE, "workspace of %zu bytes is below the required %zu",
+                workspace_bytes, wl.total);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  auto* qbar = reinterpret_cast<float*>(ws + wl.qbar);
+  auto* kbar = reinterpret_cast<float*>(ws + wl.kbar);
+  auto* kgbar = reinterpret_cast<float*>(ws + wl.kgbar);
+  SLA_CHECK(launched(launch_pool(d, static_cast<const uint16_t*>(q), qbar, s), "pool_q"));
+  SLA_CHECK(launched(launch_pool(d, static_cast<const uint16_t*>(k), kbar, s), "pool_k"));
+  SLA_CHECK(launched(launch_group_means(d, kbar, kgbar, s), "group_means"));
+  return launched(launch_coarse_scores(d, qbar, kgbar, coarse, s), "coarse_scores");
+}
+
+sla_status sla_classify_hier(const sla_config* cfg, const float* coarse, const float* scores,
+                             int8_t* mask, void* stream) {
+  Dims d;
+  SLA_CHECK(make_dims(cfg, &d));
+  if (d.G == 0) return fail(SLA_ERR_INVALID_ARGUMENT, "select_group is 0 (flat selection)");
+  SLA_CHECK(check_ptr(coarse, "coarse"));
+  SLA_CHECK(check_ptr(scores, "scores"));
+  SLA_CHECK(check_ptr(mask, "mask"));
+  return launched(launch_classify_hier(d, nullptr, nullptr, nullptr, coarse, scores, mask, nullptr,
+                                       nullptr, nullptr, static_cast<hipStream_t>(stream)),
+                  "classify_hier");
 }
 
 const char* sla_status_string(sla_status status) {

@@ -20,12 +20,15 @@ struct Dims {
   int mask_mode;
   bool global;         // linear branch over every key block (H_i, Z_i the same for all i)
   float gate;          // scale of the projected linear output (1 unless global)
+  int G;               // two-level selection: key blocks per group (0: flat selection)
+  int Tg, keep, ng;    // two-level selection: groups, kept groups, negligible groups per row
   long long BH() const { return static_cast<long long>(B) * H; }
 };
 
 // Byte offsets inside the caller's workspace.
 struct WorkspaceLayout {
   size_t qbar, kbar;        // fp32 [BH, T, D]
+  size_t kgbar;             // fp32 [BH, Tg, D]  group means of K (two-level selection)
   size_t scores;            // fp32 [BH, T, T]
   size_t lut, lut_cnt;      // int32 [BH, T, T] critical key blocks per row (ascending), int32 [BH, T]
   size_t col, col_cnt;      // int32 [BH, T, T] critical query blocks per column, int32 [BH, T]
@@ -65,6 +68,16 @@ hipError_t launch_mask_lists(const Dims& d, const int8_t* mask, int32_t* lut, in
                              uint32_t* rbits, int32_t* col, int32_t* col_cnt, uint32_t* cbits,
                              hipStream_t s);
 hipError_t launch_fill_mask(const Dims& d, int8_t* mask, int8_t value, hipStream_t s);
+// two-level selection: group means of K from the block means, the coarse score
+// map alone, and the classification (from qbar / kgbar / kbar, or from given
+// coarse and fine maps when coarse_in / scores_in are set)
+hipError_t launch_group_means(const Dims& d, const float* kbar, float* kgbar, hipStream_t s);
+hipError_t launch_coarse_scores(const Dims& d, const float* qbar, const float* kgbar,
+                                float* coarse, hipStream_t s);
+hipError_t launch_classify_hier(const Dims& d, const float* qbar, const float* kgbar,
+                                const float* kbar, const float* coarse_in, const float* scores_in,
+                                int8_t* mask, int32_t* lut, int32_t* lut_cnt, uint32_t* rbits,
+                                hipStream_t s);
 hipError_t launch_aggregate(const Dims& d, const uint32_t* bits, const uint16_t* states,
                             uint16_t* hout, float* zout, hipStream_t s);
 // column sums of the states over every key block, written to slot i = 0 of

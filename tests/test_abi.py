@@ -116,3 +116,32 @@ def test_linear_mode_and_gate_are_validated_on_the_host():
     # the gate is ignored by the method's own (marginal) linear branch
     plain = B.make_config(1, 2, 1024, 64, 0.1, 0.2, linear_gate=7.0)
     assert B.sla_block_counts(plain) == (2, 3, 11)
+
+
+def test_two_level_selection_is_validated_on_the_host():
+    from sparse_linear_attention_mean_amd import _binding as B
+    import oracle as orc
+
+    # T = 40 blocks: groups of 8 -> 5 groups of 8; groups of 6 -> 7 groups, the last of 4
+    for g, keep, fc, fn in ((8, 2, 0.25, 0.3), (6, 3, 0.35, 0.5), (1, 40, 0.1, 0.1), (40, 1, 0.9, 0.1)):
+        cfg = B.make_config(1, 2, 64 * 40, 64, fc, fn, select_group=g, select_keep=keep)
+        k_c, k_n, _ = B.sla_block_counts(cfg)
+        orc.hier_counts(40, g, keep, k_c, k_n)   # the oracle accepts it too
+        assert B.sla_workspace_size(cfg) > 0
+    bad = [
+        (8, 0, 0.1, 0.1),     # nothing kept
+        (8, 6, 0.1, 0.1),     # more kept than groups
+        (8, 2, 0.45, 0.1),    # 18 critical > 16 candidates
+        (6, 2, 0.26, 0.1),    # 11 critical > 6 + 4 (the short last group kept)
+        (41, 1, 0.1, 0.1),    # group larger than the row
+        (-1, 1, 0.1, 0.1),
+    ]
+    for g, keep, fc, fn in bad:
+        cfg = B.make_config(1, 2, 64 * 40, 64, fc, fn, select_group=g, select_keep=keep)
+        with pytest.raises(B.SlaError):
+            B.sla_block_counts(cfg)
+        assert B.sla_workspace_size(cfg) == 0
+        if g >= 1:
+            k_c, k_n, _ = orc.block_counts(40, fc, fn)
+            with pytest.raises(ValueError):
+                orc.hier_counts(40, g, keep, k_c, k_n)
