@@ -259,6 +259,54 @@ def global_linear_rate(wl, q, k, v, w, do, dev, with_bwd, gate=0.5):
             "note": "linear_mode = SLA_LINEAR_GLOBAL, same fractions"}
 
 
+def two_level_selection(dev, hip, group=8, keep=8, steps=5):
+    """Flat against two-level key-block selection on the long-sequence workload
+    (N = 65536, T = 1024): the selection stage (score map and classification,
+    or group means and the two-level classifier) and the whole forward, from
+    the library's stage events.  Also the share of critical blocks the two
+    splits have in common."""
+    import torch
+
+    from sparse_linear_attention_mean_amd import _binding as B
+    from sparse_linear_attention_mean_amd.attention import SlaProblem, bf16_from_bits
+    from sparse_linear_attention_mean_amd.inputs import WORKLOADS, make_workload_inputs
+
+    wl = WORKLOADS["pixel_b1_h8_n65536_d64"]
+    inp = make_workload_inputs(wl.name, seed=0, with_grad=False)
+    q, k, v, w = (bf16_from_bits(inp[x], dev) for x in ("q", "k", "v", "w"))
+    out = {"workload": wl.name, "select_group": group, "select_keep": keep}
+    masks = {}
+    si = B.STAGES.index("classify")
+    for label, g, kp in (("flat", 0, 0), ("two_level", group, keep)):
+        prob = SlaProblem.create(wl.batch, wl.heads, wl.seq_len, wl.head_dim, wl.frac_critical,
+                                 wl.frac_negligible, valid_len=wl.valid_len, device=dev,
+                                 select_group=g, select_keep=kp)
+        o = torch.empty(prob.shape(), dtype=torch.bfloat16, device=dev)
+        mask = prob.new_mask()
+        evs = [hip.array(2 * B.SLA_NUM_STAGES) for _ in range(steps)]
+        prob.forward(q, k, v, w, o=o, mask=mask)
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for ev in evs:
+            prob.cfg.stage_events = ctypes.cast(ev, ctypes.c_void_p).value
+            prob.forward(q, k, v, w, o=o, mask=mask)
+        b.record()
+        torch.cuda.synchronize()
+        prob.cfg.stage_events = None
+        sel = [hip.elapsed_ms(ev[2 * si], ev[2 * si + 1]) for ev in evs]
+        sel = [x for x in sel if x is not None]
+        out[label] = {"selection_ms": round(sum(sel) / len(sel), 4),
+                      "fwd_ms": round(a.elapsed_time(b) / steps, 4)}
+        masks[label] = mask
+    crit_f, crit_h = masks["flat"] == 1, masks["two_level"] == 1
+    out["critical_overlap"] = round(float((crit_f & crit_h).sum()) / max(1, int(crit_f.sum())), 4)
+    out["selection_speedup"] = round(out["flat"]["selection_ms"] /
+                                     out["two_level"]["selection_ms"], 2)
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -385,6 +433,7 @@ def main():
         rec["vs_dense"] = dense_ratio(wl, q, k, v, w, do, dev, with_bwd, ms)
         rec["mask_reuse"] = mask_reuse_rate(wl, q, k, v, w, dev, mask)
         rec["global_linear"] = global_linear_rate(wl, q, k, v, w, do, dev, with_bwd)
+        rec["two_level_selection"] = two_level_selection(dev, hip)
     if args.traffic_probe:
         src = torch.empty(128 << 20, dtype=torch.bfloat16, device=dev).fill_(1.0)
         dst = torch.empty_like(src)

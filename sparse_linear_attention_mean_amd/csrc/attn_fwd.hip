@@ -245,6 +245,20 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs args) {
   }
   l_run += __shfl_xor(l_run, 32);
 
+  // the W rows of the fusion product are loaded now, so their latency
+  // overlaps the merge and the linear branch: wave (kh, qh) finishes output
+  // columns o in [D/2 kh, D/2 kh + D/2), A operand W[o][16 cc + 8 hl .. + 7]
+  constexpr int NCL = D / 64;   // 32-row tiles per wave in each half
+  bf16x8 wf[LINEAR ? NCL : 1][C::NCC];
+  if constexpr (LINEAR) {
+#pragma unroll
+    for (int ot = 0; ot < NCL; ++ot) {
+      const uint16_t* wr = args.w + static_cast<size_t>((D / 2) * kh + 32 * ot + n32) * D + 8 * hl;
+#pragma unroll
+      for (int cc = 0; cc < C::NCC; ++cc) wf[ot][cc] = as_bf16x8(ld16(wr + 16 * cc));
+    }
+  }
+
   // ---- merge the two key halves (split-K style): wave (kh, qh) finishes the
   // O_s^T tiles ct = NH kh .. NH kh + NH - 1 and hands the others to its partner.
   constexpr int NH = C::NCT / 2;
@@ -325,17 +339,22 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs args) {
     float dpart = 0.f;
 #pragma unroll
     for (int cc = 0; cc < C::NCC; ++cc) {
+      const int a0 = 16 * cc + 8 * hl;   // this lane's head-dim indices a0 .. a0 + 7
+      const f32x4 z0 = *reinterpret_cast<const f32x4*>(&zsw[a0]);
+      const f32x4 z1 = *reinterpret_cast<const f32x4*>(&zsw[a0 + 4]);
+      const f32x4 y0 = *reinterpret_cast<const f32x4*>(&zsw[D + a0]);
+      const f32x4 y1 = *reinterpret_cast<const f32x4*>(&zsw[D + a0 + 4]);
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
         const __bf16 r = static_cast<__bf16>(phi(static_cast<float>(qf[cc][s])));
         pq[cc][s] = r;
-        const int a = 16 * cc + 8 * hl + s;
-        dpart += static_cast<float>(r) * (zsw[a] + zsw[D + a]);
+        const float z = s < 4 ? z0[s] + y0[s] : z1[s - 4] + y1[s - 4];
+        dpart += static_cast<float>(r) * z;
       }
     }
     const float den_v = dpart + __shfl_xor(dpart, 32);
     const float rden = den_v > 0.f ? 1.0f / den_v : 0.f;
-    constexpr int NCL = D / 64;   // 32-row tiles of Y^T per wave (c half kh)
+    // Y^T tiles: wave (kh, qh) computes c in [D/2 kh, D/2 kh + D/2)
     // H^T row c: rows 0 .. 63 are in kb0, rows 64 .. 127 (D = 128) in kb1
     const uint16_t* hsw = (D == 128 && kh) ? kb1 : kb0;
     const int hrow0 = D == 128 ? 0 : (D / 2) * kh;
@@ -369,11 +388,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs args) {
 #pragma unroll
     for (int ot = 0; ot < NCL; ++ot) {
       const int obase = (D / 2) * kh + 32 * ot;
-      const uint16_t* wr = args.w + static_cast<size_t>(obase + n32) * D + 8 * hl;
       f32x16 out = {};
 #pragma unroll
-      for (int cc = 0; cc < C::NCC; ++cc)
-        out = mfma32(as_bf16x8(ld16(wr + 16 * cc)), as_bf16x8(ld16(ys + 16 * cc)), out);
+      for (int cc = 0; cc < C::NCC; ++cc) out = mfma32(wf[ot][cc], as_bf16x8(ld16(ys + 16 * cc)), out);
 #pragma unroll
       for (int e4 = 0; e4 < 4; ++e4) {
         const int o0 = obase + 8 * e4 + 4 * hl;
