@@ -50,7 +50,8 @@ class _Buffers:
 
     def workspace(self, cfg, device):
         key = (cfg.batch, cfg.heads, cfg.seq_len, cfg.head_dim, cfg.valid_len,
-                cfg.frac_critical, cfg.frac_negligible, cfg.mask_mode, str(device))
+                cfg.frac_critical, cfg.frac_negligible, cfg.mask_mode, cfg.select_group,
+                cfg.select_keep, str(device))
         ws = self._ws.get(key)
         if ws is None:
             ws = torch.empty(B.sla_workspace_size(cfg), dtype=torch.uint8, device=device)
@@ -115,12 +116,14 @@ class SparseLinearAttention(torch.nn.Module):
     linear branch.  valid_len: tokens at or past it are padding (0 = none).
     The projection weight (d x d, nn.Linear layout, O = O_s + Y W^T) is kept in
     the dtype of ``weight`` (fp32 by default) and cast to bf16 per call.
+    select_group / select_keep: two-level key-block selection (groups of
+    select_group blocks, select_keep kept per query block); 0 is the flat one.
     """
 
     def __init__(self, head_dim: int, frac_critical: float, frac_negligible: float,
                  valid_len: int = 0, softmax_scale: float = 0.0, reuse_mask: bool = False,
                  weight: torch.Tensor | None = None, device=None, global_linear: bool = False,
-                 gate: float = 1.0):
+                 gate: float = 1.0, select_group: int = 0, select_keep: int = 0):
         super().__init__()
         if head_dim not in (64, 128):
             raise ValueError("head_dim must be 64 or 128")
@@ -132,6 +135,8 @@ class SparseLinearAttention(torch.nn.Module):
         self.reuse_mask = bool(reuse_mask)
         self.global_linear = bool(global_linear)   # SALAD-style linear branch over every block
         self.gate = float(gate)                     # its output scale (global_linear only)
+        self.select_group = int(select_group)       # two-level selection: blocks per group (0: flat)
+        self.select_keep = int(select_keep)         # two-level selection: groups kept per row
         if weight is None:
             weight = torch.randn(head_dim, head_dim, device=device) / math.sqrt(head_dim)
         self.weight = torch.nn.Parameter(weight.clone())
@@ -155,7 +160,8 @@ class SparseLinearAttention(torch.nn.Module):
         cfg = B.make_config(b, h, n, d, self.frac_critical, self.frac_negligible, self.valid_len,
                             self.softmax_scale, B.SLA_MASK_GIVEN if given else B.SLA_MASK_COMPUTE,
                             linear_mode=B.SLA_LINEAR_GLOBAL if self.global_linear
-                            else B.SLA_LINEAR_MARGINAL, linear_gate=self.gate)
+                            else B.SLA_LINEAR_MARGINAL, linear_gate=self.gate,
+                            select_group=self.select_group, select_keep=self.select_keep)
         B.sla_block_counts(cfg)   # validates the configuration, raises SlaError
         w = self.weight.to(torch.bfloat16)
         o, mask = SlaFunction.apply(q, k, v, w, cfg, self._mask if given else None)

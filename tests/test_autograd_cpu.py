@@ -29,3 +29,11 @@ def test_rejects_bad_fractions_through_the_library():
     x = torch.zeros(1, 2, 1024, 64, dtype=torch.bfloat16)
     with pytest.raises(B.SlaError):
         mod(x, x, x)
+
+
+def test_rejects_impossible_two_level_selection_through_the_library():
+    # 1024 tokens = 16 blocks, groups of 4: keeping 1 group leaves 4 candidates < k_c = 6
+    mod = SparseLinearAttention(64, 0.35, 0.0, select_group=4, select_keep=1)
+    x = torch.zeros(1, 2, 1024, 64, dtype=torch.bfloat16)
+    with pytest.raises(B.SlaError):
+        mod(x, x, x)

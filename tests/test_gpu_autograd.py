@@ -79,3 +79,29 @@ def test_mask_reuse_is_exact_and_skips_classification():
 
     mod.reset_mask()
     assert mod.cached_mask is None
+
+
+def test_autograd_with_two_level_selection():
+    b, h, n, d, vl, fc, fn, g, keep = 1, 2, 64 * 24, 64, 64 * 24 - 3, 0.15, 0.3, 4, 3
+    inp = make_inputs(b, h, n, d, (4, 16, 24), vl, seed=21, with_grad=True)
+    dev = device_inputs(inp)
+    q, k, v = (dev[x].clone().requires_grad_(True) for x in ("q", "k", "v"))
+    mod = SparseLinearAttention(d, fc, fn, valid_len=vl, weight=dev["w"].float(), reuse_mask=True,
+                                select_group=g, select_keep=keep)
+    o = mod(q, k, v)
+    o.backward(dev["do"])
+    torch.cuda.synchronize()
+    mask = mod.cached_mask.cpu().numpy()
+    t = n // 64
+    k_c, k_n, _ = orc.block_counts(t, fc, fn)
+    _, n_g = orc.hier_counts(t, g, keep, k_c, k_n)
+    for row in mask.reshape(-1, t):
+        assert (row == 1).sum() == k_c
+        negl_groups = set(np.flatnonzero(row == -1) // g)
+        assert len(negl_groups) == n_g
+    x = decoded(inp)
+    ref = orc.forward(x["q"], x["k"], x["v"], x["w"], 0.0, 0.0, valid_len=vl, mask=mask)
+    assert_close("o", to_np(o), ref["o"])
+    gr = orc.backward(x["q"], x["k"], x["v"], x["w"], x["do"], mask, valid_len=vl)
+    for name, tt in (("dq", q.grad), ("dk", k.grad), ("dv", v.grad)):
+        assert_close(name, to_np(tt), gr[name], atol=2e-2 * float(np.abs(gr[name]).max()))

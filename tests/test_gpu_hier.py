@@ -1,11 +1,13 @@
 """GPU parity of the two-level (hierarchical) key-block selection.
 
 Protocol, as for the flat classifier: identical fp32 maps must give
-byte-identical masks.  ``sla_classify_hier`` is checked on synthetic maps
+byte-identical masks, checked with ``sla_classify_hier`` on synthetic maps
 (ties, signed zeros, a short last group, kept and negligible groups that
-overlap); the forward's own mask must equal the oracle's two-level split of
-the GPU's coarse map (``sla_coarse_scores``) and fine map (``sla_pool_scores``),
-and the outputs and gradients under that mask are compared with the oracle.
+overlap).  The forward's mask is checked against the oracle's own coarse and
+fine maps: rows equal to the oracle's split are compared element-wise, the
+others (near-ties, rounded differently by the two independently computed
+maps) must be a valid two-level split within the rounding gap.  Gradients are
+compared with the GPU run in fixed-mask mode on the oracle's mask.
 """
 import numpy as np
 import pytest
@@ -97,12 +99,54 @@ def _hier_forward(inp, fc, fn, g, keep):
                              select_keep=keep)
     dev = device_inputs(inp)
     o, m = prob.forward(dev["q"], dev["k"], dev["v"], dev["w"])
+    # the library's own maps, classified by sla_classify_hier: the forward's
+    # internal candidate scores must reproduce them (GPU against GPU)
     coarse = prob.coarse_scores(dev["q"], dev["k"])
     scores = prob.pool_scores(dev["q"], dev["k"])
+    again = classify_hier(prob.cfg, coarse, scores)
     torch.cuda.synchronize()
+    assert torch.equal(again, m), "forward mask differs from sla_classify_hier on the same maps"
     lse, den, y = prob.saved_views()
-    return prob, dev, dict(o=to_np(o), mask=m.cpu().numpy(), lse=lse.cpu().numpy(),
-                           y=to_np(y), coarse=coarse.cpu().numpy(), scores=scores.cpu().numpy())
+    return prob, dev, dict(o=to_np(o), mask=m.cpu().numpy(), lse=lse.cpu().numpy(), y=to_np(y))
+
+
+def _oracle_maps(x, vl, g, b, h):
+    scale = orc.default_scale(x["q"].shape[-1])
+    coarse = np.stack([np.stack([orc.coarse_scores(x["q"][bb, hh], x["k"][bb, hh], vl, scale, g)
+                                 for hh in range(h)]) for bb in range(b)])
+    scores = np.stack([np.stack([orc.compressed_scores(x["q"][bb, hh], x["k"][bb, hh], vl, scale)
+                                 for hh in range(h)]) for bb in range(b)])
+    return coarse, scores
+
+
+def _hier_validity(gpu, coarse, scores, k_c, n_g, keep, g):
+    """Rows of the GPU mask that differ from the oracle's own split must still
+    be a two-level split of the oracle's maps up to the rounding gap between
+    independently computed maps.  Returns the [..., T] rows that are equal."""
+    ref = orc.classify_hier(coarse, scores, k_c, n_g, keep, g)
+    same = (gpu == ref).all(axis=-1)
+    t, tg = scores.shape[-1], coarse.shape[-1]
+    tol_c = 1e-4 * float(np.abs(coarse).max()) + 1e-6
+    tol_s = 1e-4 * float(np.abs(scores).max()) + 1e-6
+    gf = gpu.reshape(-1, t)
+    cf = coarse.reshape(-1, tg).astype(np.float64)
+    sf = scores.reshape(-1, t).astype(np.float64)
+    for r in np.flatnonzero(~same.reshape(-1)):
+        row, c, s = gf[r], cf[r], sf[r]
+        assert (row == 1).sum() == k_c, "critical count"
+        grp = np.arange(t) // g
+        kth = np.sort(c)[::-1][keep - 1]          # the keep-th largest coarse score
+        crit_groups = np.unique(grp[row == 1])
+        assert np.all(c[crit_groups] >= kth - tol_c), "critical block outside the kept groups"
+        sure = c > kth + tol_c                    # groups kept whatever the rounding
+        cand = sure[grp] & (row != 1)
+        if cand.any() and k_c:
+            assert s[row == 1].min() >= s[cand].max() - tol_s, "critical order beyond rounding"
+        negl = np.unique(grp[row == -1])
+        if n_g:
+            nth = np.sort(c)[n_g - 1]             # the n_g-th smallest coarse score
+            assert np.all(c[negl] <= nth + tol_c), "negligible group beyond rounding"
+    return same
 
 
 FWD_CASES = [
@@ -121,17 +165,21 @@ def test_forward_two_level_matches_oracle(case):
     t = n // 64
     k_c, k_n, _ = orc.block_counts(t, fc, fn)
     _, n_g = orc.hier_counts(t, g, keep, k_c, k_n)
-    ref_mask = orc.classify_hier(got["coarse"], got["scores"], k_c, n_g, keep, g)
-    assert np.array_equal(got["mask"], ref_mask), f"{name}: forward mask"
     x = decoded(inp)
+    coarse, scores = _oracle_maps(x, vl, g, b, h)
+    same = _hier_validity(got["mask"], coarse, scores, k_c, n_g, keep, g)
+    assert same.mean() >= 0.9, f"{name}: only {same.mean():.3f} of the rows equal the oracle's"
+    # outputs on the query blocks whose mask rows equal the oracle's own split
+    ref_mask = orc.classify_hier(coarse, scores, k_c, n_g, keep, g)
     ref = orc.forward(x["q"], x["k"], x["v"], x["w"], 0.0, 0.0, valid_len=vl, mask=ref_mask)
-    valid = np.arange(n) < vl
-    assert_close(f"{name} O", got["o"][:, :, valid], ref["o"][:, :, valid])
-    assert_close(f"{name} Y", got["y"][:, :, valid], ref["y"][:, :, valid])
-    # the backward under the two-level mask
-    m = torch.from_numpy(got["mask"]).cuda()
-    o = torch.from_numpy(got["o"]).cuda().to(torch.bfloat16)
-    dq, dk, dv, dw = prob.backward(dev["q"], dev["k"], dev["v"], dev["w"], o, dev["do"], m)
+    sel = np.repeat(same, 64, axis=-1) & (np.arange(n) < vl)
+    assert_close(f"{name} O", got["o"][sel], ref["o"][sel])
+    assert_close(f"{name} Y", got["y"][sel], ref["y"][sel])
+    # the backward, run with the oracle's mask held fixed
+    m = torch.from_numpy(ref_mask).cuda()
+    gp = SlaProblem.create(b, h, n, d, fc, fn, valid_len=vl, mask_mode=B.SLA_MASK_GIVEN)
+    o, m = gp.forward(dev["q"], dev["k"], dev["v"], dev["w"], mask=m)
+    dq, dk, dv, dw = gp.backward(dev["q"], dev["k"], dev["v"], dev["w"], o, dev["do"], m)
     torch.cuda.synchronize()
     gref = orc.backward(x["q"], x["k"], x["v"], x["w"], x["do"], ref_mask, valid_len=vl)
     for nm, tt in (("dq", dq), ("dk", dk), ("dv", dv), ("dw", dw)):
@@ -148,8 +196,9 @@ def test_two_level_rejects_bad_parameters():
 
 def test_two_level_full_size_long_sequence():
     """The long-sequence workload (N = 65536, d = 64, 2% critical, 20%
-    negligible) with groups of 8 blocks and 8 kept groups: every mask row
-    against the oracle's split of the GPU maps; sampled outputs."""
+    negligible) with groups of 8 blocks and 8 kept groups, in the benchmark's
+    launch configuration: every mask row against the oracle's own maps;
+    outputs on sampled query blocks whose rows equal the oracle's split."""
     name, g, keep = "pixel_b1_h8_n65536_d64", 8, 8
     wl = WORKLOADS[name]
     log(f"workload {name}, G={g}, keep={keep}")
@@ -158,15 +207,26 @@ def test_two_level_full_size_long_sequence():
     t = wl.num_blocks
     k_c, k_n, _ = orc.block_counts(t, wl.frac_critical, wl.frac_negligible)
     _, n_g = orc.hier_counts(t, g, keep, k_c, k_n)
-    ref_mask = orc.classify_hier(got["coarse"], got["scores"], k_c, n_g, keep, g)
-    assert np.array_equal(got["mask"], ref_mask)
     scale = orc.default_scale(wl.head_dim)
     w = orc.decode_bf16(inp["w"])
     rng = np.random.default_rng(1)
-    for hh in (0, wl.heads - 1):
-        q, k, v = (orc.decode_bf16(inp[x][0, hh]) for x in ("q", "k", "v"))
-        blocks = sorted(set(rng.choice(t, 5, replace=False).tolist()) | {t - 1})
-        ref = orc.forward_head(q, k, v, w, ref_mask[0, hh], wl.valid_len, scale, blocks=blocks)
+    for hh in range(wl.heads):
+        q, k = (orc.decode_bf16(inp[x][0, hh]) for x in ("q", "k"))
+        coarse = orc.coarse_scores(q, k, wl.valid_len, scale, g)
+        scores = orc.compressed_scores(q, k, wl.valid_len, scale)
+        same = _hier_validity(got["mask"][0, hh], coarse, scores, k_c, n_g, keep, g)
+        log(f"  head {hh}: mask rows equal {same.mean():.4f}")
+        assert same.mean() >= 0.9
+        if hh not in (0, wl.heads - 1):
+            continue
+        v = orc.decode_bf16(inp["v"][0, hh])
+        ref_mask = orc.classify_hier(coarse, scores, k_c, n_g, keep, g)
+        cand = np.flatnonzero(same)
+        blocks = set(rng.choice(cand, min(5, cand.size), replace=False).tolist())
+        if same[t - 1]:
+            blocks.add(t - 1)
+        blocks = sorted(blocks)
+        ref = orc.forward_head(q, k, v, w, ref_mask, wl.valid_len, scale, blocks=blocks)
         for i in blocks:
             lo, hi = i * 64, min((i + 1) * 64, wl.valid_len)
             assert_close(f"  head {hh} blk {i} O", got["o"][0, hh, lo:hi], ref["o"][lo:hi])
