@@ -26,16 +26,19 @@ namespace sla {
 constexpr int kAggNTile = 64;    // state columns per workgroup
 constexpr int kAggIWave = 128;   // query rows per wave
 constexpr int kAggIChunk = 512;  // query rows per workgroup (4 waves)
-constexpr int kAggKChunk = 512;  // key blocks of the state strip staged in LDS per pass
+constexpr int kAggKChunk = 128;  // key blocks of the state strip staged in LDS per chunk
 // LDS strip: pairs of 4-block planes, 2 x 64 columns x 4 blocks (1 KB, one
 // copy instruction) plus 128 bytes of padding, so the four lane groups of an
 // A-operand read (planes 2 g apart) fall on different banks
 constexpr int kAggPair = 2 * kAggNTile * 4 + 64;   // bf16 elements per plane pair
 
 // One workgroup owns a 64-column strip of S and 512 rows of C.  The strip is
-// shared by the four waves (each owns 128 rows), so it is copied once into
-// LDS with asynchronous global->LDS loads (72 KB per pass of 512 key blocks)
-// instead of being fetched by every wave; the marginal words stream from
+// shared by the four waves (each owns 128 rows), so it is copied into LDS with
+// asynchronous global->LDS loads instead of being fetched by every wave, in
+// chunks of 128 key blocks (18 KB) into two buffers: the next chunk's copies
+// are in flight while the current chunk is multiplied (the buffers are
+// separate arrays named statically, so the compiler does not hold the LDS
+// reads back for the copies in flight).  The marginal words stream from
 // global memory (they are small and stay in L2) two k-steps ahead, 32
 // contiguous bytes per lane and k-step.
 __global__ __launch_bounds__(256, 2) void aggregate_kernel(const uint32_t* __restrict__ bits,
@@ -45,7 +48,11 @@ __global__ __launch_bounds__(256, 2) void aggregate_kernel(const uint32_t* __res
                                                           int NB, int DD, int ntiles,
                                                           int ichunks) {
   __shared__ u32x4 table[256];
-  __shared__ __attribute__((aligned(16))) uint16_t strip[kAggKChunk / 8 * kAggPair];
+  __shared__ __attribute__((aligned(16))) uint16_t strip0[kAggKChunk / 8 * kAggPair];
+  __shared__ __attribute__((aligned(16))) uint16_t strip1[kAggKChunk / 8 * kAggPair];
+  // the chunk's marginal words: word k of rows ib .. ib + 511 at [k][row - ib]
+  __shared__ __attribute__((aligned(16))) uint32_t wsl0[kAggKChunk / 32 * kAggIChunk];
+  __shared__ __attribute__((aligned(16))) uint32_t wsl1[kAggKChunk / 32 * kAggIChunk];
   const int tid = threadIdx.x;
   {
     uint32_t w[4];
@@ -80,18 +87,16 @@ __global__ __launch_bounds__(256, 2) void aggregate_kernel(const uint32_t* __res
 
   const uint16_t* sbase = states + static_cast<size_t>(bh) * Tp * NB;
   const int ksteps = Tp / 32;
-  const uint32_t* bcol = bits + static_cast<size_t>(bh) * ksteps * Tp + (rows_ok ? rbase : 0);
-  struct Words {
-    u32x4 lo, hi;   // the words of rows rbase .. rbase + 3 and rbase + 4 .. rbase + 7
-  };
-  Words w0, w1;
-  auto fetch = [&](Words& w, int kk) {
-    const int kc = kk < ksteps ? kk : ksteps - 1;   // past the end: a harmless re-read
-    w.lo = ld16(bcol + static_cast<size_t>(kc) * Tp);
-    w.hi = ld16(bcol + static_cast<size_t>(kc) * Tp + 4);
-  };
+  const int ib = ic * kAggIChunk;
+  // bits of this workgroup's rows, bounded at the padded row count (rows past
+  // it read as zero)
+  const __amdgpu_buffer_rsrc_t brs =
+      make_rsrc(bits + static_cast<size_t>(bh) * ksteps * Tp, static_cast<uint32_t>(ksteps) * Tp * 4u);
   // one k-step (32 key blocks): A = S^T tile from the staged strip, B = bits -> bf16
-  auto step = [&](const Words& w, int kl) {
+  auto step = [&](const uint16_t* strip, const uint32_t* wsl, int kl) __attribute__((always_inline)) {
+    const uint32_t* wr = wsl + kl * kAggIChunk + (rbase - ib);   // rows rbase .. rbase + 7
+    const u32x4 wlo = *reinterpret_cast<const u32x4*>(wr);
+    const u32x4 whi = *reinterpret_cast<const u32x4*>(wr + 4);
     bf16x8 a[4], b[8];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
@@ -101,35 +106,52 @@ __global__ __launch_bounds__(256, 2) void aggregate_kernel(const uint32_t* __res
     }
 #pragma unroll
     for (int q = 0; q < 8; ++q)
-      b[q] = as_bf16x8(table[((q < 4 ? w.lo[q & 3] : w.hi[q & 3]) >> (8 * g)) & 0xffu]);
+      b[q] = as_bf16x8(table[((q < 4 ? wlo[q & 3] : whi[q & 3]) >> (8 * g)) & 0xffu]);
 #pragma unroll
     for (int m = 0; m < 4; ++m)
 #pragma unroll
       for (int q = 0; q < 8; ++q) acc[m][q] = mfma16(a[m], b[q], acc[m][q]);
   };
 
-  fetch(w0, 0);
-  fetch(w1, 1);
-  for (int kc0 = 0; kc0 < Tp; kc0 += kAggKChunk) {
+  // chunk c of the strip (key blocks 128 c ..) into dst: plane pair gi goes
+  // to dst + gi * kAggPair, lanes 0-31 plane 2 gi, lanes 32-63 plane 2 gi + 1
+  const int nch = (Tp + kAggKChunk - 1) / kAggKChunk;
+  // ... and its marginal words: k-step k, 512 rows = 2 KB, one copy of
+  // 1 KB per half (waves 0-3 take the k-steps in turn)
+  auto copy_chunk = [&](int c, uint16_t* dst, uint32_t* wdst) __attribute__((always_inline)) {
+    const int kc0 = c * kAggKChunk;
     const int kn = Tp - kc0 < kAggKChunk ? Tp - kc0 : kAggKChunk;   // multiple of 32
-    __syncthreads();   // table ready / previous pass fully consumed
-    for (int gi = wave; gi < kn / 8; gi += 4)   // plane pair gi: lanes 0-31 plane 2 gi, 32-63 plane 2 gi + 1
-      gl_to_lds16(sbase + (static_cast<size_t>(kc0 / 4 + 2 * gi + (lane >> 5)) * NB + n0 + 2 * (lane & 31)) * 4,
-                  strip + gi * kAggPair);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    const int k0 = kc0 / 32;
-    for (int kl = 0; kl < kn / 32; kl += 2) {
-      step(w0, kl);
-      fetch(w0, k0 + kl + 2);
-      if (kl + 1 >= kn / 32) break;
-      step(w1, kl + 1);
-      fetch(w1, k0 + kl + 3);
+    for (int gi = wave; gi < kn / 8; gi += 4)
+      gl_to_lds16(sbase + (static_cast<size_t>(kc0 / 4 + 2 * gi + (lane >> 5)) * NB + n0 +
+                           2 * (lane & 31)) * 4,
+                  dst + gi * kAggPair);
+    for (int h = wave; h < kn / 32 * 2; h += 4) {   // half h: k-step h / 2, rows 256 (h % 2) ..
+      const int kk = kc0 / 32 + h / 2;
+      const uint32_t off = (static_cast<uint32_t>(kk) * Tp + ib + 256 * (h & 1) + 4 * lane) * 4u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          brs, (__attribute__((address_space(3))) void*)(wdst + (h / 2) * kAggIChunk + 256 * (h & 1)),
+          16, off, 0, 0, 0);
     }
-    if ((kn / 32) & 1) {   // odd k-step count: the next pass starts with w1
-      const Words t = w0;
-      w0 = w1;
-      w1 = t;
+  };
+  auto chunk = [&](int c, const uint16_t* strip, const uint32_t* wsl) __attribute__((always_inline)) {
+    const int kc0 = c * kAggKChunk;
+    const int ks = (Tp - kc0 < kAggKChunk ? Tp - kc0 : kAggKChunk) / 32;
+    for (int kl = 0; kl < ks; ++kl) step(strip, wsl, kl);
+  };
+
+  copy_chunk(0, strip0, wsl0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();   // table ready, chunk 0 in place
+  for (int c = 0; c < nch; c += 2) {
+    if (c + 1 < nch) copy_chunk(c + 1, strip1, wsl1);
+    chunk(c, strip0, wsl0);
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's copies into strip1 have landed
+    __syncthreads();                 // strip0 consumed, strip1 complete
+    if (c + 1 < nch) {
+      if (c + 2 < nch) copy_chunk(c + 2, strip0, wsl0);
+      chunk(c + 1, strip1, wsl1);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
     }
   }
 
