@@ -398,11 +398,16 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(
 // one's products.  The resources end at valid_len: the padded rows of the
 // last query block arrive as zeros (Q = dO = 0 and D = 0 there, so they add
 // nothing to dV and, with dP = 0, nothing to dK).
-// Everything the block needs besides that stream -- K_j, V_j, dh_j^T and
-// dz_j -- is copied into LDS asynchronously when the workgroup starts, so
-// those reads overlap the first query block and the linear epilogue reads LDS
-// only.  After the loop the two query halves are merged so that every wave
-// finishes two of the four 32-column tiles.
+// Everything else the block needs -- K_j, V_j, dh_j^T and dz_j -- is copied
+// into LDS asynchronously when the workgroup starts; the loop waits only for
+// K_j, V_j and the first query block (each wave keeps one of K_j or V_j in
+// registers as its B operands), while dh_j^T and dz_j, needed only by the
+// linear epilogue, land during the first step.  Within a step each wave reads
+// all of its operands for the S / dP product and the transpose-read operands
+// of the product over queries before the P hand-off, so their latency
+// overlaps the exponentials and the barrier.  After the loop the two query
+// halves are merged so that every wave finishes two of the four 32-column
+// tiles.
 // ---------------------------------------------------------------------------
 template <int D>
 struct BkvCfg {
@@ -448,19 +453,17 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(
 
   // asynchronous copies of K_j, V_j (rows past valid_len are never used
   // unmasked), dh_j^T and dz_j
-  copy_swz<D>(k + head + static_cast<size_t>(j) * kBlock * D, ksw, 64, wave, 8, lane);
-  copy_swz<D>(v + head + static_cast<size_t>(j) * kBlock * D, vsw, 64, wave, 8, lane);
-  if (linear) {
-    const size_t hslot = static_cast<size_t>(bh) * T + (hglobal ? 0 : j);
-    copy_swz<D>(dh + hslot * D * D, dhs, D, wave, 8, lane);
-    if (wave == 7 && lane < D / 2) gl_to_lds16(dz + hslot * 2 * D + 4 * lane, dzs);
-  }
   const int cnt = col_cnt[bh * T + j];
   const int32_t* crow = col + (bh * T + j) * static_cast<long long>(T);
   // the list in a register (entry 64 g + l in lane l), read with readlane
   int colv = lane < cnt ? crow[lane] : 0;
   auto block_at = [&](int n) { return __builtin_amdgcn_readlane(colv, n & 63); };
 
+  // K_j and V_j into LDS (keys past valid_len arrive as zero)
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(k + head, static_cast<uint32_t>(L) * D * 2);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(v + head, static_cast<uint32_t>(L) * D * 2);
+  copy_swz_buf<D, 8>(krs, j * kBlock, ksw, wave, lane);
+  copy_swz_buf<D, 8>(vrs, j * kBlock, vsw, wave, lane);
   const __amdgpu_buffer_rsrc_t qrs = make_rsrc(q + head, static_cast<uint32_t>(L) * D * 2);
   const __amdgpu_buffer_rsrc_t drs = make_rsrc(dO + head, static_cast<uint32_t>(L) * D * 2);
   const __amdgpu_buffer_rsrc_t lrs = make_rsrc(lse + bh * N, static_cast<uint32_t>(L) * 4);
@@ -485,18 +488,61 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(
   for (int ct = 0; ct < C::NCT; ++ct) acc[ct] = f32x16{};
 
   if (cnt > 0) copy_q(0, qd0, lb0);
-  __builtin_amdgcn_s_waitcnt(0);   // this wave's copies have landed
-  __syncthreads();
-
-  // K_j (and V_j for the dK role) as B operands (k = head-dim index 16 cc + 8 hl + s)
-  bf16x8 kf[C::NCC], vf[C::NCC];
+  // dz_j and dh_j^T (for the linear epilogue) are issued last and not waited
+  // for here: the first step's end waits for them
+  constexpr int kDhCopies = D * D / 4096;   // dh^T copy instructions per wave
+  if (linear) {
+    const size_t hslot = static_cast<size_t>(bh) * T + (hglobal ? 0 : j);
+    if (wave == 7 && lane < D / 2) {
+      const __amdgpu_buffer_rsrc_t zrs = make_rsrc(dz + hslot * 2 * D, 2 * D * 4);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(zrs, (__attribute__((address_space(3))) void*)(dzs),
+                                               16, 16 * lane, 0, 0, 0);
+    }
+    const __amdgpu_buffer_rsrc_t hrs = make_rsrc(dh + hslot * D * D, D * D * 2);
 #pragma unroll
-  for (int cc = 0; cc < C::NCC; ++cc) {
-    const u32x4 kz = ld16(ksw + swz_off<D>(kloc, 16 * cc + 8 * hl));
-    const u32x4 vz = ld16(vsw + swz_off<D>(kloc, 16 * cc + 8 * hl));
-    kf[cc] = kv_ok ? as_bf16x8(kz) : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
-    vf[cc] = (role_dk && kv_ok) ? as_bf16x8(vz) : kf[cc];
+    for (int r0 = 0; r0 < D; r0 += 64) copy_swz_buf<D, 8>(hrs, r0, dhs + r0 * D, wave, lane);
+    __builtin_amdgcn_s_waitcnt(0xF70 | kDhCopies);   // all but the dh^T copies have landed
+  } else {
+    __builtin_amdgcn_s_waitcnt(0);
   }
+  // a barrier that does not wait for the dh^T copies
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  // B operands of S (dV role: K_j rows) or dP (dK role: V_j rows), k =
+  // head-dim index 16 cc + 8 hl + s.  Read in one asm block that waits for
+  // its own reads (outputs early-clobbered: a read's result must not land in
+  // a later read's address register): the compiler would otherwise make these
+  // reads wait for every copy in flight, the dh^T copies included.
+  bf16x8 bf[C::NCC];
+  {
+    const uint16_t* fsrc = role_dk ? vsw : ksw;
+    uint32_t fa[C::NCC];
+#pragma unroll
+    for (int cc = 0; cc < C::NCC; ++cc)
+      fa[cc] = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(fsrc + swz_off<D>(kloc, 16 * cc + 8 * hl)));
+    u32x4 fz[C::NCC];
+    if constexpr (C::NCC == 8) {
+      asm volatile(
+          "ds_read_b128 %0, %8\n\tds_read_b128 %1, %9\n\tds_read_b128 %2, %10\n\t"
+          "ds_read_b128 %3, %11\n\tds_read_b128 %4, %12\n\tds_read_b128 %5, %13\n\t"
+          "ds_read_b128 %6, %14\n\tds_read_b128 %7, %15\n\ts_waitcnt lgkmcnt(0)"
+          : "=&v"(fz[0]), "=&v"(fz[1]), "=&v"(fz[2]), "=&v"(fz[3]), "=&v"(fz[4]), "=&v"(fz[5]),
+            "=&v"(fz[6]), "=&v"(fz[7])
+          : "v"(fa[0]), "v"(fa[1]), "v"(fa[2]), "v"(fa[3]), "v"(fa[4]), "v"(fa[5]), "v"(fa[6]),
+            "v"(fa[7])
+          : "memory");
+    } else {
+      asm volatile(
+          "ds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\tds_read_b128 %2, %6\n\t"
+          "ds_read_b128 %3, %7\n\ts_waitcnt lgkmcnt(0)"
+          : "=&v"(fz[0]), "=&v"(fz[1]), "=&v"(fz[2]), "=&v"(fz[3])
+          : "v"(fa[0]), "v"(fa[1]), "v"(fa[2]), "v"(fa[3])
+          : "memory");
+    }
+#pragma unroll
+    for (int cc = 0; cc < C::NCC; ++cc)
+      bf[cc] = kv_ok ? as_bf16x8(fz[cc]) : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+  }
+
 
   const bool tail_key = key >= L;
   const bool tail_blk = (j + 1) * kBlock > L;   // uniform: the padded last key block
@@ -512,20 +558,32 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(
     // dV role: S = Q K^T and P, handed to the dK wave of the same (kh, qh)
     // through LDS; dK role meanwhile: dP = dO V^T.  Both result tiles have
     // lane = key, element e = query 32 qh + 8 (e/4) + 4 hl + e%4.
+    const uint16_t* asrc = qt + (role_dk ? C::kTile : 0);   // Q_i or dO_i rows
+    bf16x8 av[C::NCC];
+#pragma unroll
+    for (int cc = 0; cc < C::NCC; ++cc)
+      av[cc] = as_bf16x8(ld16(asrc + swz_off<D>(32 * qh + n32, 16 * cc + 8 * hl)));
+    f32x16 sd = {};
+#pragma unroll
+    for (int cc = 0; cc < C::NCC; ++cc) sd = mfma32(av[cc], bf[cc], sd);
+    // B operands of the products over queries (dO_i for dV, Q_i for dK) by
+    // transpose reads, query index in the permuted order of the S tile;
+    // read before the hand-off so their latency overlaps it
+    const uint16_t* bsrc = qt + (role_dk ? 0 : C::kTile);
+    bf16x8 bo[C::NCT][2];
+#pragma unroll
+    for (int ct = 0; ct < C::NCT; ++ct)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) bo[ct][h] = swz_op32_tr_perm<D>(bsrc, 32 * qh + 16 * h, 32 * ct, lane);
     float pf[16];
-    f32x16 dp = {};
     float* pw = psh + (wave & 3) * 16 * 64;   // [e / 4][lane][e % 4] of this (kh, qh)
     if (!role_dk) {
-      f32x16 s = {};
-#pragma unroll
-      for (int cc = 0; cc < C::NCC; ++cc)
-        s = mfma32(as_bf16x8(ld16(qt + swz_off<D>(32 * qh + n32, 16 * cc + 8 * hl))), kf[cc], s);
 #pragma unroll
       for (int e4 = 0; e4 < 4; ++e4) {
         const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lt[32 * qh + 8 * e4 + 4 * hl]);
 #pragma unroll
         for (int x = 0; x < 4; ++x)
-          pf[4 * e4 + x] = __builtin_amdgcn_exp2f(__fmaf_rn(s[4 * e4 + x], sl2, -l4[x] * kLog2e));
+          pf[4 * e4 + x] = __builtin_amdgcn_exp2f(__fmaf_rn(sd[4 * e4 + x], sl2, -l4[x] * kLog2e));
       }
       if (tail_blk) {   // keys past valid_len: no probability mass
 #pragma unroll
@@ -535,10 +593,6 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(
       for (int e4 = 0; e4 < 4; ++e4)
         *reinterpret_cast<f32x4*>(&pw[(e4 * 64 + lane) * 4]) =
             f32x4{pf[4 * e4], pf[4 * e4 + 1], pf[4 * e4 + 2], pf[4 * e4 + 3]};
-    } else {
-#pragma unroll
-      for (int cc = 0; cc < C::NCC; ++cc)
-        dp = mfma32(as_bf16x8(ld16(dt + swz_off<D>(32 * qh + n32, 16 * cc + 8 * hl))), vf[cc], dp);
     }
     // P visible to the dK waves: LDS writes done, then a barrier that does
     // not wait for the next block's copies (the asm also keeps the compiler
@@ -550,18 +604,15 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(
         const f32x4 d4 = *reinterpret_cast<const f32x4*>(&lt[64 + 32 * qh + 8 * e4 + 4 * hl]);
         const f32x4 p4 = *reinterpret_cast<const f32x4*>(&pw[(e4 * 64 + lane) * 4]);
 #pragma unroll
-        for (int x = 0; x < 4; ++x) pf[4 * e4 + x] = p4[x] * (dp[4 * e4 + x] - d4[x]);
+        for (int x = 0; x < 4; ++x) pf[4 * e4 + x] = p4[x] * (sd[4 * e4 + x] - d4[x]);
       }
     }
     const bf16x8 xb[2] = {cvt_bf16x8(pf), cvt_bf16x8(pf + 8)};
-    // dV[key][c] += P^T dO  or  dK[key][a] += dS^T Q  (B operand by transpose
-    // reads, query index in the permuted order of the S tile)
-    const uint16_t* bsrc = qt + (role_dk ? 0 : C::kTile);
+    // dV[key][c] += P^T dO  or  dK[key][a] += dS^T Q
 #pragma unroll
     for (int ct = 0; ct < C::NCT; ++ct)
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-        acc[ct] = mfma32(xb[h], swz_op32_tr_perm<D>(bsrc, 32 * qh + 16 * h, 32 * ct, lane), acc[ct]);
+      for (int h = 0; h < 2; ++h) acc[ct] = mfma32(xb[h], bo[ct][h], acc[ct]);
     __builtin_amdgcn_s_waitcnt(0);   // this wave's copies have landed
     __syncthreads();
   };
@@ -612,11 +663,11 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(
 #pragma unroll
     for (int cc = 0; cc < C::NCC; ++cc) {
       if (role_dk) {
-        af[cc] = vf[cc];
+        af[cc] = bf[cc];
       } else {
 #pragma unroll
         for (int s2 = 0; s2 < 8; ++s2)
-          af[cc][s2] = static_cast<__bf16>(kv_ok ? phi(static_cast<float>(kf[cc][s2])) : 0.f);
+          af[cc][s2] = static_cast<__bf16>(kv_ok ? phi(static_cast<float>(bf[cc][s2])) : 0.f);
       }
     }
 #pragma unroll
