@@ -285,6 +285,22 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(
     }
   };
 
+  // Byte offsets into a swizzled tile.  Row read of key 32 kh + n32 at
+  // head-dim index 16 cc + 8 hl: rowb0 ^ (cc << 5).  Permuted transpose read
+  // at key rows 32 kh + 16 h (+ 8 for the upper half), columns 32 at:
+  // (trb0 ^ (at << 6)) + 32 D h, upper half ^ (16 D + 16).  (The XOR swizzle
+  // touches only the chunk bits, which these identities use.)
+  const uint32_t rowb0 = 2u * swz_off<D>(32 * kh + n32, 8 * hl);
+  const uint32_t trb0 = 2u * swz_off<D>(32 * kh + 4 * hl + ((lane & 15) >> 2),
+                                        16 * ((lane >> 4) & 1) + 4 * (lane & 3));
+  auto row16 = [&](const uint16_t* t, uint32_t boff) __attribute__((always_inline)) {
+    return as_bf16x8(*reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(t) + boff));
+  };
+  auto tr16 = [&](const uint16_t* t, uint32_t boff) __attribute__((always_inline)) {
+    const char* p = reinterpret_cast<const char*>(t);
+    return as_bf16x8(lds_tr4(reinterpret_cast<const uint16_t*>(p + boff)),
+                     lds_tr4(reinterpret_cast<const uint16_t*>(p + (boff ^ (16u * D + 16u)))));
+  };
   // one key block from (kt, vt); the next one is copied into (kn, vn), or
   // this block's dQ rows after the last one
   auto step = [&](int n, const uint16_t* kt, const uint16_t* vt, uint16_t* kn, uint16_t* vn,
@@ -297,12 +313,24 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(
       copy_kv(n + 1, kn, vn);
     else
       copy_dq(reinterpret_cast<float*>(kn), reinterpret_cast<float*>(vn));
+    // the offsets pass through an empty asm each step, so the per-read XORs
+    // are formed next to their reads instead of occupying registers
+    uint32_t rb = rowb0, tb = trb0;
+    asm("" : "+v"(rb), "+v"(tb));
     f32x16 st = {}, dpt = {};
 #pragma unroll
     for (int cc = 0; cc < C::NCC; ++cc) {
-      st = mfma32(as_bf16x8(ld16(kt + swz_off<D>(32 * kh + n32, 16 * cc + 8 * hl))), qf[cc], st);
-      dpt = mfma32(as_bf16x8(ld16(vt + swz_off<D>(32 * kh + n32, 16 * cc + 8 * hl))), dof[cc], dpt);
+      st = mfma32(row16(kt, rb ^ (cc << 5)), qf[cc], st);
+      dpt = mfma32(row16(vt, rb ^ (cc << 5)), dof[cc], dpt);
     }
+    // B operands of dS K (K[keys][a] by transpose reads, keys in the permuted
+    // order of the S^T tile), read before the exponentials so their latency
+    // overlaps them
+    bf16x8 bo[C::NAT][2];
+#pragma unroll
+    for (int at = 0; at < C::NAT; ++at)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) bo[at][h] = tr16(kt, (tb ^ (at << 6)) + 32u * D * h);
     float dsf[16];
 #pragma unroll
     for (int e = 0; e < 16; ++e) dsf[e] = __builtin_amdgcn_exp2f(__fmaf_rn(st[e], sl2, -lse2));
@@ -316,13 +344,11 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(
 #pragma unroll
     for (int e = 0; e < 16; ++e) dsf[e] *= dpt[e] - dsv;
     const bf16x8 ds[2] = {cvt_bf16x8(dsf), cvt_bf16x8(dsf + 8)};
-    // dQ[q][a] += dS[q][keys] K[keys][a]: B operand K[keys of chunk h][a] by
-    // transpose reads, keys in the permuted order of the S^T tile
+    // dQ[q][a] += dS[q][keys] K[keys][a]
 #pragma unroll
     for (int at = 0; at < C::NAT; ++at)
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-        acc[at] = mfma32(ds[h], swz_op32_tr_perm<D>(kt, 32 * kh + 16 * h, 32 * at, lane), acc[at]);
+      for (int h = 0; h < 2; ++h) acc[at] = mfma32(ds[h], bo[at][h], acc[at]);
     __builtin_amdgcn_s_waitcnt(0);   // this wave's copies have landed
     __syncthreads();
   };
