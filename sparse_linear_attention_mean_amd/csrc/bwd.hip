@@ -42,8 +42,10 @@ __global__ void w_transpose_kernel(const uint16_t* __restrict__ w, uint16_t* __r
 //   dq[r][a] = dphi(q)[r][a] phi'(q[r][a])           (initial value of dQ)
 // Rows r >= valid_len and rows with den = 0 get zero linear gradients.
 // Every global read is issued up front: H_i^T and Z_i go straight to LDS
-// with asynchronous copies, the row operands into registers, so their
-// latencies overlap each other and the dY products.
+// with asynchronous copies, the row operands into registers through buffer
+// resources that end at valid_len (no branches around the loads), and the
+// W^T rows of the dY products stream four chunks ahead of their MFMAs, so
+// the latencies overlap each other instead of adding up.
 // ---------------------------------------------------------------------------
 
 template <int D>
@@ -66,7 +68,8 @@ __global__ __launch_bounds__(256, 2) void bwd_prep_kernel(
   const uint32_t wg = xcd_remap(blockIdx.x, gridDim.x);
   const int i = wg % T;
   const long long bh = wg / T;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n32 = lane & 31, hl = lane >> 5;
   const int qh = wave & 1, ch = wave >> 1;
   const size_t head = static_cast<size_t>(bh) * N * D;
@@ -74,61 +77,90 @@ __global__ __launch_bounds__(256, 2) void bwd_prep_kernel(
   const int row = i * kBlock + rloc;   // < N always; rows >= valid_len are read, never used
   const bool valid = row < L;
 
-  // asynchronous copies of H_i^T and Z_i
+  // Every read goes through a buffer resource that ends at valid_len (rows
+  // past it read as zero, no branches), and all of them are issued before
+  // the first product.  H_i^T and Z_i go to LDS with asynchronous copies.
+  // W^T rows (A operand of dY^T), a ring read four chunks ahead of their
+  // products; the first four are issued before everything else
+  constexpr int WA = 4;
+  bf16x8 wa[WA];
+  auto wld = [&](int u) __attribute__((always_inline)) {
+    const int ct = u / NCC, cc = u % NCC;
+    return as_bf16x8(ld16(wT + static_cast<size_t>((D / 2) * ch + 32 * ct + n32) * D + 16 * cc + 8 * hl));
+  };
+#pragma unroll
+  for (int u = 0; u < WA; ++u) wa[u] = wld(u);
+  const uint32_t rbytes = static_cast<uint32_t>(L) * D * 2;
+  const __amdgpu_buffer_rsrc_t drs = make_rsrc(dO + head, rbytes);
+  const __amdgpu_buffer_rsrc_t ors = make_rsrc(o + head, rbytes);
+  const __amdgpu_buffer_rsrc_t yrs = make_rsrc(y + head, rbytes);
+  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(q + head, rbytes);
   if (linear) {
     const size_t hslot = static_cast<size_t>(bh) * T + (hglobal ? 0 : i);
-    copy_swz<D>(hst + hslot * D * D, hs, D, wave, 4, lane);
-    if (wave == 0 && lane < D / 2) gl_to_lds16(zst + hslot * 2 * D + 4 * lane, zs);
-  }
-
-  // dO fragments for dY, and the row pieces of O, Y, dO and Q that match the
-  // dY^T / dphi(q)^T accumulator layout (column 8 e4 + 4 hl + x of each tile)
-  bf16x8 dof[NCC];
-  {
-    const uint16_t* src = dO + head + static_cast<size_t>(row) * D + 8 * hl;
+    const __amdgpu_buffer_rsrc_t hrs = make_rsrc(hst + hslot * D * D, D * D * 2);
 #pragma unroll
-    for (int cc = 0; cc < NCC; ++cc)
-      dof[cc] = valid ? as_bf16x8(ld16(src + 16 * cc)) : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+    for (int r0 = 0; r0 < D; r0 += 64) copy_swz_buf<D, 4>(hrs, r0, hs + r0 * D, wave, lane);
+    if (wave == 0 && lane < D / 2) {
+      const __amdgpu_buffer_rsrc_t zrs = make_rsrc(zst + hslot * 2 * D, 2 * D * 4);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(zrs, (__attribute__((address_space(3))) void*)(zs),
+                                               16, 16 * lane, 0, 0, 0);
+    }
   }
-  const size_t rb = head + static_cast<size_t>(row) * D;
-  u32x2 yv[NT][4], ov[NT][4], dv[NT][4], qv[NT][4];
+  const uint32_t rowb = static_cast<uint32_t>(row) * D * 2;
+  // dO fragments (B operand of dY^T, k = o = 16 cc + 8 hl + s) and O at the
+  // same places of the wave's c half (for dO . O)
+  bf16x8 dof[NCC];
+#pragma unroll
+  for (int cc = 0; cc < NCC; ++cc) dof[cc] = as_bf16x8(buf_ld16(drs, rowb + (16 * cc + 8 * hl) * 2, 0));
+  u32x4 ov[NCC / 2];
+#pragma unroll
+  for (int cc = 0; cc < NCC / 2; ++cc)
+    ov[cc] = buf_ld16(ors, rowb + (16 * ((NCC / 2) * ch + cc) + 8 * hl) * 2, 0);
+  // the row pieces of Y and Q that match the dY^T / dphi(q)^T accumulator
+  // layout (column 8 e4 + 4 hl + x of each tile)
+  u32x2 yv[NT][4], qv[NT][4];
 #pragma unroll
   for (int ct = 0; ct < NT; ++ct)
 #pragma unroll
     for (int e4 = 0; e4 < 4; ++e4) {
-      const int c0 = (D / 2) * ch + 32 * ct + 8 * e4 + 4 * hl;
-      yv[ct][e4] = ld8(y + rb + c0);
-      ov[ct][e4] = ld8(o + rb + c0);
-      dv[ct][e4] = ld8(dO + rb + c0);
-      qv[ct][e4] = ld8(q + rb + c0);
+      const uint32_t c0 = (D / 2) * ch + 32 * ct + 8 * e4 + 4 * hl;
+      yv[ct][e4] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(yrs, rowb + c0 * 2, 0, 0));
+      qv[ct][e4] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(qrs, rowb + c0 * 2, 0, 0));
     }
   const float dn_r = (linear && valid) ? den[bh * N + row] : 0.f;
 
   // dY^T tiles for c in [D/2 ch, D/2 ch + D/2)
   f32x16 dyt[NT];
+  {
 #pragma unroll
-  for (int ct = 0; ct < NT; ++ct) {
-    dyt[ct] = f32x16{};
-    const uint16_t* wr = wT + static_cast<size_t>((D / 2) * ch + 32 * ct + n32) * D + 8 * hl;
+    for (int ct = 0; ct < NT; ++ct) {
+      dyt[ct] = f32x16{};
 #pragma unroll
-    for (int cc = 0; cc < NCC; ++cc) dyt[ct] = mfma32(as_bf16x8(ld16(wr + 16 * cc)), dof[cc], dyt[ct]);
+      for (int cc = 0; cc < NCC; ++cc) {
+        const int u = ct * NCC + cc;
+        const bf16x8 a = wa[u % WA];
+        if (u + WA < NT * NCC) wa[u % WA] = wld(u + WA);
+        dyt[ct] = mfma32(a, dof[cc], dyt[ct]);
+      }
 #pragma unroll
-    for (int e = 0; e < 16; ++e) dyt[ct][e] *= gate;   // dY of the ungated Y (gate 1: exact)
+      for (int e = 0; e < 16; ++e) dyt[ct][e] *= gate;   // dY of the ungated Y (gate 1: exact)
+    }
   }
   // partial row dots over this lane's c values
   float p_oo = 0.f, p_yy = 0.f;
+#pragma unroll
+  for (int cc = 0; cc < NCC / 2; ++cc)
+#pragma unroll
+    for (int s2 = 0; s2 < 8; ++s2)
+      p_oo = __fmaf_rn(static_cast<float>(ch ? dof[NCC / 2 + cc][s2] : dof[cc][s2]),
+                       bf16_to_f32(u4_elem(ov[cc], s2)), p_oo);
 #pragma unroll
   for (int ct = 0; ct < NT; ++ct)
 #pragma unroll
     for (int e4 = 0; e4 < 4; ++e4)
 #pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        const float yy = bf16_to_f32(u4_half(yv[ct][e4], x));
-        const float oo = bf16_to_f32(u4_half(ov[ct][e4], x));
-        const float dd = bf16_to_f32(u4_half(dv[ct][e4], x));
-        p_yy = __fmaf_rn(dyt[ct][4 * e4 + x], yy, p_yy);
-        p_oo = __fmaf_rn(dd, oo, p_oo);
-      }
+      for (int x = 0; x < 4; ++x)
+        p_yy = __fmaf_rn(dyt[ct][4 * e4 + x], bf16_to_f32(u4_half(yv[ct][e4], x)), p_yy);
   p_oo += __shfl_xor(p_oo, 32);
   p_yy += __shfl_xor(p_yy, 32);
   if (hl == 0) {
@@ -163,7 +195,7 @@ __global__ __launch_bounds__(256, 2) void bwd_prep_kernel(
   __builtin_amdgcn_s_waitcnt(0);   // this wave's copies into hs / zs have landed
   __syncthreads();
   // dphi(q)^T[a][r]: wave covers rows half qh and a in [D/2 ch, D/2 ch + D/2)
-  float* dqrow = dq + rb;
+  float* dqrow = dq + head + static_cast<size_t>(row) * D;
   const float ddv = rowd[rloc];
 #pragma unroll
   for (int at = 0; at < NT; ++at) {
