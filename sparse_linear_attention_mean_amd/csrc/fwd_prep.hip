@@ -294,13 +294,16 @@ __global__ __launch_bounds__(256) void scores_kernel(const float* __restrict__ q
 }
 
 // ---------------------------------------------------------------------------
-// classify: one workgroup per row (bh, i).  Keys are 64-bit: the fp32 score
-// mapped to an unsigned code that increases as the score decreases (-0 folded
-// onto +0), in the high word, and the block index in the low word; a bitonic
-// sort in LDS then gives the total order (score descending, index ascending).
-// Positions 0..k_c-1 are critical, T-k_n..T-1 negligible, the rest marginal.
-// Writes the mask row; optionally the ascending critical list and the
-// marginal bit row.  Rows i in [T, Tp) only clear their bit row.
+// classify: one wave per row (bh, i).  A key block's sort key is the pair
+// (code, j): code is the fp32 score mapped to an unsigned value that grows as
+// the score falls (-0 folded onto +0), j the block index.  Positions
+// 0..k_c-1 of the ascending order are critical, T-k_n..T-1 negligible, the
+// rest marginal.  Instead of sorting the row, the key at each of the two
+// boundary positions is found by a radix select on the code (four 8-bit
+// digits, a 256-bin histogram per wave in LDS), and keys whose code equals
+// the boundary code are ranked by index with ballots.  Writes the mask row;
+// optionally the ascending critical list and the marginal bit row.  Rows i
+// in [T, Tp) only clear their bit row.
 // ---------------------------------------------------------------------------
 constexpr int kMaxT = 2048;
 
@@ -308,6 +311,118 @@ __device__ __forceinline__ uint32_t descending_code(float s) {
   uint32_t u = __float_as_uint(s + 0.0f);   // -0 -> +0
   const uint32_t asc = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
   return ~asc;
+}
+
+// NCH: 64-wide chunks a lane walks (at least ceil(T / 64))
+template <int NCH>
+__global__ __launch_bounds__(256) void classify_kernel(const float* __restrict__ scores,
+                                                       int8_t* __restrict__ mask,
+                                                       int32_t* __restrict__ lut,
+                                                       int32_t* __restrict__ lut_cnt,
+                                                       uint32_t* __restrict__ rbits, int T,
+                                                       int Tp, int rows, int kc, int kn) {
+  __shared__ __attribute__((aligned(16))) uint32_t hists[4][256];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int i = blockIdx.x * 4 + wave;
+  const long long bh = blockIdx.y;
+  const int words = Tp / 32;
+  if (i >= rows) return;
+  if (i >= T) {
+    if (rbits)
+      for (int w = lane; w < words; w += 64) rbits[(bh * words + w) * Tp + i] = 0u;
+    return;
+  }
+  uint32_t* hist = hists[wave];
+  const int nch = (T + 63) / 64;
+  const float* row = scores + (bh * T + i) * T;
+  uint32_t code[NCH];
+#pragma unroll
+  for (int u = 0; u < NCH; ++u) {
+    const int j = 64 * u + lane;
+    code[u] = (u < nch && j < T) ? descending_code(row[j]) : 0u;
+  }
+  const unsigned long long lt = (1ull << lane) - 1ull;
+
+  // Radix select: the code of the key at position r (0-based) of the row's
+  // ascending order, and that key's 0-based rank among the keys with the
+  // same code (which are ordered by index).
+  auto select = [&](int r, uint32_t& code_at, int& tie_at) __attribute__((always_inline)) {
+    uint32_t prefix = 0u, pmask = 0u;
+#pragma unroll
+    for (int pass = 0; pass < 4; ++pass) {
+      const int sh = 24 - 8 * pass;
+      *reinterpret_cast<u32x4*>(&hist[4 * lane]) = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int u = 0; u < NCH; ++u) {
+        if (u < nch && 64 * u + lane < T && (code[u] & pmask) == prefix)
+          atomicAdd(&hist[(code[u] >> sh) & 255u], 1u);
+      }
+      const u32x4 hv = *reinterpret_cast<const u32x4*>(&hist[4 * lane]);
+      const int sum = static_cast<int>(hv[0] + hv[1] + hv[2] + hv[3]);
+      int incl = sum;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int t = __shfl_up(incl, d);
+        if (lane >= d) incl += t;
+      }
+      // the first lane whose bins reach past position r holds the digit
+      const unsigned long long hit = __ballot(incl > r);
+      const int src = __builtin_ctzll(hit);
+      int below = incl - sum, digit = 4 * lane;
+#pragma unroll
+      for (int k = 0; k < 3; ++k) {
+        if (below + static_cast<int>(hv[k]) > r) break;
+        below += static_cast<int>(hv[k]);
+        ++digit;
+      }
+      digit = __shfl(digit, src);
+      below = __shfl(below, src);
+      r -= below;
+      prefix |= static_cast<uint32_t>(digit) << sh;
+      pmask |= 0xFFu << sh;
+    }
+    code_at = prefix;
+    tie_at = r;
+  };
+  // critical: positions <= k_c - 1; negligible: positions >= T - k_n
+  uint32_t cc = 0u, cn = 0xFFFFFFFFu;
+  int qc = -1, qn = 1 << 30;
+  if (kc > 0) select(kc - 1, cc, qc);
+  if (kn > 0) select(T - kn, cn, qn);
+
+  int8_t* mrow = mask + (bh * T + i) * T;
+  int32_t* lrow = lut ? lut + (bh * T + i) * T : nullptr;
+  uint32_t* brow = rbits ? rbits + bh * words * Tp + i : nullptr;   // word w at brow[w * Tp]
+  int tc = 0, tn = 0, cnt = 0;
+#pragma unroll
+  for (int u = 0; u < NCH; ++u) {
+    if (u < nch) {
+      const int j = 64 * u + lane;
+      const bool valid = j < T;
+      const uint32_t c = code[u];
+      const bool eqc = valid && kc > 0 && c == cc;
+      const bool eqn = valid && kn > 0 && c == cn;
+      const unsigned long long bc = __ballot(eqc), bn = __ballot(eqn);
+      const int tie_c = tc + __popcll(bc & lt), tie_n = tn + __popcll(bn & lt);
+      tc += __popcll(bc);
+      tn += __popcll(bn);
+      const bool crit = valid && kc > 0 && (c < cc || (eqc && tie_c <= qc));
+      const bool negl = valid && kn > 0 && (c > cn || (eqn && tie_n >= qn));
+      if (valid) mrow[j] = crit ? 1 : (negl ? -1 : 0);
+      const unsigned long long bcrit = __ballot(crit);
+      if (lrow && crit) lrow[cnt + __popcll(bcrit & lt)] = j;
+      cnt += __popcll(bcrit);
+      if (brow) {
+        const unsigned long long bm = __ballot(valid && !crit && !negl);
+        if (lane == 0) {
+          brow[(2 * u) * Tp] = static_cast<uint32_t>(bm);
+          if (2 * u + 1 < words) brow[(2 * u + 1) * Tp] = static_cast<uint32_t>(bm >> 32);
+        }
+      }
+    }
+  }
+  if (lut_cnt && lane == 0) lut_cnt[bh * T + i] = cnt;
 }
 
 // Writes a classified row cls[0..T) (in LDS, complete): the mask row, and
@@ -370,39 +485,6 @@ __device__ void bitonic_sort(unsigned long long* keys, int n2) {
   }
 }
 
-__global__ __launch_bounds__(256) void classify_kernel(const float* __restrict__ scores,
-                                                       int8_t* __restrict__ mask,
-                                                       int32_t* __restrict__ lut,
-                                                       int32_t* __restrict__ lut_cnt,
-                                                       uint32_t* __restrict__ rbits, int T,
-                                                       int Tp, int kc, int kn) {
-  __shared__ unsigned long long keys[kMaxT];
-  __shared__ int8_t cls[kMaxT];
-  const int i = blockIdx.x;
-  const long long bh = blockIdx.y;
-  const int tid = threadIdx.x;
-  const int words = Tp / 32;
-  if (i >= T) {
-    if (rbits)
-      for (int w = tid; w < words; w += 256) rbits[(bh * words + w) * Tp + i] = 0u;
-    return;
-  }
-  int n2 = 1;
-  while (n2 < T) n2 <<= 1;
-  const float* row = scores + (bh * T + i) * T;
-  for (int j = tid; j < n2; j += 256)
-    keys[j] = (j < T) ? ((static_cast<unsigned long long>(descending_code(row[j])) << 32) |
-                         static_cast<unsigned long long>(j))
-                      : ~0ull;
-  __syncthreads();
-  bitonic_sort(keys, n2);
-  for (int p = tid; p < T; p += 256) {
-    const int j = static_cast<int>(keys[p] & 0xffffffffull);
-    cls[j] = p < kc ? 1 : (p >= T - kn ? -1 : 0);
-  }
-  __syncthreads();
-  emit_row(cls, mask, lut, lut_cnt, rbits, bh, i, T, Tp);
-}
 
 // ---------------------------------------------------------------------------
 // Two-level selection, after the abstract of "Trainable Log-linear Sparse
@@ -657,8 +739,13 @@ hipError_t launch_scores(const Dims& d, const float* qbar, const float* kbar, fl
 hipError_t launch_classify(const Dims& d, const float* scores, int8_t* mask, int32_t* lut,
                            int32_t* lut_cnt, uint32_t* rbits, hipStream_t s) {
   const int rows = rbits ? d.Tp : d.T;
-  hipLaunchKernelGGL(classify_kernel, dim3(rows, static_cast<unsigned>(d.BH())), dim3(256), 0, s,
-                     scores, mask, lut, lut_cnt, rbits, d.T, d.Tp, d.kc, d.kn);
+  const dim3 grid((rows + 3) / 4, static_cast<unsigned>(d.BH()));
+  if (d.T <= 512)
+    hipLaunchKernelGGL(classify_kernel<8>, grid, dim3(256), 0, s, scores, mask, lut, lut_cnt, rbits,
+                       d.T, d.Tp, rows, d.kc, d.kn);
+  else
+    hipLaunchKernelGGL(classify_kernel<kMaxT / 64>, grid, dim3(256), 0, s, scores, mask, lut, lut_cnt,
+                       rbits, d.T, d.Tp, rows, d.kc, d.kn);
   return hipGetLastError();
 }
 
