@@ -131,7 +131,7 @@ def test_forward_given_mask(d):
 
 @pytest.mark.parametrize("t,kind", [(37, "workload"), (37, "integers"), (64, "constant"),
                                     (50, "signed_zeros"), (1, "integers"), (2048, "workload"),
-                                    (129, "integers")])
+                                    (129, "integers"), (512, "integers"), (513, "signed_zeros")])
 def test_classify_bit_exact(t, kind):
     """Identical fp32 score maps must give byte-identical masks."""
     rng = np.random.default_rng(t)
