@@ -29,7 +29,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 DEFAULT_WORKLOAD = "video_dit_b2_h12_n32768_d128"
-DOMINANT = {"fwd": "attention", "fwdbwd": "attention"}
+DOMINANT = {"fwd": "attention", "fwdbwd": "bwd_kv"}
 
 
 def parse():
@@ -379,14 +379,35 @@ def main():
     dense_flops = (4.0 + (10.0 if with_bwd else 0.0)) * bh * wl.seq_len ** 2 * d
     value = flops / (ms * 1e-3) / 1e12
 
-    # dominant kernel: the fused forward attention (MFMA-bound)
-    dom = DOMINANT[args.mode]
-    dom_ms = stage_ms.get(dom)
-    linear_flops = (2 * 2.0 * 64 * d * d * bh * t) if k_m > 0 else 0.0
-    dom_flops = flops_fwd_crit + linear_flops
-    achieved = dom_flops / (dom_ms * 1e-3) / 1e12 if dom_ms else None
-    digest = kernel_sources_digest(["attn_fwd.hip", "sla_device.h"])
-    traffic = traffic_from_profile("attn_fwd", wl.name, digest)
+    # Rooflines of the two MFMA-bound kernels, each from its own stage events
+    # (one launch per stage).  Algorithmic flops per launch:
+    #   fused forward attention: 4 b^2 d per critical pair, plus the linear
+    #     branch phi(Q) H_i and Y W^T (2 x 2 b d^2 per query block);
+    #   key-block backward (dK, dV): its share of the 10 b^2 d per critical
+    #     pair, S, dP, P^T dO and dS^T Q (8 b^2 d), plus the linear-branch
+    #     terms phi(K) dh and V dh^T (2 x 2 b d^2 per key block).
+    linear = k_m > 0
+    lin_blk = (2 * 2.0 * 64 * d * d * bh * t) if linear else 0.0
+
+    def roofline(stage, flops_k, label, tag, sources):
+        kms = stage_ms.get(stage)
+        ach = flops_k / (kms * 1e-3) / 1e12 if kms else None
+        return {
+            "kernel": label,
+            "bound": "mfma",
+            "achieved": round(ach, 2) if ach else None,
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(ach / PEAK_BF16_TFLOPS, 4) if ach else None,
+            "traffic": traffic_from_profile(tag, wl.name, kernel_sources_digest(sources)),
+        }
+
+    rl_fwd = roofline("attention", flops_fwd_crit + lin_blk,
+                      "attn_fwd_kernel (fused sparse + linear + projection)", "attn_fwd",
+                      ["attn_fwd.hip", "sla_device.h"])
+    rl_kv = roofline("bwd_kv", 8.0 * 64 * 64 * d * pairs + lin_blk,
+                     "bwd_kv_kernel (key-block backward: dK, dV)", "bwd_kv",
+                     ["bwd.hip", "sla_device.h"]) if with_bwd else None
 
     rec = {
         "metric": "SLA fwd/bwd effective TFLOPS + % bf16 MFMA peak at N=32768,H=12,d=128",
@@ -411,16 +432,10 @@ def main():
         "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "tflops_dense_equivalent": round(dense_flops / (ms * 1e-3) / 1e12, 1),
         "stages_ms": {kk: round(vv, 4) for kk, vv in stage_ms.items()},
-        "roofline": {
-            "kernel": "attn_fwd_kernel (fused sparse + linear + projection)",
-            "bound": "mfma",
-            "achieved": round(achieved, 2) if achieved else None,
-            "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_BF16_TFLOPS, 4) if achieved else None,
-            "traffic": traffic,
-        },
+        "roofline": rl_kv if DOMINANT[args.mode] == "bwd_kv" else rl_fwd,
     }
+    if DOMINANT[args.mode] == "bwd_kv":
+        rec["roofline_attention_fwd"] = rl_fwd
     if with_bwd:
         fwd_ms = sum(stage_ms.get(s, 0.0) for s in B.STAGES[:5])
         bwd_ms = sum(stage_ms.get(s, 0.0) for s in B.STAGES[5:])

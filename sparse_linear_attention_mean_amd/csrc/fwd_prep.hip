@@ -313,6 +313,88 @@ __device__ __forceinline__ uint32_t descending_code(float s) {
   return ~asc;
 }
 
+// Radix select over the keys one wave holds: key 64 u + lane has code
+// code[u] and takes part where ok[u].  Finds the key at position r (0-based)
+// of the ascending (code, index) order: its code, and its rank among the
+// keys with that code (those are ordered by index).  Four passes over 8-bit
+// digits, each a 256-bin histogram in the wave's own LDS words (one wave's
+// LDS accesses execute in order, so no barrier is needed), a prefix sum over
+// the bins and a ballot for the bin that holds position r.
+template <int NC>
+__device__ __forceinline__ void wave_select(const uint32_t (&code)[NC], const bool (&ok)[NC], int r,
+                                            uint32_t* hist, int lane, uint32_t& code_at,
+                                            int& tie_at) {
+  uint32_t prefix = 0u, pmask = 0u;
+#pragma unroll
+  for (int pass = 0; pass < 4; ++pass) {
+    const int sh = 24 - 8 * pass;
+    *reinterpret_cast<u32x4*>(&hist[4 * lane]) = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int u = 0; u < NC; ++u)
+      if (ok[u] && (code[u] & pmask) == prefix) atomicAdd(&hist[(code[u] >> sh) & 255u], 1u);
+    const u32x4 hv = *reinterpret_cast<const u32x4*>(&hist[4 * lane]);
+    const int sum = static_cast<int>(hv[0] + hv[1] + hv[2] + hv[3]);
+    int incl = sum;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int t = __shfl_up(incl, d);
+      if (lane >= d) incl += t;
+    }
+    // the first lane whose bins reach past position r holds the digit
+    const int src = __builtin_ctzll(__ballot(incl > r));
+    int below = incl - sum, digit = 4 * lane;
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      if (below + static_cast<int>(hv[k]) > r) break;
+      below += static_cast<int>(hv[k]);
+      ++digit;
+    }
+    digit = __shfl(digit, src);
+    below = __shfl(below, src);
+    r -= below;
+    prefix |= static_cast<uint32_t>(digit) << sh;
+    pmask |= 0xFFu << sh;
+  }
+  code_at = prefix;
+  tie_at = r;
+}
+
+// One wave writes row i of the mask, and optionally its ascending critical
+// list with the count and its marginal bit row (word-major), from per-chunk
+// flags: key block 64 u + lane is critical where crit[u], negligible where
+// negl[u] (and not critical), marginal otherwise; ok[u]: the block exists.
+template <int NC>
+__device__ __forceinline__ void wave_emit(const bool (&ok)[NC], const bool (&crit)[NC],
+                                          const bool (&negl)[NC], int8_t* __restrict__ mask,
+                                          int32_t* __restrict__ lut, int32_t* __restrict__ lut_cnt,
+                                          uint32_t* __restrict__ rbits, long long bh, int i, int T,
+                                          int Tp, int nch, int lane) {
+  const int words = Tp / 32;
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  int8_t* mrow = mask + (bh * T + i) * T;
+  int32_t* lrow = lut ? lut + (bh * T + i) * T : nullptr;
+  uint32_t* brow = rbits ? rbits + bh * words * Tp + i : nullptr;   // word w at brow[w * Tp]
+  int cnt = 0;
+#pragma unroll
+  for (int u = 0; u < NC; ++u) {
+    if (u < nch) {
+      const int j = 64 * u + lane;
+      if (ok[u]) mrow[j] = crit[u] ? 1 : (negl[u] ? -1 : 0);
+      const unsigned long long bcrit = __ballot(crit[u]);
+      if (lrow && crit[u]) lrow[cnt + __popcll(bcrit & lt)] = j;
+      cnt += __popcll(bcrit);
+      if (brow) {
+        const unsigned long long bm = __ballot(ok[u] && !crit[u] && !negl[u]);
+        if (lane == 0) {
+          brow[(2 * u) * Tp] = static_cast<uint32_t>(bm);
+          if (2 * u + 1 < words) brow[(2 * u + 1) * Tp] = static_cast<uint32_t>(bm >> 32);
+        }
+      }
+    }
+  }
+  if (lut_cnt && lane == 0) lut_cnt[bh * T + i] = cnt;
+}
+
 // NCH: 64-wide chunks a lane walks (at least ceil(T / 64))
 template <int NCH>
 __global__ __launch_bounds__(256) void classify_kernel(const float* __restrict__ scores,
@@ -337,153 +419,35 @@ __global__ __launch_bounds__(256) void classify_kernel(const float* __restrict__
   const int nch = (T + 63) / 64;
   const float* row = scores + (bh * T + i) * T;
   uint32_t code[NCH];
+  bool ok[NCH];
 #pragma unroll
   for (int u = 0; u < NCH; ++u) {
     const int j = 64 * u + lane;
-    code[u] = (u < nch && j < T) ? descending_code(row[j]) : 0u;
+    ok[u] = u < nch && j < T;
+    code[u] = ok[u] ? descending_code(row[j]) : 0u;
   }
-  const unsigned long long lt = (1ull << lane) - 1ull;
-
-  // Radix select: the code of the key at position r (0-based) of the row's
-  // ascending order, and that key's 0-based rank among the keys with the
-  // same code (which are ordered by index).
-  auto select = [&](int r, uint32_t& code_at, int& tie_at) __attribute__((always_inline)) {
-    uint32_t prefix = 0u, pmask = 0u;
-#pragma unroll
-    for (int pass = 0; pass < 4; ++pass) {
-      const int sh = 24 - 8 * pass;
-      *reinterpret_cast<u32x4*>(&hist[4 * lane]) = u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int u = 0; u < NCH; ++u) {
-        if (u < nch && 64 * u + lane < T && (code[u] & pmask) == prefix)
-          atomicAdd(&hist[(code[u] >> sh) & 255u], 1u);
-      }
-      const u32x4 hv = *reinterpret_cast<const u32x4*>(&hist[4 * lane]);
-      const int sum = static_cast<int>(hv[0] + hv[1] + hv[2] + hv[3]);
-      int incl = sum;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const int t = __shfl_up(incl, d);
-        if (lane >= d) incl += t;
-      }
-      // the first lane whose bins reach past position r holds the digit
-      const unsigned long long hit = __ballot(incl > r);
-      const int src = __builtin_ctzll(hit);
-      int below = incl - sum, digit = 4 * lane;
-#pragma unroll
-      for (int k = 0; k < 3; ++k) {
-        if (below + static_cast<int>(hv[k]) > r) break;
-        below += static_cast<int>(hv[k]);
-        ++digit;
-      }
-      digit = __shfl(digit, src);
-      below = __shfl(below, src);
-      r -= below;
-      prefix |= static_cast<uint32_t>(digit) << sh;
-      pmask |= 0xFFu << sh;
-    }
-    code_at = prefix;
-    tie_at = r;
-  };
   // critical: positions <= k_c - 1; negligible: positions >= T - k_n
   uint32_t cc = 0u, cn = 0xFFFFFFFFu;
   int qc = -1, qn = 1 << 30;
-  if (kc > 0) select(kc - 1, cc, qc);
-  if (kn > 0) select(T - kn, cn, qn);
-
-  int8_t* mrow = mask + (bh * T + i) * T;
-  int32_t* lrow = lut ? lut + (bh * T + i) * T : nullptr;
-  uint32_t* brow = rbits ? rbits + bh * words * Tp + i : nullptr;   // word w at brow[w * Tp]
-  int tc = 0, tn = 0, cnt = 0;
+  if (kc > 0) wave_select(code, ok, kc - 1, hist, lane, cc, qc);
+  if (kn > 0) wave_select(code, ok, T - kn, hist, lane, cn, qn);
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  bool crit[NCH], negl[NCH];
+  int tc = 0, tn = 0;
 #pragma unroll
   for (int u = 0; u < NCH; ++u) {
-    if (u < nch) {
-      const int j = 64 * u + lane;
-      const bool valid = j < T;
-      const uint32_t c = code[u];
-      const bool eqc = valid && kc > 0 && c == cc;
-      const bool eqn = valid && kn > 0 && c == cn;
-      const unsigned long long bc = __ballot(eqc), bn = __ballot(eqn);
-      const int tie_c = tc + __popcll(bc & lt), tie_n = tn + __popcll(bn & lt);
-      tc += __popcll(bc);
-      tn += __popcll(bn);
-      const bool crit = valid && kc > 0 && (c < cc || (eqc && tie_c <= qc));
-      const bool negl = valid && kn > 0 && (c > cn || (eqn && tie_n >= qn));
-      if (valid) mrow[j] = crit ? 1 : (negl ? -1 : 0);
-      const unsigned long long bcrit = __ballot(crit);
-      if (lrow && crit) lrow[cnt + __popcll(bcrit & lt)] = j;
-      cnt += __popcll(bcrit);
-      if (brow) {
-        const unsigned long long bm = __ballot(valid && !crit && !negl);
-        if (lane == 0) {
-          brow[(2 * u) * Tp] = static_cast<uint32_t>(bm);
-          if (2 * u + 1 < words) brow[(2 * u + 1) * Tp] = static_cast<uint32_t>(bm >> 32);
-        }
-      }
-    }
+    const bool eqc = ok[u] && kc > 0 && code[u] == cc;
+    const bool eqn = ok[u] && kn > 0 && code[u] == cn;
+    const unsigned long long bc = __ballot(eqc), bn = __ballot(eqn);
+    const int tie_c = tc + __popcll(bc & lt), tie_n = tn + __popcll(bn & lt);
+    tc += __popcll(bc);
+    tn += __popcll(bn);
+    crit[u] = ok[u] && kc > 0 && (code[u] < cc || (eqc && tie_c <= qc));
+    negl[u] = ok[u] && kn > 0 && (code[u] > cn || (eqn && tie_n >= qn));
   }
-  if (lut_cnt && lane == 0) lut_cnt[bh * T + i] = cnt;
+  wave_emit(ok, crit, negl, mask, lut, lut_cnt, rbits, bh, i, T, Tp, nch, lane);
 }
 
-// Writes a classified row cls[0..T) (in LDS, complete): the mask row, and
-// optionally the ascending critical list with its length and the marginal bits
-// of the row (word-major).  Called by all 256 threads of the workgroup.
-__device__ void emit_row(const int8_t* cls, int8_t* __restrict__ mask, int32_t* __restrict__ lut,
-                         int32_t* __restrict__ lut_cnt, uint32_t* __restrict__ rbits, long long bh,
-                         int i, int T, int Tp) {
-  const int tid = threadIdx.x;
-  const int words = Tp / 32;
-  int8_t* mrow = mask + (bh * T + i) * T;
-  for (int j = tid; j < T; j += 256) mrow[j] = cls[j];
-  if (tid < 64) {
-    const int lane = tid;
-    if (lut) {
-      int cnt = 0;
-      int32_t* lrow = lut + (bh * T + i) * T;
-      for (int base = 0; base < T; base += 64) {
-        const int j = base + lane;
-        const bool f = j < T && cls[j] == 1;
-        const unsigned long long bal = __ballot(f);
-        if (f) lrow[cnt + __popcll(bal & ((1ull << lane) - 1ull))] = j;
-        cnt += __popcll(bal);
-      }
-      if (lane == 0) lut_cnt[bh * T + i] = cnt;
-    }
-    if (rbits) {
-      uint32_t* brow = rbits + bh * words * Tp + i;   // word w of this row at brow[w * Tp]
-      for (int base = 0; base < Tp; base += 64) {
-        const int j = base + lane;
-        const bool f = j < T && cls[j] == 0;
-        const unsigned long long bal = __ballot(f);
-        if (lane == 0) {
-          brow[(base / 32) * Tp] = static_cast<uint32_t>(bal);
-          if (base / 32 + 1 < words) brow[(base / 32 + 1) * Tp] = static_cast<uint32_t>(bal >> 32);
-        }
-      }
-    }
-  }
-}
-
-// In-place bitonic sort (ascending) of keys[0, n2) in LDS, n2 a power of two;
-// called by all 256 threads, ends synchronised.
-__device__ void bitonic_sort(unsigned long long* keys, int n2) {
-  const int tid = threadIdx.x;
-  for (int size = 2; size <= n2; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int t = tid; t < n2 / 2; t += 256) {
-        const int lo = 2 * t - (t & (stride - 1));
-        const int hi = lo + stride;
-        const bool up = ((lo & size) == 0);
-        const unsigned long long a = keys[lo], b = keys[hi];
-        if ((a > b) == up) {
-          keys[lo] = b;
-          keys[hi] = a;
-        }
-      }
-      __syncthreads();
-    }
-  }
-}
 
 
 // ---------------------------------------------------------------------------
@@ -544,92 +508,134 @@ __global__ __launch_bounds__(256) void coarse_scores_kernel(const float* __restr
     coarse[(bh * T + i) * Tg + g] = ordered_score(qs, kgbar + (bh * Tg + g) * D, D, scale);
 }
 
-// one workgroup per row (bh, i): coarse keys (computed, or read from
-// coarse_in) sorted to pick the kept and negligible groups, then the fine keys
-// of the candidate blocks (computed, or read from scores_in) sorted to pick the
-// critical ones; the row is written like the flat classifier's.
+// One wave per row (bh, i).  Level 1: the coarse keys of the Tg groups
+// (computed, or read from coarse_in); the keys at positions keep - 1 and
+// Tg - n_g of their ascending (code, index) order are found by the radix
+// select, which marks the kept groups (positions < keep) and the negligible
+// ones (positions >= Tg - n_g).  Level 2: the blocks of the kept groups,
+// compacted in block order into candidate slots, get fine keys (computed, or
+// read from scores_in); the key at position k_c - 1 of their order bounds
+// the critical blocks.  Blocks of negligible groups that are not critical are
+// negligible, the rest marginal; the row is written like the flat
+// classifier's.  NC: 64-wide chunks a lane walks (at least ceil(T / 64)).
+template <int NC>
 __global__ __launch_bounds__(256) void classify_hier_kernel(
     const float* __restrict__ qbar, const float* __restrict__ kgbar,
     const float* __restrict__ kbar, const float* __restrict__ coarse_in,
     const float* __restrict__ scores_in, int8_t* __restrict__ mask, int32_t* __restrict__ lut,
     int32_t* __restrict__ lut_cnt, uint32_t* __restrict__ rbits, int T, int Tp, int D, int G,
-    int Tg, int keep, int ng, int kc, float scale) {
-  __shared__ unsigned long long keys[kMaxT];
-  __shared__ int8_t cls[kMaxT];
-  __shared__ uint8_t gflag[kMaxT];   // bit 0: kept, bit 1: negligible
-  __shared__ int kpre[kMaxT];        // kept groups before group g
-  __shared__ __attribute__((aligned(16))) float qs[128];
-  const int i = blockIdx.x;
+    int Tg, int keep, int ng, int kc, float scale, int rows) {
+  __shared__ __attribute__((aligned(16))) uint32_t hists[4][256];
+  __shared__ __attribute__((aligned(16))) float qsh[4][128];
+  __shared__ uint8_t gfl[4][kMaxT];    // per group: bit 0 kept, bit 1 negligible
+  __shared__ int16_t candj[4][kMaxT];  // candidate slot -> block
+  __shared__ int8_t crs[4][kMaxT];     // per block: critical
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int i = blockIdx.x * 4 + wave;
   const long long bh = blockIdx.y;
-  const int tid = threadIdx.x;
-  const int words = Tp / 32;
+  if (i >= rows) return;
   if (i >= T) {
+    const int words = Tp / 32;
     if (rbits)
-      for (int w = tid; w < words; w += 256) rbits[(bh * words + w) * Tp + i] = 0u;
+      for (int w = lane; w < words; w += 64) rbits[(bh * words + w) * Tp + i] = 0u;
     return;
   }
+  uint32_t* hist = hists[wave];
+  float* qs = qsh[wave];
   const bool given = coarse_in != nullptr;
   if (!given)
-    for (int a = tid; a < D; a += 256) qs[a] = qbar[(bh * T + i) * D + a];
-  __syncthreads();
+    for (int a = lane; a < D; a += 64) qs[a] = qbar[(bh * T + i) * D + a];
+  __builtin_amdgcn_wave_barrier();
+  const unsigned long long lt = (1ull << lane) - 1ull;
+
   // ---- level 1: groups
-  int n2 = 1;
-  while (n2 < Tg) n2 <<= 1;
-  for (int g = tid; g < n2; g += 256) {
-    unsigned long long key = ~0ull;
-    if (g < Tg) {
-      const float c = given ? coarse_in[(bh * T + i) * Tg + g]
-                            : ordered_score(qs, kgbar + (bh * Tg + g) * D, D, scale);
-      key = (static_cast<unsigned long long>(descending_code(c)) << 32) |
-            static_cast<unsigned long long>(g);
-    }
-    keys[g] = key;
+  const int ngc = (Tg + 63) / 64;
+  uint32_t gcode[NC];
+  bool gok[NC];
+#pragma unroll
+  for (int u = 0; u < NC; ++u) {
+    const int g = 64 * u + lane;
+    gok[u] = u < ngc && g < Tg;
+    gcode[u] = gok[u] ? descending_code(given ? coarse_in[(bh * T + i) * Tg + g]
+                                              : ordered_score(qs, kgbar + (bh * Tg + g) * D, D, scale))
+                      : 0u;
   }
-  __syncthreads();
-  bitonic_sort(keys, n2);
-  for (int p = tid; p < Tg; p += 256) {
-    const int g = static_cast<int>(keys[p] & 0xffffffffull);
-    gflag[g] = static_cast<uint8_t>((p < keep ? 1 : 0) | (p >= Tg - ng ? 2 : 0));
-  }
-  __syncthreads();
-  // candidates in block order: kept groups ascending (only the last group can
-  // be short, so a kept group's first candidate slot is G times the kept
-  // groups before it)
-  if (tid < 64) {
-    int cnt = 0;
-    for (int base = 0; base < Tg; base += 64) {
-      const int g = base + tid;
-      const bool f = g < Tg && (gflag[g] & 1);
-      const unsigned long long bal = __ballot(f);
-      if (g < Tg) kpre[g] = cnt + __popcll(bal & ((1ull << tid) - 1ull));
-      cnt += __popcll(bal);
+  uint32_t ck = 0u, cn = 0xFFFFFFFFu;
+  int qk = -1, qn = 1 << 30;
+  wave_select(gcode, gok, keep - 1, hist, lane, ck, qk);
+  if (ng > 0) wave_select(gcode, gok, Tg - ng, hist, lane, cn, qn);
+  {
+    int tk = 0, tn = 0;
+#pragma unroll
+    for (int u = 0; u < NC; ++u) {
+      const bool eqk = gok[u] && gcode[u] == ck;
+      const bool eqn = gok[u] && ng > 0 && gcode[u] == cn;
+      const unsigned long long bk = __ballot(eqk), bn = __ballot(eqn);
+      const int tie_k = tk + __popcll(bk & lt), tie_n = tn + __popcll(bn & lt);
+      tk += __popcll(bk);
+      tn += __popcll(bn);
+      const bool kept = gok[u] && (gcode[u] < ck || (eqk && tie_k <= qk));
+      const bool negl = gok[u] && ng > 0 && (gcode[u] > cn || (eqn && tie_n >= qn));
+      if (gok[u]) gfl[wave][64 * u + lane] = static_cast<uint8_t>((kept ? 1 : 0) | (negl ? 2 : 0));
     }
   }
-  __syncthreads();
-  // ---- level 2: fine keys of the candidate blocks (keep groups of G blocks,
-  // less the missing blocks of the short last group when it is kept)
-  const int ncand = keep * G - ((gflag[Tg - 1] & 1) ? Tg * G - T : 0);
-  int m2 = 1;
-  while (m2 < ncand) m2 <<= 1;
-  for (int p = tid; p < m2; p += 256) keys[p] = ~0ull;
-  __syncthreads();
-  for (int j = tid; j < T; j += 256) {
-    const int g = j / G;
-    if (gflag[g] & 1) {
-      const float sc = given ? scores_in[(bh * T + i) * T + j]
-                             : ordered_score(qs, kbar + (bh * T + j) * D, D, scale);
-      keys[kpre[g] * G + (j - g * G)] =
-          (static_cast<unsigned long long>(descending_code(sc)) << 32) |
-          static_cast<unsigned long long>(j);
+  __builtin_amdgcn_wave_barrier();
+
+  // ---- level 2: the blocks of the kept groups into candidate slots, in
+  // block order (so slot order breaks ties like block order)
+  const int nch = (T + 63) / 64;
+  int ncand = 0;
+#pragma unroll
+  for (int u = 0; u < NC; ++u) {
+    if (u < nch) {
+      const int j = 64 * u + lane;
+      const bool c = j < T && (gfl[wave][j / G] & 1);
+      crs[wave][j] = 0;
+      const unsigned long long bc = __ballot(c);
+      if (c) candj[wave][ncand + __popcll(bc & lt)] = static_cast<int16_t>(j);
+      ncand += __popcll(bc);
     }
   }
-  __syncthreads();
-  bitonic_sort(keys, m2);
-  for (int j = tid; j < T; j += 256) cls[j] = (gflag[j / G] & 2) ? -1 : 0;
-  __syncthreads();
-  for (int p = tid; p < kc; p += 256) cls[static_cast<int>(keys[p] & 0xffffffffull)] = 1;
-  __syncthreads();
-  emit_row(cls, mask, lut, lut_cnt, rbits, bh, i, T, Tp);
+  __builtin_amdgcn_wave_barrier();
+  const int ncc = (ncand + 63) / 64;
+  uint32_t fcode[NC];
+  bool fok[NC];
+#pragma unroll
+  for (int u = 0; u < NC; ++u) {
+    const int sl = 64 * u + lane;
+    fok[u] = u < ncc && sl < ncand;
+    fcode[u] = 0u;
+    if (fok[u]) {
+      const int j = candj[wave][sl];
+      fcode[u] = descending_code(given ? scores_in[(bh * T + i) * T + j]
+                                       : ordered_score(qs, kbar + (bh * T + j) * D, D, scale));
+    }
+  }
+  if (kc > 0) {
+    uint32_t cc;
+    int qc;
+    wave_select(fcode, fok, kc - 1, hist, lane, cc, qc);
+    int tc = 0;
+#pragma unroll
+    for (int u = 0; u < NC; ++u) {
+      const bool eqc = fok[u] && fcode[u] == cc;
+      const unsigned long long bc = __ballot(eqc);
+      const int tie_c = tc + __popcll(bc & lt);
+      tc += __popcll(bc);
+      if (fok[u] && (fcode[u] < cc || (eqc && tie_c <= qc))) crs[wave][candj[wave][64 * u + lane]] = 1;
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+  bool ok[NC], crit[NC], negl[NC];
+#pragma unroll
+  for (int u = 0; u < NC; ++u) {
+    const int j = 64 * u + lane;
+    ok[u] = u < nch && j < T;
+    crit[u] = ok[u] && crs[wave][j] != 0;
+    negl[u] = ok[u] && !crit[u] && (gfl[wave][j / G] & 2);
+  }
+  wave_emit(ok, crit, negl, mask, lut, lut_cnt, rbits, bh, i, T, Tp, nch, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -768,9 +774,19 @@ hipError_t launch_classify_hier(const Dims& d, const float* qbar, const float* k
                                 int8_t* mask, int32_t* lut, int32_t* lut_cnt, uint32_t* rbits,
                                 hipStream_t s) {
   const int rows = rbits ? d.Tp : d.T;
-  hipLaunchKernelGGL(classify_hier_kernel, dim3(rows, static_cast<unsigned>(d.BH())), dim3(256), 0,
-                     s, qbar, kgbar, kbar, coarse_in, scores_in, mask, lut, lut_cnt, rbits, d.T,
-                     d.Tp, d.D, d.G, d.Tg, d.keep, d.ng, d.kc, d.scale);
+  const dim3 grid((rows + 3) / 4, static_cast<unsigned>(d.BH()));
+  if (d.T <= 512)
+    hipLaunchKernelGGL(classify_hier_kernel<8>, grid, dim3(256), 0, s, qbar, kgbar, kbar, coarse_in,
+                       scores_in, mask, lut, lut_cnt, rbits, d.T, d.Tp, d.D, d.G, d.Tg, d.keep,
+                       d.ng, d.kc, d.scale, rows);
+  else if (d.T <= 1024)
+    hipLaunchKernelGGL(classify_hier_kernel<16>, grid, dim3(256), 0, s, qbar, kgbar, kbar, coarse_in,
+                       scores_in, mask, lut, lut_cnt, rbits, d.T, d.Tp, d.D, d.G, d.Tg, d.keep,
+                       d.ng, d.kc, d.scale, rows);
+  else
+    hipLaunchKernelGGL(classify_hier_kernel<kMaxT / 64>, grid, dim3(256), 0, s, qbar, kgbar, kbar,
+                       coarse_in, scores_in, mask, lut, lut_cnt, rbits, d.T, d.Tp, d.D, d.G, d.Tg,
+                       d.keep, d.ng, d.kc, d.scale, rows);
   return hipGetLastError();
 }
 
