@@ -54,6 +54,9 @@ HIER_CASES = [
     (33, 1, 33, 0.2, 0.3),     # unit groups, all kept: the flat split
     (129, 16, 5, 0.1, 0.2),
     (1024, 8, 8, 0.02, 0.2),   # the long-sequence workload's split
+    (600, 4, 40, 0.05, 0.1),   # 160 candidate blocks (several 64-wide chunks)
+    (1500, 16, 20, 0.02, 0.1), # more than 1024 blocks, short last group
+    (2048, 2, 1024, 0.05, 0.05),  # every group kept: all 2048 blocks are candidates
 ]
 
 
