@@ -841,17 +841,18 @@ __global__ __launch_bounds__(256) void dw_part_kernel(const uint16_t* __restrict
     for (int e = 0; e < 16; ++e) {
       const int c = 32 * ct + 8 * (e / 4) + 4 * (lane >> 5) + (e % 4);
       const int o = 32 * ot + n32;
-      out[static_cast<size_t>(o) * D + c] = acc[x][e];   // dW[o][c]
+      out[static_cast<size_t>(c) * D + o] = acc[x][e];   // dW^T[c][o]: lanes on consecutive o
     }
   }
 }
 
-// Fixed-order reduction of the partials: workgroup of 256 threads per 64
-// entries; thread group g (of 4) sums partials g, g + 4, ... in order, and the
-// four group sums are added in order; times the linear-output gate (1 for SLA).
+// Fixed-order reduction of the partials (stored transposed, entry e = c D + o):
+// workgroup of 256 threads per 64 entries; thread group g (of 4) sums
+// partials g, g + 4, ... in order, and the four group sums are added in order;
+// times the linear-output gate (1 for SLA); written to dW[o][c].
 __global__ __launch_bounds__(256) void dw_reduce_kernel(const float* __restrict__ part,
-                                                        float* __restrict__ dw, int DD, int parts,
-                                                        float gate) {
+                                                        float* __restrict__ dw, int DD, int D,
+                                                        int parts, float gate) {
   __shared__ float red[4][64];
   const int tid = threadIdx.x, g = tid >> 6;
   const int e = blockIdx.x * 64 + (tid & 63);
@@ -869,7 +870,8 @@ __global__ __launch_bounds__(256) void dw_reduce_kernel(const float* __restrict_
   }
   red[g][tid & 63] = s;
   __syncthreads();
-  if (g == 0 && e < DD) dw[e] = gate * (((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid]);
+  if (g == 0 && e < DD)
+    dw[(e % D) * D + e / D] = gate * (((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid]);
 }
 
 // ---------------------------------------------------------------------------
@@ -934,8 +936,8 @@ hipError_t launch_dw(const Dims& d, const uint16_t* y, const uint16_t* dO, float
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int dd = d.D * d.D;
-  hipLaunchKernelGGL(dw_reduce_kernel, dim3((dd + 63) / 64), dim3(256), 0, s, part, dw, dd, parts,
-                     d.gate);
+  hipLaunchKernelGGL(dw_reduce_kernel, dim3((dd + 63) / 64), dim3(256), 0, s, part, dw, dd, d.D,
+                     parts, d.gate);
   return hipGetLastError();
 }
 

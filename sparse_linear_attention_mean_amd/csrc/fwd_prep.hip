@@ -223,12 +223,14 @@ __global__ __launch_bounds__(2 * D) void pool_kernel(const uint16_t* __restrict_
   const int i = static_cast<int>(r % T);
   const int tid = threadIdx.x;
   const int cg = tid % (D / 8), c = tid / (D / 8);
-  const uint16_t* src = x + (static_cast<size_t>(bh) * N + static_cast<size_t>(i) * kBlock) * D + 8 * cg;
+  // rows past valid_len read as zero through the bounded resource (no branches)
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(x + static_cast<size_t>(bh) * N * D,
+                                              static_cast<uint32_t>(L) * D * 2);
   const int nvalid = min(kBlock, L - i * kBlock);
   u32x4 v[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t)
-    v[t] = 4 * c + t < nvalid ? ld16(src + static_cast<size_t>(4 * c + t) * D) : u32x4{0u, 0u, 0u, 0u};
+    v[t] = buf_ld16(rs, static_cast<uint32_t>((i * kBlock + 4 * c + t) * D + 8 * cg) * 2u, 0);
   float s[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
