@@ -117,17 +117,34 @@ __global__ __launch_bounds__(256, 2) void bwd_prep_kernel(
   for (int cc = 0; cc < NCC / 2; ++cc)
     ov[cc] = buf_ld16(ors, rowb + (16 * ((NCC / 2) * ch + cc) + 8 * hl) * 2, 0);
   // the row pieces of Y and Q that match the dY^T / dphi(q)^T accumulator
-  // layout (column 8 e4 + 4 hl + x of each tile)
+  // layout: lane (row, hl) needs columns 8 e4 + 4 hl .. + 3 of each 32-wide
+  // tile.  Each lane loads 16 bytes, columns 16 p + 8 hl .. + 7, and the two
+  // lanes of a row swap the halves the other one needs (lanes l and l + 32:
+  // v_permlane32_swap), so a row's 64 bytes of a tile take two loads.
+  u32x4 yl[NT][2], ql[NT][2];
+#pragma unroll
+  for (int ct = 0; ct < NT; ++ct)
+#pragma unroll
+    for (int p2 = 0; p2 < 2; ++p2) {
+      const uint32_t c0 = (D / 2) * ch + 32 * ct + 16 * p2 + 8 * hl;
+      yl[ct][p2] = buf_ld16(yrs, rowb + c0 * 2, 0);
+      ql[ct][p2] = buf_ld16(qrs, rowb + c0 * 2, 0);
+    }
+  auto halves = [&](const u32x4& x, u32x2& even, u32x2& odd) __attribute__((always_inline)) {
+    const auto s0 = __builtin_amdgcn_permlane32_swap(x[0], x[2], false, false);
+    const auto s1 = __builtin_amdgcn_permlane32_swap(x[1], x[3], false, false);
+    even = u32x2{s0[0], s1[0]};   // e4 = 2 p: columns 16 p + 4 hl .. + 3
+    odd = u32x2{s0[1], s1[1]};    // e4 = 2 p + 1: columns 16 p + 8 + 4 hl .. + 3
+  };
+  const float dn_r = (linear && valid) ? den[bh * N + row] : 0.f;
   u32x2 yv[NT][4], qv[NT][4];
 #pragma unroll
   for (int ct = 0; ct < NT; ++ct)
 #pragma unroll
-    for (int e4 = 0; e4 < 4; ++e4) {
-      const uint32_t c0 = (D / 2) * ch + 32 * ct + 8 * e4 + 4 * hl;
-      yv[ct][e4] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(yrs, rowb + c0 * 2, 0, 0));
-      qv[ct][e4] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(qrs, rowb + c0 * 2, 0, 0));
+    for (int p2 = 0; p2 < 2; ++p2) {
+      halves(yl[ct][p2], yv[ct][2 * p2], yv[ct][2 * p2 + 1]);
+      halves(ql[ct][p2], qv[ct][2 * p2], qv[ct][2 * p2 + 1]);
     }
-  const float dn_r = (linear && valid) ? den[bh * N + row] : 0.f;
 
   // dY^T tiles for c in [D/2 ch, D/2 ch + D/2)
   f32x16 dyt[NT];
@@ -178,9 +195,8 @@ __global__ __launch_bounds__(256, 2) void bwd_prep_kernel(
     ddel[bh * N + row] = dd_r;
     rowd[rloc] = dd_r;
   }
-  // dN = dY / den (bf16) to global and LDS
+  // dN = dY / den (bf16) into LDS, then to global memory from there
   {
-    uint16_t* dst = dn + head + static_cast<size_t>(row) * D;
 #pragma unroll
     for (int ct = 0; ct < NT; ++ct)
 #pragma unroll
@@ -188,12 +204,22 @@ __global__ __launch_bounds__(256, 2) void bwd_prep_kernel(
         const int c0 = (D / 2) * ch + 32 * ct + 8 * e4 + 4 * hl;
         const u32x2 v = {pack_bf16x2(dyt[ct][4 * e4] * rden, dyt[ct][4 * e4 + 1] * rden),
                          pack_bf16x2(dyt[ct][4 * e4 + 2] * rden, dyt[ct][4 * e4 + 3] * rden)};
-        st8(dst + c0, v);
         st8(&dns[rloc * HP + c0], v);
       }
   }
   __builtin_amdgcn_s_waitcnt(0);   // this wave's copies into hs / zs have landed
   __syncthreads();
+  {
+    // the block's dN rows, 16 contiguous bytes per lane (whole rows per
+    // instruction instead of one row per lane)
+    uint16_t* dblk = dn + head + static_cast<size_t>(i) * kBlock * D;
+#pragma unroll
+    for (int u = 0; u < kBlock * D / 8 / 256; ++u) {
+      const int e = tid + 256 * u;
+      const int r = e / (D / 8), c8 = e % (D / 8);
+      st16(dblk + static_cast<size_t>(r) * D + 8 * c8, ld16(&dns[r * HP + 8 * c8]));
+    }
+  }
   // dphi(q)^T[a][r]: wave covers rows half qh and a in [D/2 ch, D/2 ch + D/2)
   float* dqrow = dq + head + static_cast<size_t>(row) * D;
   const float ddv = rowd[rloc];
