@@ -41,11 +41,13 @@ __global__ void w_transpose_kernel(const uint16_t* __restrict__ w, uint16_t* __r
 //   dphi(q)^T[a][r] = sum_c H[a][c] dN[r][c] + dd_r Z[a]  (wave: rows half, a half)
 //   dq[r][a] = dphi(q)[r][a] phi'(q[r][a])           (initial value of dQ)
 // Rows r >= valid_len and rows with den = 0 get zero linear gradients.
-// Every global read is issued up front: H_i^T and Z_i go straight to LDS
-// with asynchronous copies, the row operands into registers through buffer
-// resources that end at valid_len (no branches around the loads), and the
-// W^T rows of the dY products stream four chunks ahead of their MFMAs, so
-// the latencies overlap each other instead of adding up.
+// Every global read of the first phase is issued up front, through buffer
+// resources that end at valid_len (no branches around the loads): W^T, the dO
+// tile and Z_i by asynchronous copies into LDS (whole rows per instruction),
+// O in 16 contiguous bytes per lane, the Y and Q pieces of each lane's rows
+// as 16-byte loads whose halves two lanes exchange.  Rows per lane would
+// cost one texture-address pass per row touched, which is what limited this
+// kernel.  H_i^T follows into the W^T buffer once the dY products are done.
 // ---------------------------------------------------------------------------
 
 template <int D>
@@ -59,10 +61,13 @@ __global__ __launch_bounds__(256, 2) void bwd_prep_kernel(
   constexpr int HP = D + 8;    // dN row pitch
   constexpr int NCC = D / 16;
   constexpr int NT = D / 64;   // 32-wide tiles per wave in each half
-  __shared__ __attribute__((aligned(16))) uint16_t hs[D * D];     // H^T[c][a], swizzled tile
-  __shared__ __attribute__((aligned(16))) uint16_t dns[64 * HP];  // dN[r][c]
+  // W^T[c][o] (swizzled) for the dY products, then H^T[c][a] (swizzled)
+  __shared__ __attribute__((aligned(16))) uint16_t hs[D * D];
+  // the dO tile (swizzled, unpadded) for the dY products, then dN[r][c] (pitch HP)
+  __shared__ __attribute__((aligned(16))) uint16_t dns[64 * HP];
   __shared__ __attribute__((aligned(16))) float zs[2 * D];        // Z_i (two parts)
-  __shared__ float red[2][2][64];                                 // [c half][dO.O, dY.Y][row]
+  __shared__ float red_oo[64];                                    // dO . O per row
+  __shared__ float red_yy[2][64];                                 // dY . Y per c half and row
   __shared__ float rowd[64];
 
   const uint32_t wg = xcd_remap(blockIdx.x, gridDim.x);
@@ -78,44 +83,38 @@ __global__ __launch_bounds__(256, 2) void bwd_prep_kernel(
   const bool valid = row < L;
 
   // Every read goes through a buffer resource that ends at valid_len (rows
-  // past it read as zero, no branches), and all of them are issued before
-  // the first product.  H_i^T and Z_i go to LDS with asynchronous copies.
-  // W^T rows (A operand of dY^T), a ring read four chunks ahead of their
-  // products; the first four are issued before everything else
-  constexpr int WA = 4;
-  bf16x8 wa[WA];
-  auto wld = [&](int u) __attribute__((always_inline)) {
-    const int ct = u / NCC, cc = u % NCC;
-    return as_bf16x8(ld16(wT + static_cast<size_t>((D / 2) * ch + 32 * ct + n32) * D + 16 * cc + 8 * hl));
-  };
-#pragma unroll
-  for (int u = 0; u < WA; ++u) wa[u] = wld(u);
+  // past it read as zero, no branches) and is issued before the first
+  // product.  W^T (the A operand of dY^T, the same for every workgroup) and
+  // the dO tile arrive by asynchronous copies, whole rows per instruction,
+  // into the buffers that later hold H_i^T and dN; H_i^T is copied in once
+  // the dY products are done with W^T.
   const uint32_t rbytes = static_cast<uint32_t>(L) * D * 2;
   const __amdgpu_buffer_rsrc_t drs = make_rsrc(dO + head, rbytes);
   const __amdgpu_buffer_rsrc_t ors = make_rsrc(o + head, rbytes);
   const __amdgpu_buffer_rsrc_t yrs = make_rsrc(y + head, rbytes);
   const __amdgpu_buffer_rsrc_t qrs = make_rsrc(q + head, rbytes);
-  if (linear) {
-    const size_t hslot = static_cast<size_t>(bh) * T + (hglobal ? 0 : i);
-    const __amdgpu_buffer_rsrc_t hrs = make_rsrc(hst + hslot * D * D, D * D * 2);
+  {
+    const __amdgpu_buffer_rsrc_t wrs = make_rsrc(wT, D * D * 2);
 #pragma unroll
-    for (int r0 = 0; r0 < D; r0 += 64) copy_swz_buf<D, 4>(hrs, r0, hs + r0 * D, wave, lane);
-    if (wave == 0 && lane < D / 2) {
-      const __amdgpu_buffer_rsrc_t zrs = make_rsrc(zst + hslot * 2 * D, 2 * D * 4);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(zrs, (__attribute__((address_space(3))) void*)(zs),
-                                               16, 16 * lane, 0, 0, 0);
-    }
+    for (int r0 = 0; r0 < D; r0 += 64) copy_swz_buf<D, 4>(wrs, r0, hs + r0 * D, wave, lane);
+  }
+  copy_swz_buf<D, 4>(drs, i * kBlock, dns, wave, lane);   // dO tile, swizzled (unpadded)
+  const size_t hslot = static_cast<size_t>(bh) * T + (hglobal ? 0 : i);
+  if (linear && wave == 0 && lane < D / 2) {
+    const __amdgpu_buffer_rsrc_t zrs = make_rsrc(zst + hslot * 2 * D, 2 * D * 4);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(zrs, (__attribute__((address_space(3))) void*)(zs),
+                                             16, 16 * lane, 0, 0, 0);
+  }
+  // O in 16 contiguous bytes per lane (row e / (D / 8), chunk e % (D / 8)),
+  // for dO . O by rows
+  constexpr int OC = kBlock * D / 8 / 256;
+  u32x4 oc[OC];
+#pragma unroll
+  for (int u = 0; u < OC; ++u) {
+    const int e = tid + 256 * u;
+    oc[u] = buf_ld16(ors, static_cast<uint32_t>((i * kBlock + e / (D / 8)) * D + 8 * (e % (D / 8))) * 2u, 0);
   }
   const uint32_t rowb = static_cast<uint32_t>(row) * D * 2;
-  // dO fragments (B operand of dY^T, k = o = 16 cc + 8 hl + s) and O at the
-  // same places of the wave's c half (for dO . O)
-  bf16x8 dof[NCC];
-#pragma unroll
-  for (int cc = 0; cc < NCC; ++cc) dof[cc] = as_bf16x8(buf_ld16(drs, rowb + (16 * cc + 8 * hl) * 2, 0));
-  u32x4 ov[NCC / 2];
-#pragma unroll
-  for (int cc = 0; cc < NCC / 2; ++cc)
-    ov[cc] = buf_ld16(ors, rowb + (16 * ((NCC / 2) * ch + cc) + 8 * hl) * 2, 0);
   // the row pieces of Y and Q that match the dY^T / dphi(q)^T accumulator
   // layout: lane (row, hl) needs columns 8 e4 + 4 hl .. + 3 of each 32-wide
   // tile.  Each lane loads 16 bytes, columns 16 p + 8 hl .. + 7, and the two
@@ -145,32 +144,44 @@ __global__ __launch_bounds__(256, 2) void bwd_prep_kernel(
       halves(yl[ct][p2], yv[ct][2 * p2], yv[ct][2 * p2 + 1]);
       halves(ql[ct][p2], qv[ct][2 * p2], qv[ct][2 * p2 + 1]);
     }
+  __builtin_amdgcn_s_waitcnt(0);   // this wave's copies of W^T, dO and Z have landed
+  __syncthreads();
 
-  // dY^T tiles for c in [D/2 ch, D/2 ch + D/2)
+  // dY^T tiles for c in [D/2 ch, D/2 ch + D/2): A = W^T rows, B = dO rows
+  // (k = o = 16 cc + 8 hl + s), both from LDS
   f32x16 dyt[NT];
   {
+    bf16x8 dof[NCC];
+#pragma unroll
+    for (int cc = 0; cc < NCC; ++cc) dof[cc] = as_bf16x8(ld16(dns + swz_off<D>(rloc, 16 * cc + 8 * hl)));
 #pragma unroll
     for (int ct = 0; ct < NT; ++ct) {
       dyt[ct] = f32x16{};
 #pragma unroll
-      for (int cc = 0; cc < NCC; ++cc) {
-        const int u = ct * NCC + cc;
-        const bf16x8 a = wa[u % WA];
-        if (u + WA < NT * NCC) wa[u % WA] = wld(u + WA);
-        dyt[ct] = mfma32(a, dof[cc], dyt[ct]);
-      }
+      for (int cc = 0; cc < NCC; ++cc)
+        dyt[ct] = mfma32(as_bf16x8(ld16(hs + swz_off<D>((D / 2) * ch + 32 * ct + n32, 16 * cc + 8 * hl))),
+                         dof[cc], dyt[ct]);
 #pragma unroll
       for (int e = 0; e < 16; ++e) dyt[ct][e] *= gate;   // dY of the ungated Y (gate 1: exact)
     }
   }
-  // partial row dots over this lane's c values
-  float p_oo = 0.f, p_yy = 0.f;
+  // dO . O by rows: each lane's chunks, summed over the D / 8 lanes of a row
 #pragma unroll
-  for (int cc = 0; cc < NCC / 2; ++cc)
+  for (int u = 0; u < OC; ++u) {
+    const int e = tid + 256 * u;
+    const int r = e / (D / 8), c8 = e % (D / 8);
+    const u32x4 dz4 = ld16(dns + swz_off<D>(r, 8 * c8));
+    float pr = 0.f;
 #pragma unroll
     for (int s2 = 0; s2 < 8; ++s2)
-      p_oo = __fmaf_rn(static_cast<float>(ch ? dof[NCC / 2 + cc][s2] : dof[cc][s2]),
-                       bf16_to_f32(u4_elem(ov[cc], s2)), p_oo);
+      pr = __fmaf_rn(bf16_to_f32(static_cast<uint16_t>(u4_elem(dz4, s2))),
+                     bf16_to_f32(static_cast<uint16_t>(u4_elem(oc[u], s2))), pr);
+#pragma unroll
+    for (int m = 1; m < D / 8; m <<= 1) pr += __shfl_xor(pr, m);
+    if (c8 == 0) red_oo[r] = pr;
+  }
+  // dY . Y partial row dots over this lane's c values
+  float p_yy = 0.f;
 #pragma unroll
   for (int ct = 0; ct < NT; ++ct)
 #pragma unroll
@@ -178,15 +189,16 @@ __global__ __launch_bounds__(256, 2) void bwd_prep_kernel(
 #pragma unroll
       for (int x = 0; x < 4; ++x)
         p_yy = __fmaf_rn(dyt[ct][4 * e4 + x], bf16_to_f32(u4_half(yv[ct][e4], x)), p_yy);
-  p_oo += __shfl_xor(p_oo, 32);
   p_yy += __shfl_xor(p_yy, 32);
-  if (hl == 0) {
-    red[ch][0][rloc] = p_oo;
-    red[ch][1][rloc] = p_yy;
+  if (hl == 0) red_yy[ch][rloc] = p_yy;
+  __syncthreads();   // W^T and the dO tile read by every wave
+  if (linear) {
+    const __amdgpu_buffer_rsrc_t hrs = make_rsrc(hst + hslot * D * D, D * D * 2);
+#pragma unroll
+    for (int r0 = 0; r0 < D; r0 += 64) copy_swz_buf<D, 4>(hrs, r0, hs + r0 * D, wave, lane);
   }
-  __syncthreads();
-  const float s_oo = red[0][0][rloc] + red[1][0][rloc];
-  const float s_yy = red[0][1][rloc] + red[1][1][rloc];
+  const float s_oo = red_oo[rloc];
+  const float s_yy = red_yy[0][rloc] + red_yy[1][rloc];
   const bool lin = valid && dn_r > 0.f;
   const float rden = lin ? 1.0f / dn_r : 0.f;
   const float dd_r = lin ? -s_yy * rden : 0.f;
@@ -207,7 +219,7 @@ __global__ __launch_bounds__(256, 2) void bwd_prep_kernel(
         st8(&dns[rloc * HP + c0], v);
       }
   }
-  __builtin_amdgcn_s_waitcnt(0);   // this wave's copies into hs / zs have landed
+  __builtin_amdgcn_s_waitcnt(0);   // this wave's copies of H^T have landed
   __syncthreads();
   {
     // the block's dN rows, 16 contiguous bytes per lane (whole rows per
