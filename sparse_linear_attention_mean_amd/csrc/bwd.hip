@@ -37,38 +37,33 @@ __global__ void w_transpose_kernel(const uint16_t* __restrict__ w, uint16_t* __r
 // bwd_prep: one workgroup (4 waves) per query block i.
 //   dY^T[c][r] = sum_o W[o][c] dO[r][o]             (wave: rows half qh, c half ch)
 //   D_r = dO_r . O_r - dY_r . Y_r,  dd_r = -(dY_r . Y_r) / den_r
-//   dN[r][c] = dY[r][c] / den_r     (bf16, also staged in LDS)
-//   dphi(q)^T[a][r] = sum_c H[a][c] dN[r][c] + dd_r Z[a]  (wave: rows half, a half)
-//   dq[r][a] = dphi(q)[r][a] phi'(q[r][a])           (initial value of dQ)
-// Rows r >= valid_len and rows with den = 0 get zero linear gradients.
-// Every global read of the first phase is issued up front, through buffer
-// resources that end at valid_len (no branches around the loads): W^T, the dO
-// tile and Z_i by asynchronous copies into LDS (whole rows per instruction),
-// O in 16 contiguous bytes per lane, the Y and Q pieces of each lane's rows
-// as 16-byte loads whose halves two lanes exchange.  Rows per lane would
-// cost one texture-address pass per row touched, which is what limited this
-// kernel.  H_i^T follows into the W^T buffer once the dY products are done.
+//   dN[r][c] = dY[r][c] / den_r     (bf16, staged in LDS and stored whole rows
+//                                    per instruction)
+// Rows r >= valid_len and rows with den = 0 get dN = 0 and dd = 0, so every
+// linear gradient built from them (dQ in bwd_q, dH / dZ in the state builder)
+// is zero.
+// Every global read is issued up front, through buffer resources that end at
+// valid_len (no branches around the loads): W^T and the dO tile by
+// asynchronous copies into LDS (whole rows per instruction), O in 16
+// contiguous bytes per lane, the Y pieces of each lane's rows as 16-byte
+// loads whose halves two lanes exchange.  Rows per lane would cost one
+// texture-address pass per row touched, which is what limited this kernel.
 // ---------------------------------------------------------------------------
 
 template <int D>
 __global__ __launch_bounds__(256, 2) void bwd_prep_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ o,
-    const uint16_t* __restrict__ dO, const uint16_t* __restrict__ wT,
-    const float* __restrict__ den, const uint16_t* __restrict__ y,
-    const uint16_t* __restrict__ hst, const float* __restrict__ zst, float* __restrict__ dsum,
-    float* __restrict__ ddel, uint16_t* __restrict__ dn, float* __restrict__ dq, int N, int L,
-    int T, bool linear, bool hglobal, float gate) {
+    const uint16_t* __restrict__ o, const uint16_t* __restrict__ dO,
+    const uint16_t* __restrict__ wT, const float* __restrict__ den,
+    const uint16_t* __restrict__ y, float* __restrict__ dsum, float* __restrict__ ddel,
+    uint16_t* __restrict__ dn, int N, int L, int T, bool linear, float gate) {
   constexpr int HP = D + 8;    // dN row pitch
   constexpr int NCC = D / 16;
   constexpr int NT = D / 64;   // 32-wide tiles per wave in each half
-  // W^T[c][o] (swizzled) for the dY products, then H^T[c][a] (swizzled)
-  __shared__ __attribute__((aligned(16))) uint16_t hs[D * D];
+  __shared__ __attribute__((aligned(16))) uint16_t hs[D * D];     // W^T[c][o], swizzled
   // the dO tile (swizzled, unpadded) for the dY products, then dN[r][c] (pitch HP)
   __shared__ __attribute__((aligned(16))) uint16_t dns[64 * HP];
-  __shared__ __attribute__((aligned(16))) float zs[2 * D];        // Z_i (two parts)
   __shared__ float red_oo[64];                                    // dO . O per row
   __shared__ float red_yy[2][64];                                 // dY . Y per c half and row
-  __shared__ float rowd[64];
 
   const uint32_t wg = xcd_remap(blockIdx.x, gridDim.x);
   const int i = wg % T;
@@ -85,26 +80,18 @@ __global__ __launch_bounds__(256, 2) void bwd_prep_kernel(
   // Every read goes through a buffer resource that ends at valid_len (rows
   // past it read as zero, no branches) and is issued before the first
   // product.  W^T (the A operand of dY^T, the same for every workgroup) and
-  // the dO tile arrive by asynchronous copies, whole rows per instruction,
-  // into the buffers that later hold H_i^T and dN; H_i^T is copied in once
-  // the dY products are done with W^T.
+  // the dO tile arrive by asynchronous copies, whole rows per instruction;
+  // the dO tile's buffer later holds dN.
   const uint32_t rbytes = static_cast<uint32_t>(L) * D * 2;
   const __amdgpu_buffer_rsrc_t drs = make_rsrc(dO + head, rbytes);
   const __amdgpu_buffer_rsrc_t ors = make_rsrc(o + head, rbytes);
   const __amdgpu_buffer_rsrc_t yrs = make_rsrc(y + head, rbytes);
-  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(q + head, rbytes);
   {
     const __amdgpu_buffer_rsrc_t wrs = make_rsrc(wT, D * D * 2);
 #pragma unroll
     for (int r0 = 0; r0 < D; r0 += 64) copy_swz_buf<D, 4>(wrs, r0, hs + r0 * D, wave, lane);
   }
   copy_swz_buf<D, 4>(drs, i * kBlock, dns, wave, lane);   // dO tile, swizzled (unpadded)
-  const size_t hslot = static_cast<size_t>(bh) * T + (hglobal ? 0 : i);
-  if (linear && wave == 0 && lane < D / 2) {
-    const __amdgpu_buffer_rsrc_t zrs = make_rsrc(zst + hslot * 2 * D, 2 * D * 4);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(zrs, (__attribute__((address_space(3))) void*)(zs),
-                                             16, 16 * lane, 0, 0, 0);
-  }
   // O in 16 contiguous bytes per lane (row e / (D / 8), chunk e % (D / 8)),
   // for dO . O by rows
   constexpr int OC = kBlock * D / 8 / 256;
@@ -115,36 +102,24 @@ __global__ __launch_bounds__(256, 2) void bwd_prep_kernel(
     oc[u] = buf_ld16(ors, static_cast<uint32_t>((i * kBlock + e / (D / 8)) * D + 8 * (e % (D / 8))) * 2u, 0);
   }
   const uint32_t rowb = static_cast<uint32_t>(row) * D * 2;
-  // the row pieces of Y and Q that match the dY^T / dphi(q)^T accumulator
-  // layout: lane (row, hl) needs columns 8 e4 + 4 hl .. + 3 of each 32-wide
-  // tile.  Each lane loads 16 bytes, columns 16 p + 8 hl .. + 7, and the two
-  // lanes of a row swap the halves the other one needs (lanes l and l + 32:
-  // v_permlane32_swap), so a row's 64 bytes of a tile take two loads.
-  u32x4 yl[NT][2], ql[NT][2];
+  // the row pieces of Y that match the dY^T accumulator layout: lane (row,
+  // hl) needs columns 8 e4 + 4 hl .. + 3 of each 32-wide tile.  Each lane
+  // loads 16 bytes, columns 16 p + 8 hl .. + 7, and the two lanes of a row
+  // swap the halves the other one needs (v_permlane32_swap), so a row's 64
+  // bytes of a tile take two loads.
+  u32x4 yl[NT][2];
 #pragma unroll
   for (int ct = 0; ct < NT; ++ct)
 #pragma unroll
-    for (int p2 = 0; p2 < 2; ++p2) {
-      const uint32_t c0 = (D / 2) * ch + 32 * ct + 16 * p2 + 8 * hl;
-      yl[ct][p2] = buf_ld16(yrs, rowb + c0 * 2, 0);
-      ql[ct][p2] = buf_ld16(qrs, rowb + c0 * 2, 0);
-    }
-  auto halves = [&](const u32x4& x, u32x2& even, u32x2& odd) __attribute__((always_inline)) {
-    const auto s0 = __builtin_amdgcn_permlane32_swap(x[0], x[2], false, false);
-    const auto s1 = __builtin_amdgcn_permlane32_swap(x[1], x[3], false, false);
-    even = u32x2{s0[0], s1[0]};   // e4 = 2 p: columns 16 p + 4 hl .. + 3
-    odd = u32x2{s0[1], s1[1]};    // e4 = 2 p + 1: columns 16 p + 8 + 4 hl .. + 3
-  };
+    for (int p2 = 0; p2 < 2; ++p2)
+      yl[ct][p2] = buf_ld16(yrs, rowb + ((D / 2) * ch + 32 * ct + 16 * p2 + 8 * hl) * 2, 0);
   const float dn_r = (linear && valid) ? den[bh * N + row] : 0.f;
-  u32x2 yv[NT][4], qv[NT][4];
+  u32x2 yv[NT][4];
 #pragma unroll
   for (int ct = 0; ct < NT; ++ct)
 #pragma unroll
-    for (int p2 = 0; p2 < 2; ++p2) {
-      halves(yl[ct][p2], yv[ct][2 * p2], yv[ct][2 * p2 + 1]);
-      halves(ql[ct][p2], qv[ct][2 * p2], qv[ct][2 * p2 + 1]);
-    }
-  __builtin_amdgcn_s_waitcnt(0);   // this wave's copies of W^T, dO and Z have landed
+    for (int p2 = 0; p2 < 2; ++p2) row_halves(yl[ct][p2], yv[ct][2 * p2], yv[ct][2 * p2 + 1]);
+  __builtin_amdgcn_s_waitcnt(0);   // this wave's copies of W^T and dO have landed
   __syncthreads();
 
   // dY^T tiles for c in [D/2 ch, D/2 ch + D/2): A = W^T rows, B = dO rows
@@ -191,12 +166,7 @@ __global__ __launch_bounds__(256, 2) void bwd_prep_kernel(
         p_yy = __fmaf_rn(dyt[ct][4 * e4 + x], bf16_to_f32(u4_half(yv[ct][e4], x)), p_yy);
   p_yy += __shfl_xor(p_yy, 32);
   if (hl == 0) red_yy[ch][rloc] = p_yy;
-  __syncthreads();   // W^T and the dO tile read by every wave
-  if (linear) {
-    const __amdgpu_buffer_rsrc_t hrs = make_rsrc(hst + hslot * D * D, D * D * 2);
-#pragma unroll
-    for (int r0 = 0; r0 < D; r0 += 64) copy_swz_buf<D, 4>(hrs, r0, hs + r0 * D, wave, lane);
-  }
+  __syncthreads();   // the dO tile read by every wave
   const float s_oo = red_oo[rloc];
   const float s_yy = red_yy[0][rloc] + red_yy[1][rloc];
   const bool lin = valid && dn_r > 0.f;
@@ -205,7 +175,6 @@ __global__ __launch_bounds__(256, 2) void bwd_prep_kernel(
   if (ch == 0 && hl == 0) {
     dsum[bh * N + row] = valid ? s_oo - s_yy : 0.f;
     ddel[bh * N + row] = dd_r;
-    rowd[rloc] = dd_r;
   }
   // dN = dY / den (bf16) into LDS, then to global memory from there
   {
@@ -219,7 +188,6 @@ __global__ __launch_bounds__(256, 2) void bwd_prep_kernel(
         st8(&dns[rloc * HP + c0], v);
       }
   }
-  __builtin_amdgcn_s_waitcnt(0);   // this wave's copies of H^T have landed
   __syncthreads();
   {
     // the block's dN rows, 16 contiguous bytes per lane (whole rows per
@@ -232,47 +200,23 @@ __global__ __launch_bounds__(256, 2) void bwd_prep_kernel(
       st16(dblk + static_cast<size_t>(r) * D + 8 * c8, ld16(&dns[r * HP + 8 * c8]));
     }
   }
-  // dphi(q)^T[a][r]: wave covers rows half qh and a in [D/2 ch, D/2 ch + D/2)
-  float* dqrow = dq + head + static_cast<size_t>(row) * D;
-  const float ddv = rowd[rloc];
-#pragma unroll
-  for (int at = 0; at < NT; ++at) {
-    const int abase = (D / 2) * ch + 32 * at;
-    f32x16 acc = {};
-    if (linear) {
-#pragma unroll
-      for (int cc = 0; cc < NCC; ++cc) {
-        const bf16x8 a = swz_op32_tr<D>(hs, 16 * cc, abase, lane);
-        const bf16x8 b = as_bf16x8(ld16(&dns[rloc * HP + 16 * cc + 8 * hl]));
-        acc = mfma32(a, b, acc);
-      }
-    }
-    // lane holds dphi^T[a = abase + 8 (e/4) + 4 hl + e%4][row]
-#pragma unroll
-    for (int e4 = 0; e4 < 4; ++e4) {
-      const int a0 = abase + 8 * e4 + 4 * hl;
-      float r[4];
-#pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        const float qa = bf16_to_f32(u4_half(qv[at][e4], x));
-        const float z = lin ? zs[a0 + x] + zs[D + a0 + x] : 0.f;
-        const float g = acc[4 * e4 + x] + ddv * z;
-        r[x] = lin ? g * phi_prime(qa) : 0.f;
-      }
-      *reinterpret_cast<float4*>(dqrow + a0) = make_float4(r[0], r[1], r[2], r[3]);
-    }
-  }
 }
 
 // ---------------------------------------------------------------------------
-// bwd_q: one workgroup per query block i; sparse part of dQ over the critical
-// key blocks, added to the linear part already in dq.
+// bwd_q: one workgroup per query block i; dQ = the sparse part over the
+// critical key blocks plus the linear part:
 //   S^T = K Q^T, P^T = exp2(S^T scale log2e - lse log2e), dP^T = V dO^T,
-//   dS^T = P^T (dP^T - D), dQ += scale dS K
+//   dS^T = P^T (dP^T - D), dQ_s = scale dS K
+//   dphi(q)^T[a][r] = sum_c H_i[a][c] dN[r][c] + dd_r Z_i[a],
+//   dQ_l[r][a] = dphi(q)[r][a] phi'(q[r][a])
 // Waves (kh, qh) as in the forward; dS^T's result tile is the A operand of
 // dS K directly (k index permuted) and K_j is read a second time from the
 // same LDS tile with transpose reads.  K_j and V_j are double-buffered with
-// the next block's loads in flight during the current block's MFMAs.
+// the next block's loads in flight during the current block's MFMAs.  H_i^T
+// and Z_i are copied into the buffers the last key block leaves free; the
+// linear part is computed in the layout of the query rows (lane = row, so
+// phi'(q) comes from the Q fragments already in registers) and transposed
+// through LDS onto the sparse part.
 // ---------------------------------------------------------------------------
 template <int D>
 struct BqCfg {
@@ -286,6 +230,8 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dO,
     const float* __restrict__ lse, const float* __restrict__ dsum,
     const int32_t* __restrict__ lut, const int32_t* __restrict__ lut_cnt,
+    const uint16_t* __restrict__ dn, const float* __restrict__ ddel,
+    const uint16_t* __restrict__ hst, const float* __restrict__ zst, bool linear, bool hglobal,
     float* __restrict__ dq, int N, int L, int T, float scale) {
   using C = BqCfg<D>;
   // separate arrays, named statically by every access: the compiler can tell
@@ -294,6 +240,7 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t kb1[C::kTile];
   __shared__ __attribute__((aligned(16))) uint16_t vb0[C::kTile];
   __shared__ __attribute__((aligned(16))) uint16_t vb1[C::kTile];
+  __shared__ __attribute__((aligned(16))) float zq[2 * D];   // Z_i (two parts)
 
   const uint32_t wg = xcd_remap(blockIdx.x, gridDim.x);
   const int i = wg % T;
@@ -342,16 +289,19 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(
     copy_swz_buf<D, 4>(krs, jb * kBlock, kd, wave, lane);
     copy_swz_buf<D, 4>(vrs, jb * kBlock, vd, wave, lane);
   };
-  // This block's dQ rows (the linear part written by the preparation kernel,
-  // fp32 64 x D) are copied into the buffers the last key block leaves free:
-  // rows 0..31 into its K buffer, rows 32..63 into its V buffer.
-  auto copy_dq = [&](float* r0, float* r1) __attribute__((always_inline)) {
-    const float* src = dq + head + static_cast<size_t>(i) * kBlock * D;
-    constexpr int kCopies = 32 * D / 4 / 64;   // 16-byte chunks / 64 per copy, per half
-#pragma unroll
-    for (int it = wave; it < kCopies; it += 4) {
-      gl_to_lds16(src + 4 * (it * 64 + lane), r0 + it * 256);
-      gl_to_lds16(src + 32 * D + 4 * (it * 64 + lane), r1 + it * 256);
+  // H_i^T (bf16 D x D, swizzled 64-row tiles) and Z_i for the linear part go
+  // into the buffers the last key block leaves free: rows 0..63 of H_i^T into
+  // its K buffer, rows 64..127 (D = 128) into its V buffer.
+  const size_t hslot = static_cast<size_t>(bh) * T + (hglobal ? 0 : i);
+  auto copy_h = [&](uint16_t* h0, uint16_t* h1) __attribute__((always_inline)) {
+    if (!linear) return;
+    const __amdgpu_buffer_rsrc_t hrs = make_rsrc(hst + hslot * D * D, D * D * 2);
+    copy_swz_buf<D, 4>(hrs, 0, h0, wave, lane);
+    if constexpr (D > 64) copy_swz_buf<D, 4>(hrs, 64, h1, wave, lane);
+    if (wave == 0 && lane < D / 2) {
+      const __amdgpu_buffer_rsrc_t zrs = make_rsrc(zst + hslot * 2 * D, 2 * D * 4);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(zrs, (__attribute__((address_space(3))) void*)(zq),
+                                               16, 16 * lane, 0, 0, 0);
     }
   };
 
@@ -372,7 +322,7 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(
                      lds_tr4(reinterpret_cast<const uint16_t*>(p + (boff ^ (16u * D + 16u)))));
   };
   // one key block from (kt, vt); the next one is copied into (kn, vn), or
-  // this block's dQ rows after the last one
+  // H_i^T and Z_i after the last one
   auto step = [&](int n, const uint16_t* kt, const uint16_t* vt, uint16_t* kn, uint16_t* vn,
                   bool masked) __attribute__((always_inline)) {
     if (((n + 1) & 63) == 0 && n + 1 < cnt) {
@@ -382,7 +332,7 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(
     if (n + 1 < cnt)
       copy_kv(n + 1, kn, vn);
     else
-      copy_dq(reinterpret_cast<float*>(kn), reinterpret_cast<float*>(vn));
+      copy_h(kn, vn);
     // the offsets pass through an empty asm each step, so the per-read XORs
     // are formed next to their reads instead of occupying registers
     uint32_t rb = rowb0, tb = trb0;
@@ -424,7 +374,9 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(
   };
 
   if (cnt == 0) {
-    copy_dq(reinterpret_cast<float*>(kb0), reinterpret_cast<float*>(vb0));
+    copy_h(kb0, vb0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
   } else {
     copy_kv(0, kb0, vb0);
     __builtin_amdgcn_s_waitcnt(0);
@@ -437,14 +389,26 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(
   // merge the key halves: wave (kh, qh) finishes the tiles at = NH kh .. NH kh + NH - 1
   // and hands the others to its partner (other kh); then add the linear part.
   // The last block's buffers hold the exchange (waves 0, 1 in its K buffer,
-  // 2, 3 in its V buffer), the other ones the dQ rows.
+  // 2, 3 in its V buffer), the other ones H_i^T, then the linear part.
   constexpr int NH = C::NAT / 2;
   const bool odd = cnt & 1;   // the last block (cnt - 1) was read from kb0 / vb0
-                              // (cnt = 0: the dQ rows are in kb0 / vb0 as well)
+                              // (cnt = 0: H_i^T is in kb0 / vb0 as well)
   float* exq = reinterpret_cast<float*>(qh ? (odd ? vb0 : vb1) : (odd ? kb0 : kb1));
-  const float* dqs = reinterpret_cast<const float*>(qh ? (odd ? vb1 : vb0) : (odd ? kb1 : kb0));
+  const uint16_t* ht0 = odd ? kb1 : kb0;   // H_i^T rows 0..63
+  const uint16_t* ht1 = odd ? vb1 : vb0;   // H_i^T rows 64..127
+  float* lq = reinterpret_cast<float*>(qh ? (odd ? vb1 : vb0) : (odd ? kb1 : kb0));
   float* exo = exq + kh * NH * 16 * 64;
   const float* exp_ = exq + (kh ^ 1) * NH * 16 * 64;
+  // the linear part's operands: this lane's dN row (B operand, k = c) and dd
+  bf16x8 dnf[C::NCC];
+  float ddr = 0.f;
+  if (linear) {
+    const uint16_t* dr = dn + head + static_cast<size_t>(row) * D + 8 * hl;
+#pragma unroll
+    for (int cc = 0; cc < C::NCC; ++cc)
+      dnf[cc] = valid ? as_bf16x8(ld16(dr + 16 * cc)) : as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+    ddr = valid ? ddel[bh * N + row] : 0.f;
+  }
   __syncthreads();
   f32x16 fin[NH];
   if (kh == 0) {
@@ -462,8 +426,55 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(
       for (int e = 0; e < 16; ++e) exo[(x * 16 + e) * 64 + lane] = acc[x][e];
     }
   }
-  __builtin_amdgcn_s_waitcnt(0);   // this wave's dQ copies have landed
-  __syncthreads();
+  // linear part of this wave's tiles, transposed: lane = row 32 qh + n32,
+  // element e = column a = 32 (NH kh + x) + 8 (e/4) + 4 hl + e%4
+  f32x16 lin[NH];
+  if (linear) {
+#pragma unroll
+    for (int x = 0; x < NH; ++x) {
+      const int at = NH * kh + x;
+      lin[x] = f32x16{};
+#pragma unroll
+      for (int cc = 0; cc < C::NCC; ++cc) {
+        const uint16_t* ht = 16 * cc < 64 ? ht0 : ht1;
+        lin[x] = mfma32(swz_op32_tr<D>(ht, (16 * cc) % 64, 32 * at, lane), dnf[cc], lin[x]);
+      }
+#pragma unroll
+      for (int p2 = 0; p2 < 2; ++p2) {
+        // phi'(q) for columns 32 at + 16 p2 + 8 (e4 % 2) + 4 hl .. + 3 (e4 = 2 p2, 2 p2 + 1)
+        u32x2 qe, qo;
+        row_halves(__builtin_bit_cast(u32x4, qf[2 * at + p2]), qe, qo);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int e4 = 2 * p2 + h;
+          const int a0 = 32 * at + 8 * e4 + 4 * hl;
+#pragma unroll
+          for (int x4 = 0; x4 < 4; ++x4) {
+            const float z = zq[a0 + x4] + zq[D + a0 + x4];
+            const float g = lin[x][4 * e4 + x4] + ddr * z;
+            lin[x][4 * e4 + x4] = g * phi_prime(bf16_to_f32(u4_half(h ? qo : qe, x4)));
+          }
+        }
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();   // the exchange is visible, every wave is done with H_i^T
+  // The linear part goes to rows of fp32 in the freed H_i^T buffer of this
+  // query half (row r at lq + r D, columns XOR-swizzled by row in 16-byte
+  // steps so that the 32 rows of a store fall on different banks); each wave
+  // reads back only what it wrote, so no barrier is needed before the reads.
+  auto lq_at = [&](int r, int a) { return r * D + (a ^ ((r & (D / 4 - 1)) << 2)); };
+  if (linear) {
+#pragma unroll
+    for (int x = 0; x < NH; ++x)
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const int a0 = 32 * (NH * kh + x) + 8 * e4 + 4 * hl;
+        *reinterpret_cast<f32x4*>(lq + lq_at(n32, a0)) =
+            f32x4{lin[x][4 * e4], lin[x][4 * e4 + 1], lin[x][4 * e4 + 2], lin[x][4 * e4 + 3]};
+      }
+  }
   // lane holds dQ[q = 32 qh + 8 (e/4) + 4 hl + e%4][a = 32 at + n32]
 #pragma unroll
   for (int x = 0; x < NH; ++x)
@@ -472,8 +483,9 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(
       const int qlh = 8 * (e / 4) + 4 * hl + (e % 4);   // row within the half
       const int a = 32 * (NH * kh + x) + n32;
       const float sparse = scale * (fin[x][e] + exp_[(x * 16 + e) * 64 + lane]);
+      const float lpart = linear ? lq[lq_at(qlh, a)] : 0.f;
       const int qr = i * kBlock + 32 * qh + qlh;
-      dq[head + static_cast<size_t>(qr) * D + a] = qr < L ? dqs[qlh * D + a] + sparse : 0.f;
+      dq[head + static_cast<size_t>(qr) * D + a] = qr < L ? lpart + sparse : 0.f;
     }
 }
 
@@ -920,30 +932,31 @@ hipError_t launch_w_transpose(const Dims& d, const uint16_t* w, uint16_t* wT, hi
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_prep(const Dims& d, const uint16_t* q, const uint16_t* o,
-                           const uint16_t* dO, const uint16_t* wT, const float* den,
-                           const uint16_t* y, const uint16_t* hst, const float* zst, bool linear,
-                           float* dsum, float* ddel, uint16_t* dn, float* dq, hipStream_t s) {
+hipError_t launch_bwd_prep(const Dims& d, const uint16_t* o, const uint16_t* dO,
+                           const uint16_t* wT, const float* den, const uint16_t* y, bool linear,
+                           float* dsum, float* ddel, uint16_t* dn, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(d.BH() * d.T));
   if (d.D == 128)
-    hipLaunchKernelGGL(bwd_prep_kernel<128>, grid, dim3(256), 0, s, q, o, dO, wT, den, y, hst, zst,
-                       dsum, ddel, dn, dq, d.N, d.L, d.T, linear, d.global, d.gate);
+    hipLaunchKernelGGL(bwd_prep_kernel<128>, grid, dim3(256), 0, s, o, dO, wT, den, y, dsum, ddel,
+                       dn, d.N, d.L, d.T, linear, d.gate);
   else
-    hipLaunchKernelGGL(bwd_prep_kernel<64>, grid, dim3(256), 0, s, q, o, dO, wT, den, y, hst, zst,
-                       dsum, ddel, dn, dq, d.N, d.L, d.T, linear, d.global, d.gate);
+    hipLaunchKernelGGL(bwd_prep_kernel<64>, grid, dim3(256), 0, s, o, dO, wT, den, y, dsum, ddel,
+                       dn, d.N, d.L, d.T, linear, d.gate);
   return hipGetLastError();
 }
 
 hipError_t launch_bwd_q(const Dims& d, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                         const uint16_t* dO, const float* lse, const float* dsum,
-                        const int32_t* lut, const int32_t* lut_cnt, float* dq, hipStream_t s) {
+                        const int32_t* lut, const int32_t* lut_cnt, const uint16_t* dn,
+                        const float* ddel, const uint16_t* hst, const float* zst, bool linear,
+                        float* dq, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(d.BH() * d.T));
   if (d.D == 128)
     hipLaunchKernelGGL(bwd_q_kernel<128>, grid, dim3(256), 0, s, q, k, v, dO, lse, dsum, lut,
-                       lut_cnt, dq, d.N, d.L, d.T, d.scale);
+                       lut_cnt, dn, ddel, hst, zst, linear, d.global, dq, d.N, d.L, d.T, d.scale);
   else
     hipLaunchKernelGGL(bwd_q_kernel<64>, grid, dim3(256), 0, s, q, k, v, dO, lse, dsum, lut,
-                       lut_cnt, dq, d.N, d.L, d.T, d.scale);
+                       lut_cnt, dn, ddel, hst, zst, linear, d.global, dq, d.N, d.L, d.T, d.scale);
   return hipGetLastError();
 }
 

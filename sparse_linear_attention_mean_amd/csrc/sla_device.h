@@ -101,6 +101,17 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const u32x2& lo, const u32x2& hi) {
   return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
 }
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+// A lane pair (l, l + 32) holding 8 consecutive bf16 of one row each, columns
+// c0 + 8 hl .. + 7 (hl = l / 32), is turned into the two 4-column pieces the
+// 32x32 MFMA result layout gives lane (row, hl) for that row: even = columns
+// c0 + 4 hl .. + 3, odd = columns c0 + 8 + 4 hl .. + 3 (v_permlane32_swap
+// exchanges the halves the other lane needs).
+__device__ __forceinline__ void row_halves(const u32x4& x, u32x2& even, u32x2& odd) {
+  const auto s0 = __builtin_amdgcn_permlane32_swap(x[0], x[2], false, false);
+  const auto s1 = __builtin_amdgcn_permlane32_swap(x[1], x[3], false, false);
+  even = u32x2{s0[0], s1[0]};
+  odd = u32x2{s0[1], s1[1]};
+}
 __device__ __forceinline__ u32x2 ld8(const void* p) { return *reinterpret_cast<const u32x2*>(p); }
 __device__ __forceinline__ void st16(void* p, const u32x4& v) { *reinterpret_cast<u32x4*>(p) = v; }
 __device__ __forceinline__ void st8(void* p, const u32x2& v) { *reinterpret_cast<u32x2*>(p) = v; }

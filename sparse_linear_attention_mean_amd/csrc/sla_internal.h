@@ -92,13 +92,14 @@ hipError_t launch_attn_fwd(const Dims& d, const uint16_t* q, const uint16_t* k,
 
 // backward
 hipError_t launch_w_transpose(const Dims& d, const uint16_t* w, uint16_t* wT, hipStream_t s);
-hipError_t launch_bwd_prep(const Dims& d, const uint16_t* q, const uint16_t* o,
-                           const uint16_t* dO, const uint16_t* wT, const float* den,
-                           const uint16_t* y, const uint16_t* hst, const float* zst, bool linear,
-                           float* dsum, float* ddel, uint16_t* dn, float* dq, hipStream_t s);
+hipError_t launch_bwd_prep(const Dims& d, const uint16_t* o, const uint16_t* dO,
+                           const uint16_t* wT, const float* den, const uint16_t* y, bool linear,
+                           float* dsum, float* ddel, uint16_t* dn, hipStream_t s);
 hipError_t launch_bwd_q(const Dims& d, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                         const uint16_t* dO, const float* lse, const float* dsum,
-                        const int32_t* lut, const int32_t* lut_cnt, float* dq, hipStream_t s);
+                        const int32_t* lut, const int32_t* lut_cnt, const uint16_t* dn,
+                        const float* ddel, const uint16_t* hst, const float* zst, bool linear,
+                        float* dq, hipStream_t s);
 hipError_t launch_bwd_kv(const Dims& d, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                          const uint16_t* dO, const float* lse, const float* dsum,
                          const int32_t* col, const int32_t* col_cnt, const uint16_t* dh,
