@@ -34,150 +34,152 @@ __global__ void w_transpose_kernel(const uint16_t* __restrict__ w, uint16_t* __r
 }
 
 // ---------------------------------------------------------------------------
-// bwd_prep: one workgroup (4 waves) per query block i.
+// bwd_prep: one workgroup (4 waves) per run of consecutive query blocks
+// (blocks b0 .. b1 - 1 of the flattened (batch x head, block) order; there are
+// `parts` runs of nearly equal length).  Per query block i:
 //   dY^T[c][r] = sum_o W[o][c] dO[r][o]             (wave: rows half qh, c half ch)
 //   D_r = dO_r . O_r - dY_r . Y_r,  dd_r = -(dY_r . Y_r) / den_r
 //   dN[r][c] = dY[r][c] / den_r     (bf16, staged in LDS and stored whole rows
 //                                    per instruction)
-// Rows r >= valid_len and rows with den = 0 get dN = 0 and dd = 0, so every
-// linear gradient built from them (dQ in bwd_q, dH / dZ in the state builder)
-// is zero.
-// Every global read is issued up front, through buffer resources that end at
-// valid_len (no branches around the loads): W^T and the dO tile by
-// asynchronous copies into LDS (whole rows per instruction), O in 16
-// contiguous bytes per lane, the Y pieces of each lane's rows as 16-byte
-// loads whose halves two lanes exchange.  Rows per lane would cost one
-// texture-address pass per row touched, which is what limited this kernel.
+//   dW^T partial += Y_i^T dO_i     (one 32 x 32 tile set per wave, fp32)
+// and at the end the run's dW^T partial is written for the fixed-order
+// reduction.  Rows r >= valid_len and rows with den = 0 get dN = 0 and
+// dd = 0, so every linear gradient built from them (dQ in bwd_q, dH / dZ in
+// the state builder) is zero; padded rows read as zero and add nothing to dW.
+// W^T is copied into LDS once per workgroup; per block the dO and Y tiles
+// arrive by asynchronous copies (whole rows per instruction, through buffer
+// resources that end at valid_len) and O in 16 contiguous bytes per lane.
+// Both products of a block read their operands from these tiles: the dY^T
+// product takes the dO rows, the dW product takes Y^T and dO^T by transpose
+// reads.  (Rows loaded one per lane had made the texture-address unit the
+// limit: one address pass per row touched.)
 // ---------------------------------------------------------------------------
-
 template <int D>
 __global__ __launch_bounds__(256, 2) void bwd_prep_kernel(
     const uint16_t* __restrict__ o, const uint16_t* __restrict__ dO,
     const uint16_t* __restrict__ wT, const float* __restrict__ den,
     const uint16_t* __restrict__ y, float* __restrict__ dsum, float* __restrict__ ddel,
-    uint16_t* __restrict__ dn, int N, int L, int T, bool linear, float gate) {
+    uint16_t* __restrict__ dn, float* __restrict__ dwp, long long nblocks, int parts, int N,
+    int L, int T, bool linear, float gate) {
   constexpr int HP = D + 8;    // dN row pitch
   constexpr int NCC = D / 16;
   constexpr int NT = D / 64;   // 32-wide tiles per wave in each half
+  constexpr int TPW = (D / 32) * (D / 32) / 4;   // dW^T tiles per wave
+  constexpr int OC = kBlock * D / 8 / 256;       // 16-byte O pieces per thread
   __shared__ __attribute__((aligned(16))) uint16_t hs[D * D];     // W^T[c][o], swizzled
-  // the dO tile (swizzled, unpadded) for the dY products, then dN[r][c] (pitch HP)
+  // the dO tile (swizzled, unpadded) for the products, then dN[r][c] (pitch HP)
   __shared__ __attribute__((aligned(16))) uint16_t dns[64 * HP];
+  __shared__ __attribute__((aligned(16))) uint16_t ys[64 * D];    // Y tile, swizzled
   __shared__ float red_oo[64];                                    // dO . O per row
   __shared__ float red_yy[2][64];                                 // dY . Y per c half and row
 
-  const uint32_t wg = xcd_remap(blockIdx.x, gridDim.x);
-  const int i = wg % T;
-  const long long bh = wg / T;
+  const int w = static_cast<int>(xcd_remap(blockIdx.x, gridDim.x));
+  const long long b0 = nblocks * w / parts, b1 = nblocks * (w + 1) / parts;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n32 = lane & 31, hl = lane >> 5;
   const int qh = wave & 1, ch = wave >> 1;
-  const size_t head = static_cast<size_t>(bh) * N * D;
   const int rloc = 32 * qh + n32;
-  const int row = i * kBlock + rloc;   // < N always; rows >= valid_len are read, never used
-  const bool valid = row < L;
-
-  // Every read goes through a buffer resource that ends at valid_len (rows
-  // past it read as zero, no branches) and is issued before the first
-  // product.  W^T (the A operand of dY^T, the same for every workgroup) and
-  // the dO tile arrive by asynchronous copies, whole rows per instruction;
-  // the dO tile's buffer later holds dN.
   const uint32_t rbytes = static_cast<uint32_t>(L) * D * 2;
-  const __amdgpu_buffer_rsrc_t drs = make_rsrc(dO + head, rbytes);
-  const __amdgpu_buffer_rsrc_t ors = make_rsrc(o + head, rbytes);
-  const __amdgpu_buffer_rsrc_t yrs = make_rsrc(y + head, rbytes);
   {
     const __amdgpu_buffer_rsrc_t wrs = make_rsrc(wT, D * D * 2);
 #pragma unroll
     for (int r0 = 0; r0 < D; r0 += 64) copy_swz_buf<D, 4>(wrs, r0, hs + r0 * D, wave, lane);
   }
-  copy_swz_buf<D, 4>(drs, i * kBlock, dns, wave, lane);   // dO tile, swizzled (unpadded)
-  // O in 16 contiguous bytes per lane (row e / (D / 8), chunk e % (D / 8)),
-  // for dO . O by rows
-  constexpr int OC = kBlock * D / 8 / 256;
-  u32x4 oc[OC];
+  f32x16 dwa[TPW];
 #pragma unroll
-  for (int u = 0; u < OC; ++u) {
-    const int e = tid + 256 * u;
-    oc[u] = buf_ld16(ors, static_cast<uint32_t>((i * kBlock + e / (D / 8)) * D + 8 * (e % (D / 8))) * 2u, 0);
-  }
-  const uint32_t rowb = static_cast<uint32_t>(row) * D * 2;
-  // the row pieces of Y that match the dY^T accumulator layout: lane (row,
-  // hl) needs columns 8 e4 + 4 hl .. + 3 of each 32-wide tile.  Each lane
-  // loads 16 bytes, columns 16 p + 8 hl .. + 7, and the two lanes of a row
-  // swap the halves the other one needs (v_permlane32_swap), so a row's 64
-  // bytes of a tile take two loads.
-  u32x4 yl[NT][2];
-#pragma unroll
-  for (int ct = 0; ct < NT; ++ct)
-#pragma unroll
-    for (int p2 = 0; p2 < 2; ++p2)
-      yl[ct][p2] = buf_ld16(yrs, rowb + ((D / 2) * ch + 32 * ct + 16 * p2 + 8 * hl) * 2, 0);
-  const float dn_r = (linear && valid) ? den[bh * N + row] : 0.f;
-  u32x2 yv[NT][4];
-#pragma unroll
-  for (int ct = 0; ct < NT; ++ct)
-#pragma unroll
-    for (int p2 = 0; p2 < 2; ++p2) row_halves(yl[ct][p2], yv[ct][2 * p2], yv[ct][2 * p2 + 1]);
-  __builtin_amdgcn_s_waitcnt(0);   // this wave's copies of W^T and dO have landed
-  __syncthreads();
+  for (int x = 0; x < TPW; ++x) dwa[x] = f32x16{};
 
-  // dY^T tiles for c in [D/2 ch, D/2 ch + D/2): A = W^T rows, B = dO rows
-  // (k = o = 16 cc + 8 hl + s), both from LDS
-  f32x16 dyt[NT];
-  {
-    bf16x8 dof[NCC];
+  for (long long b = b0; b < b1; ++b) {
+    const int i = static_cast<int>(b % T);
+    const long long bh = b / T;
+    const size_t head = static_cast<size_t>(bh) * N * D;
+    const int row = i * kBlock + rloc;   // < N always; rows >= valid_len read as zero
+    const bool valid = row < L;
+    const __amdgpu_buffer_rsrc_t drs = make_rsrc(dO + head, rbytes);
+    const __amdgpu_buffer_rsrc_t ors = make_rsrc(o + head, rbytes);
+    const __amdgpu_buffer_rsrc_t yrs = make_rsrc(y + head, rbytes);
+    copy_swz_buf<D, 4>(drs, i * kBlock, dns, wave, lane);   // dO tile, swizzled (unpadded)
+    copy_swz_buf<D, 4>(yrs, i * kBlock, ys, wave, lane);    // Y tile, swizzled
+    // O in 16 contiguous bytes per lane (row e / (D / 8), chunk e % (D / 8)),
+    // for dO . O by rows
+    u32x4 oc[OC];
 #pragma unroll
-    for (int cc = 0; cc < NCC; ++cc) dof[cc] = as_bf16x8(ld16(dns + swz_off<D>(rloc, 16 * cc + 8 * hl)));
-#pragma unroll
-    for (int ct = 0; ct < NT; ++ct) {
-      dyt[ct] = f32x16{};
-#pragma unroll
-      for (int cc = 0; cc < NCC; ++cc)
-        dyt[ct] = mfma32(as_bf16x8(ld16(hs + swz_off<D>((D / 2) * ch + 32 * ct + n32, 16 * cc + 8 * hl))),
-                         dof[cc], dyt[ct]);
-#pragma unroll
-      for (int e = 0; e < 16; ++e) dyt[ct][e] *= gate;   // dY of the ungated Y (gate 1: exact)
+    for (int u = 0; u < OC; ++u) {
+      const int e = tid + 256 * u;
+      oc[u] = buf_ld16(ors, static_cast<uint32_t>((i * kBlock + e / (D / 8)) * D + 8 * (e % (D / 8))) * 2u, 0);
     }
-  }
-  // dO . O by rows: each lane's chunks, summed over the D / 8 lanes of a row
+    const float dn_r = (linear && valid) ? den[bh * N + row] : 0.f;
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's copies have landed
+    __syncthreads();
+
+    // dY^T tiles for c in [D/2 ch, D/2 ch + D/2): A = W^T rows, B = dO rows
+    // (k = o = 16 cc + 8 hl + s), both from LDS
+    f32x16 dyt[NT];
+    {
+      bf16x8 dof[NCC];
 #pragma unroll
-  for (int u = 0; u < OC; ++u) {
-    const int e = tid + 256 * u;
-    const int r = e / (D / 8), c8 = e % (D / 8);
-    const u32x4 dz4 = ld16(dns + swz_off<D>(r, 8 * c8));
-    float pr = 0.f;
+      for (int cc = 0; cc < NCC; ++cc) dof[cc] = as_bf16x8(ld16(dns + swz_off<D>(rloc, 16 * cc + 8 * hl)));
 #pragma unroll
-    for (int s2 = 0; s2 < 8; ++s2)
-      pr = __fmaf_rn(bf16_to_f32(static_cast<uint16_t>(u4_elem(dz4, s2))),
-                     bf16_to_f32(static_cast<uint16_t>(u4_elem(oc[u], s2))), pr);
+      for (int ct = 0; ct < NT; ++ct) {
+        dyt[ct] = f32x16{};
 #pragma unroll
-    for (int m = 1; m < D / 8; m <<= 1) pr += __shfl_xor(pr, m);
-    if (c8 == 0) red_oo[r] = pr;
-  }
-  // dY . Y partial row dots over this lane's c values
-  float p_yy = 0.f;
+        for (int cc = 0; cc < NCC; ++cc)
+          dyt[ct] = mfma32(as_bf16x8(ld16(hs + swz_off<D>((D / 2) * ch + 32 * ct + n32, 16 * cc + 8 * hl))),
+                           dof[cc], dyt[ct]);
 #pragma unroll
-  for (int ct = 0; ct < NT; ++ct)
+        for (int e = 0; e < 16; ++e) dyt[ct][e] *= gate;   // dY of the ungated Y (gate 1: exact)
+      }
+    }
+    // dW^T[c][o] += sum_r Y[r][c] dO[r][o]: A = Y^T, B = dO^T, both by transpose reads (k = r)
 #pragma unroll
-    for (int e4 = 0; e4 < 4; ++e4)
+    for (int x = 0; x < TPW; ++x) {
+      const int tt = wave * TPW + x;
+      const int ct = tt / (D / 32), ot = tt % (D / 32);
 #pragma unroll
-      for (int x = 0; x < 4; ++x)
-        p_yy = __fmaf_rn(dyt[ct][4 * e4 + x], bf16_to_f32(u4_half(yv[ct][e4], x)), p_yy);
-  p_yy += __shfl_xor(p_yy, 32);
-  if (hl == 0) red_yy[ch][rloc] = p_yy;
-  __syncthreads();   // the dO tile read by every wave
-  const float s_oo = red_oo[rloc];
-  const float s_yy = red_yy[0][rloc] + red_yy[1][rloc];
-  const bool lin = valid && dn_r > 0.f;
-  const float rden = lin ? 1.0f / dn_r : 0.f;
-  const float dd_r = lin ? -s_yy * rden : 0.f;
-  if (ch == 0 && hl == 0) {
-    dsum[bh * N + row] = valid ? s_oo - s_yy : 0.f;
-    ddel[bh * N + row] = dd_r;
-  }
-  // dN = dY / den (bf16) into LDS, then to global memory from there
-  {
+      for (int kk = 0; kk < 4; ++kk)
+        dwa[x] = mfma32(swz_op32_tr<D>(ys, 16 * kk, 32 * ct, lane), swz_op32_tr<D>(dns, 16 * kk, 32 * ot, lane),
+                        dwa[x]);
+    }
+    // dO . O by rows: each lane's chunks, summed over the D / 8 lanes of a row
+#pragma unroll
+    for (int u = 0; u < OC; ++u) {
+      const int e = tid + 256 * u;
+      const int r = e / (D / 8), c8 = e % (D / 8);
+      const u32x4 dz4 = ld16(dns + swz_off<D>(r, 8 * c8));
+      float pr = 0.f;
+#pragma unroll
+      for (int s2 = 0; s2 < 8; ++s2)
+        pr = __fmaf_rn(bf16_to_f32(static_cast<uint16_t>(u4_elem(dz4, s2))),
+                       bf16_to_f32(static_cast<uint16_t>(u4_elem(oc[u], s2))), pr);
+#pragma unroll
+      for (int m = 1; m < D / 8; m <<= 1) pr += __shfl_xor(pr, m);
+      if (c8 == 0) red_oo[r] = pr;
+    }
+    // dY . Y partial row dots over this lane's c values (the lane's Y pieces,
+    // columns 8 e4 + 4 hl .. + 3 of each tile, from the Y tile)
+    float p_yy = 0.f;
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct)
+#pragma unroll
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const u32x2 yv = ld8(ys + swz_off<D>(rloc, (D / 2) * ch + 32 * ct + 8 * e4 + 4 * hl));
+#pragma unroll
+        for (int x = 0; x < 4; ++x) p_yy = __fmaf_rn(dyt[ct][4 * e4 + x], bf16_to_f32(u4_half(yv, x)), p_yy);
+      }
+    p_yy += __shfl_xor(p_yy, 32);
+    if (hl == 0) red_yy[ch][rloc] = p_yy;
+    __syncthreads();   // the dO and Y tiles read by every wave
+    const float s_oo = red_oo[rloc];
+    const float s_yy = red_yy[0][rloc] + red_yy[1][rloc];
+    const bool lin = valid && dn_r > 0.f;
+    const float rden = lin ? 1.0f / dn_r : 0.f;
+    const float dd_r = lin ? -s_yy * rden : 0.f;
+    if (ch == 0 && hl == 0) {
+      dsum[bh * N + row] = valid ? s_oo - s_yy : 0.f;
+      ddel[bh * N + row] = dd_r;
+    }
+    // dN = dY / den (bf16) into LDS, then to global memory from there
 #pragma unroll
     for (int ct = 0; ct < NT; ++ct)
 #pragma unroll
@@ -187,17 +189,30 @@ __global__ __launch_bounds__(256, 2) void bwd_prep_kernel(
                          pack_bf16x2(dyt[ct][4 * e4 + 2] * rden, dyt[ct][4 * e4 + 3] * rden)};
         st8(&dns[rloc * HP + c0], v);
       }
-  }
-  __syncthreads();
-  {
-    // the block's dN rows, 16 contiguous bytes per lane (whole rows per
-    // instruction instead of one row per lane)
-    uint16_t* dblk = dn + head + static_cast<size_t>(i) * kBlock * D;
+    __syncthreads();
+    {
+      // the block's dN rows, 16 contiguous bytes per lane (whole rows per
+      // instruction instead of one row per lane)
+      uint16_t* dblk = dn + head + static_cast<size_t>(i) * kBlock * D;
 #pragma unroll
-    for (int u = 0; u < kBlock * D / 8 / 256; ++u) {
-      const int e = tid + 256 * u;
-      const int r = e / (D / 8), c8 = e % (D / 8);
-      st16(dblk + static_cast<size_t>(r) * D + 8 * c8, ld16(&dns[r * HP + 8 * c8]));
+      for (int u = 0; u < kBlock * D / 8 / 256; ++u) {
+        const int e = tid + 256 * u;
+        const int r = e / (D / 8), c8 = e % (D / 8);
+        st16(dblk + static_cast<size_t>(r) * D + 8 * c8, ld16(&dns[r * HP + 8 * c8]));
+      }
+    }
+    __syncthreads();   // dns read by every wave before the next block's copies
+  }
+  // the run's dW^T partial, transposed storage dW^T[c][o] (lanes on consecutive o)
+  float* out = dwp + static_cast<size_t>(w) * D * D;
+#pragma unroll
+  for (int x = 0; x < TPW; ++x) {
+    const int tt = wave * TPW + x;
+    const int ct = tt / (D / 32), ot = tt % (D / 32);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int c = 32 * ct + 8 * (e / 4) + 4 * hl + (e % 4);
+      out[static_cast<size_t>(c) * D + 32 * ot + n32] = dwa[x][e];
     }
   }
 }
@@ -818,85 +833,7 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// dW: partial sums over chunks of 64-row blocks, dW^T[c][o] = sum_r Y[r][c] dO[r][o]
-// (A = Y^T staged by transposing in LDS, B = dO^T tile), then a fixed-order
-// reduction of the partials.
-// ---------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(256) void dw_part_kernel(const uint16_t* __restrict__ y,
-                                                      const uint16_t* __restrict__ dO,
-                                                      float* __restrict__ part,
-                                                      long long nblocks, int parts, int N, int L,
-                                                      int T) {
-  constexpr int P = D == 128 ? 152 : 72;
-  constexpr int TILES = (D / 32) * (D / 32);
-  constexpr int TPW = TILES / 4;
-  constexpr int CH = kBlock * D / 8 / 256;   // 16-byte chunks per thread per tensor
-  __shared__ __attribute__((aligned(16))) uint16_t ys[64 * P];
-  __shared__ __attribute__((aligned(16))) uint16_t ds_[64 * P];
-  const int w = blockIdx.x;
-  const long long b0 = nblocks * w / parts, b1 = nblocks * (w + 1) / parts;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n32 = lane & 31;
-  f32x16 acc[TPW];
-#pragma unroll
-  for (int x = 0; x < TPW; ++x) acc[x] = f32x16{};
-  // the next block's rows are loaded into registers while the current one is multiplied
-  u32x4 ry[CH], rd[CH];
-  auto load = [&](long long b) {
-    const int blk = static_cast<int>(b % T);
-    const uint16_t* ysrc = y + static_cast<size_t>(b) * kBlock * D;
-    const uint16_t* dsrc = dO + static_cast<size_t>(b) * kBlock * D;
-#pragma unroll
-    for (int u = 0; u < CH; ++u) {
-      const int e = tid + 256 * u;
-      const int t = e / (D / 8);
-      ry[u] = ld16(ysrc + 8 * static_cast<size_t>(e));
-      const bool ok = blk * kBlock + t < L;   // padded rows of dO do not count
-      rd[u] = ok ? ld16(dsrc + 8 * static_cast<size_t>(e)) : u32x4{0u, 0u, 0u, 0u};
-    }
-  };
-  auto store = [&]() {
-#pragma unroll
-    for (int u = 0; u < CH; ++u) {
-      const int e = tid + 256 * u;
-      const int t = e / (D / 8), c8 = 8 * (e % (D / 8));
-      st16(&ys[t * P + c8], ry[u]);
-      st16(&ds_[t * P + c8], rd[u]);
-    }
-  };
-  if (b0 < b1) load(b0);
-  for (long long b = b0; b < b1; ++b) {
-    __syncthreads();
-    store();
-    if (b + 1 < b1) load(b + 1);
-    __syncthreads();
-    // dW^T[c][o] = sum_t Y[t][c] dO[t][o]: both operands by transpose reads (k = t)
-#pragma unroll
-    for (int x = 0; x < TPW; ++x) {
-      const int tt = wave * TPW + x;
-      const int ct = tt / (D / 32), ot = tt % (D / 32);
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-        acc[x] = mfma32(lds_op32_tr<false>(ys, P, 16 * kk, 32 * ct, lane),
-                        lds_op32_tr<false>(ds_, P, 16 * kk, 32 * ot, lane), acc[x]);
-    }
-  }
-  float* out = part + static_cast<size_t>(w) * D * D;
-#pragma unroll
-  for (int x = 0; x < TPW; ++x) {
-    const int tt = wave * TPW + x;
-    const int ct = tt / (D / 32), ot = tt % (D / 32);
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int c = 32 * ct + 8 * (e / 4) + 4 * (lane >> 5) + (e % 4);
-      const int o = 32 * ot + n32;
-      out[static_cast<size_t>(c) * D + o] = acc[x][e];   // dW^T[c][o]: lanes on consecutive o
-    }
-  }
-}
-
-// Fixed-order reduction of the partials (stored transposed, entry e = c D + o):
+// dW: fixed-order reduction of the partials that bwd_prep writes (stored transposed, entry e = c D + o):
 // workgroup of 256 threads per 64 entries; thread group g (of 4) sums
 // partials g, g + 4, ... in order, and the four group sums are added in order;
 // times the linear-output gate (1 for SLA); written to dW[o][c].
@@ -934,14 +871,15 @@ hipError_t launch_w_transpose(const Dims& d, const uint16_t* w, uint16_t* wT, hi
 
 hipError_t launch_bwd_prep(const Dims& d, const uint16_t* o, const uint16_t* dO,
                            const uint16_t* wT, const float* den, const uint16_t* y, bool linear,
-                           float* dsum, float* ddel, uint16_t* dn, hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>(d.BH() * d.T));
+                           float* dsum, float* ddel, uint16_t* dn, float* dw_part, hipStream_t s) {
+  const long long nblocks = d.BH() * d.T;
+  const int parts = dw_parts(d);
   if (d.D == 128)
-    hipLaunchKernelGGL(bwd_prep_kernel<128>, grid, dim3(256), 0, s, o, dO, wT, den, y, dsum, ddel,
-                       dn, d.N, d.L, d.T, linear, d.gate);
+    hipLaunchKernelGGL(bwd_prep_kernel<128>, dim3(parts), dim3(256), 0, s, o, dO, wT, den, y, dsum,
+                       ddel, dn, dw_part, nblocks, parts, d.N, d.L, d.T, linear, d.gate);
   else
-    hipLaunchKernelGGL(bwd_prep_kernel<64>, grid, dim3(256), 0, s, o, dO, wT, den, y, dsum, ddel,
-                       dn, d.N, d.L, d.T, linear, d.gate);
+    hipLaunchKernelGGL(bwd_prep_kernel<64>, dim3(parts), dim3(256), 0, s, o, dO, wT, den, y, dsum,
+                       ddel, dn, dw_part, nblocks, parts, d.N, d.L, d.T, linear, d.gate);
   return hipGetLastError();
 }
 
@@ -974,21 +912,10 @@ hipError_t launch_bwd_kv(const Dims& d, const uint16_t* q, const uint16_t* k, co
   return hipGetLastError();
 }
 
-hipError_t launch_dw(const Dims& d, const uint16_t* y, const uint16_t* dO, float* part, float* dw,
-                     hipStream_t s) {
-  const long long nblocks = d.BH() * d.T;
-  const int parts = static_cast<int>(std::min<long long>(kDwParts, nblocks));
-  if (d.D == 128)
-    hipLaunchKernelGGL(dw_part_kernel<128>, dim3(parts), dim3(256), 0, s, y, dO, part, nblocks,
-                       parts, d.N, d.L, d.T);
-  else
-    hipLaunchKernelGGL(dw_part_kernel<64>, dim3(parts), dim3(256), 0, s, y, dO, part, nblocks,
-                       parts, d.N, d.L, d.T);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+hipError_t launch_dw_reduce(const Dims& d, const float* part, float* dw, hipStream_t s) {
   const int dd = d.D * d.D;
   hipLaunchKernelGGL(dw_reduce_kernel, dim3((dd + 63) / 64), dim3(256), 0, s, part, dw, dd, d.D,
-                     parts, d.gate);
+                     dw_parts(d), d.gate);
   return hipGetLastError();
 }
 

@@ -397,7 +397,7 @@ sla_status sla_backward(const sla_config* cfg, const void* q, const void* k, con
   SLA_CHECK(launched(launch_mask_lists(d, mask, lut, lut_cnt, rbits, col, col_cnt, cbits, s),
                      "mask_lists"));
   SLA_CHECK(launched(launch_w_transpose(d, static_cast<const uint16_t*>(w), wT, s), "w_transpose"));
-  SLA_CHECK(launched(launch_bwd_prep(d, o16, do16, wT, den, y, linear, dsum, ddel, dn, s),
+  SLA_CHECK(launched(launch_bwd_prep(d, o16, do16, wT, den, y, linear, dsum, ddel, dn, dwp, s),
                      "bwd_prep"));
   if (linear) {
     SLA_CHECK(launched(launch_dstate(d, q16, dn, ddel, states, s), "dstate"));
@@ -416,7 +416,7 @@ sla_status sla_backward(const sla_config* cfg, const void* q, const void* k, con
   SLA_CHECK(launched(launch_bwd_q(d, q16, k16, v16, do16, lse, dsum, lut, lut_cnt, dn, ddel, hst,
                                   zst, linear, dq, s),
                      "bwd_q"));
-  SLA_CHECK(launched(launch_dw(d, y, do16, dwp, dw, s), "dw"));
+  SLA_CHECK(launched(launch_dw_reduce(d, dwp, dw, s), "dw_reduce"));
   SLA_CHECK(stg.end(SLA_STAGE_BWD_Q));
   return SLA_OK;
 }

@@ -50,6 +50,11 @@ struct SavedLayout {
 };
 
 constexpr int kDwParts = 1024;
+// runs of query blocks (one dW partial each) in the backward preparation
+inline int dw_parts(const Dims& d) {
+  const long long nblocks = d.BH() * d.T;
+  return static_cast<int>(nblocks < kDwParts ? nblocks : kDwParts);
+}
 
 WorkspaceLayout workspace_layout(const Dims& d);
 SavedLayout saved_layout(const Dims& d);
@@ -94,7 +99,7 @@ hipError_t launch_attn_fwd(const Dims& d, const uint16_t* q, const uint16_t* k,
 hipError_t launch_w_transpose(const Dims& d, const uint16_t* w, uint16_t* wT, hipStream_t s);
 hipError_t launch_bwd_prep(const Dims& d, const uint16_t* o, const uint16_t* dO,
                            const uint16_t* wT, const float* den, const uint16_t* y, bool linear,
-                           float* dsum, float* ddel, uint16_t* dn, hipStream_t s);
+                           float* dsum, float* ddel, uint16_t* dn, float* dw_part, hipStream_t s);
 hipError_t launch_bwd_q(const Dims& d, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                         const uint16_t* dO, const float* lse, const float* dsum,
                         const int32_t* lut, const int32_t* lut_cnt, const uint16_t* dn,
@@ -104,7 +109,6 @@ hipError_t launch_bwd_kv(const Dims& d, const uint16_t* q, const uint16_t* k, co
                          const uint16_t* dO, const float* lse, const float* dsum,
                          const int32_t* col, const int32_t* col_cnt, const uint16_t* dh,
                          const float* dz, bool linear, float* dk, float* dv, hipStream_t s);
-hipError_t launch_dw(const Dims& d, const uint16_t* y, const uint16_t* dO, float* part, float* dw,
-                     hipStream_t s);
+hipError_t launch_dw_reduce(const Dims& d, const float* part, float* dw, hipStream_t s);
 
 }  // namespace sla
