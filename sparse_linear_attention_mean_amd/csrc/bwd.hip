@@ -457,8 +457,15 @@ __global__ __launch_bounds__(256, 2) void bwd_q_kernel(
 #pragma unroll
       for (int p2 = 0; p2 < 2; ++p2) {
         // phi'(q) for columns 32 at + 16 p2 + 8 (e4 % 2) + 4 hl .. + 3 (e4 = 2 p2, 2 p2 + 1)
+        // (kh is uniform but not a constant: both candidates are read with
+        // static indices and passed through an empty asm before the select,
+        // otherwise the compiler turns the select into an indexed access and
+        // moves the Q fragments to scratch memory)
+        u32x4 q0 = __builtin_bit_cast(u32x4, qf[2 * x + p2]);
+        u32x4 q1 = __builtin_bit_cast(u32x4, qf[2 * (NH + x) + p2]);
+        asm("" : "+v"(q0), "+v"(q1));
         u32x2 qe, qo;
-        row_halves(__builtin_bit_cast(u32x4, qf[2 * at + p2]), qe, qo);
+        row_halves(kh ? q1 : q0, qe, qo);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int e4 = 2 * p2 + h;
