@@ -49,7 +49,7 @@ struct SavedLayout {
   size_t lse, den, y, hst, zst, total;
 };
 
-constexpr int kDwParts = 1024;
+constexpr int kDwParts = 512;
 // runs of query blocks (one dW partial each) in the backward preparation
 inline int dw_parts(const Dims& d) {
   const long long nblocks = d.BH() * d.T;
