@@ -109,6 +109,24 @@ def test_backward_given_mask(d):
     _check_grads(f"given_d{d}", got, ref)
 
 
+@pytest.mark.parametrize("case", [(1, 9, 4160, 64, (26, 8, 20), 4150),
+                                  (2, 8, 4160, 128, (26, 8, 20), 4100)],
+                         ids=["585_blocks_d64", "1040_blocks_d128"])
+def test_backward_multi_block_runs(case):
+    """More query blocks than dW partials (512): the preparation kernel's
+    workgroups run through one to three blocks each, runs that cross head
+    (and batch) boundaries and end in the ragged tail; every gradient, dW in
+    particular, against the oracle."""
+    b, h, n, d, grid, vl = case
+    log(f"multi-block runs: B={b} H={h} N={n} d={d} L={vl} ({b * h * (n // 64)} blocks)")
+    inp = make_inputs(b, h, n, d, grid, vl, seed=31)
+    x = decoded(inp)
+    mask = _oracle_mask(x, 0.1, 0.2, vl)
+    ref = orc.backward(x["q"], x["k"], x["v"], x["w"], x["do"], mask, valid_len=vl)
+    got = _gpu_fwd_bwd(inp, 0.0, 0.0, mask)
+    _check_grads(f"runs_d{d}", got, ref)
+
+
 def test_backward_is_deterministic():
     inp = make_inputs(1, 2, 1024, 128, (4, 16, 16), 1000, seed=21)
     x = decoded(inp)
