@@ -310,7 +310,8 @@ def two_level_selection(dev, hip, group=8, keep=8, steps=5):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; multi-GPU runs are not part of it",
+        print(json.dumps({"error": "the library runs on one GPU; it has no multi-GPU path, "
+                                   "so --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
     import torch
