@@ -138,8 +138,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs args) {
   float m_run = -INFINITY;   // running max (log2 units) of this lane's query
   float l_run = 0.f;         // partial row sum over this lane's keys
 
-  // S^T = K Q^T for the K tile kt; K operand rows read four chunks ahead
-  auto s_tile = [&](const uint16_t* kt) __attribute__((always_inline)) {
+  // S^T = K Q^T for the K tile kt; K operand rows read four chunks ahead;
+  // hook(cc) runs after MFMA cc (the copies of the next tiles are issued
+  // there, one instruction at a time, so a wave that stalls on a full copy
+  // queue does so while its MFMAs run instead of before them)
+  auto s_tile = [&](const uint16_t* kt, auto&& hook) __attribute__((always_inline)) {
     constexpr int KA = C::NCC < 4 ? C::NCC : 4;
     bf16x8 ka[KA];
 #pragma unroll
@@ -152,13 +155,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs args) {
       if (cc + KA < C::NCC)
         ka[cc % KA] = as_bf16x8(ld16(kt + swz_off<D>(32 * kh + n32, 16 * (cc + KA) + 8 * hl)));
       st = mfma32(a, qf[cc], st);
+      hook(cc);
     }
     return st;
   };
+  auto no_hook = [](int) {};
   // online softmax of one S^T tile (base 2, lazy rescale) and O^T += V^T P^T
   // with the V tile vt; masked: the tile of the padded last key block jl
-  auto soft_pv = [&](f32x16 st, const uint16_t* vt,
-                     bool masked) __attribute__((always_inline)) {
+  auto soft_pv = [&](f32x16 st, const uint16_t* vt, bool masked) __attribute__((always_inline)) {
     if (masked) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
@@ -211,11 +215,19 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs args) {
   // n - 1 in sp; K_{n+1} is copied into kn (the buffer of K_{n-1}) and V_n
   // into vn (the buffer of V_{n-2}).
   f32x16 sp;
+  // (the copy instructions go between the S^T MFMAs: D / 32 for the K tile,
+  // then D / 32 for the V tile, one after each of the D / 16 MFMAs)
   auto iter = [&](int n, const uint16_t* kc, uint16_t* kn, uint16_t* vn,
                   const uint16_t* vp) __attribute__((always_inline)) {
-    copy_k(n + 1, kn);
-    copy_v(n, vn);
-    const f32x16 sn = s_tile(kc);
+    const bool kmore = n + 1 < cnt;
+    const int jk = kmore ? block_at(n + 1) : 0, jv = block_at(n);
+    const f32x16 sn = s_tile(kc, [&](int cc) __attribute__((always_inline)) {
+      if (cc < D / 32) {
+        if (kmore) copy_swz_buf_one<D, 4>(krs, jk * kBlock, kn, wave, lane, cc);
+      } else {
+        copy_swz_buf_one<D, 4>(vrs, jv * kBlock, vn, wave, lane, cc - D / 32);
+      }
+    });
     soft_pv(sp, vp, false);
     sp = sn;
     sync();
@@ -228,7 +240,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs args) {
     sync();
     copy_k(1, kb1);
     copy_v(0, vb0);
-    sp = s_tile(kb0);
+    sp = s_tile(kb0, no_hook);
     sync();
     int n = 1;
     for (; n + 1 < cnt; n += 2) {

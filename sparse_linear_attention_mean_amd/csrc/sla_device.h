@@ -231,6 +231,18 @@ __device__ __forceinline__ void copy_swz_buf(__amdgpu_buffer_rsrc_t rs, int row0
                                              16, voff, 0, 0, 0);
   }
 }
+// the u-th of this wave's kCopies / NW copy instructions of copy_swz_buf
+// (callers spread them between independent work)
+template <int D, int NW>
+__device__ __forceinline__ void copy_swz_buf_one(__amdgpu_buffer_rsrc_t rs, int row0, uint16_t* dst,
+                                                 int w, int lane, int u) {
+  const int it = w + NW * u;
+  const int p = it * 64 + lane;
+  const int r = p / (D / 8), sl = p % (D / 8);
+  const int voff = ((row0 + r) * D + 8 * (sl ^ swz<D>(r))) * 2;
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + it * 512),
+                                           16, voff, 0, 0, 0);
+}
 // four consecutive rows of one column: lane gets M[kb + 4 (l/32) + s][n0 + l%32], s < 4
 template <int D>
 __device__ __forceinline__ u32x2 swz_col4(const uint16_t* m, int kb, int n0, int lane) {
