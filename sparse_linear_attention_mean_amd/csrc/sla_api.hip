@@ -369,7 +369,6 @@ sla_status sla_backward(const sla_config* cfg, const void* q, const void* k, con
   auto* lut_cnt = reinterpret_cast<int32_t*>(ws + wl.lut_cnt);
   auto* col = reinterpret_cast<int32_t*>(ws + wl.col);
   auto* col_cnt = reinterpret_cast<int32_t*>(ws + wl.col_cnt);
-  auto* rbits = reinterpret_cast<uint32_t*>(ws + wl.rbits);
   auto* cbits = reinterpret_cast<uint32_t*>(ws + wl.cbits);
   auto* states = reinterpret_cast<uint16_t*>(ws + wl.states);
   auto* dh = reinterpret_cast<uint16_t*>(ws + wl.dstate);
@@ -394,7 +393,8 @@ sla_status sla_backward(const sla_config* cfg, const void* q, const void* k, con
   const bool linear = d.global || given || ((d.km > 0 || d.G > 0) && d.kc < d.T);
 
   SLA_CHECK(stg.begin(SLA_STAGE_BWD_PRE));
-  SLA_CHECK(launched(launch_mask_lists(d, mask, lut, lut_cnt, rbits, col, col_cnt, cbits, s),
+  // (the row bits only feed the forward's aggregation: not built here)
+  SLA_CHECK(launched(launch_mask_lists(d, mask, lut, lut_cnt, nullptr, col, col_cnt, cbits, s),
                      "mask_lists"));
   SLA_CHECK(launched(launch_w_transpose(d, static_cast<const uint16_t*>(w), wT, s), "w_transpose"));
   SLA_CHECK(launched(launch_bwd_prep(d, o16, do16, wT, den, y, linear, dsum, ddel, dn, dwp, s),
