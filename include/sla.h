@@ -112,9 +112,10 @@ enum {
   SLA_STAGE_CLASSIFY = 2,   /* forward: compressed scores + classification  */
   SLA_STAGE_AGGREGATE = 3,  /* forward: marginal sums H_i, Z_i (or totals)  */
   SLA_STAGE_ATTENTION = 4,  /* forward: fused sparse + linear + projection  */
-  SLA_STAGE_BWD_PRE = 5,    /* backward: mask lists, D, dY, linear dQ, dH   */
-  SLA_STAGE_BWD_KV = 6,     /* backward: transposed sums, dK and dV         */
-  SLA_STAGE_BWD_Q = 7       /* backward: sparse dQ and dW                   */
+  SLA_STAGE_BWD_PRE = 5,    /* backward: mask lists, D, dN, dW partials,
+                                dH / dZ and their transposed sums        */
+  SLA_STAGE_BWD_KV = 6,     /* backward: dK and dV (sparse + linear)        */
+  SLA_STAGE_BWD_Q = 7       /* backward: dQ (sparse + linear), dW reduction */
 };
 
 typedef struct sla_config {
