@@ -14,9 +14,9 @@
 //       dphi(k_t) = dh_j v_t + dz_j, dK += dphi(k) phi'(k), dV += phi(K_j) dh_j
 // Deterministic: every reduction has a fixed order, no atomics.
 //
-// Kernels here: the query-side preparation (dY, D, dN, dd and the linear dQ),
-// the KV-major sparse + linear dK / dV kernel, the Q-major sparse dQ kernel,
-// the two-stage dW reduction and two small transposes.
+// Kernels here: the query-side preparation (dY, D, dN, dd and the dW
+// partials), the KV-major sparse + linear dK / dV kernel, the Q-major sparse +
+// linear dQ kernel, the fixed-order dW reduction and the W transpose.
 #include "sla_device.h"
 #include "sla_internal.h"
 
