@@ -253,38 +253,46 @@ __global__ __launch_bounds__(256) void scores_kernel(const float* __restrict__ q
                                                      const float* __restrict__ kbar,
                                                      float* __restrict__ scores, int T,
                                                      float scale) {
-  constexpr int A4 = D / 4;   // float4 columns; one float4 of row padding
-  __shared__ f32x4 qs[64][A4 + 1];
-  __shared__ f32x4 ks[64][A4 + 1];
+  constexpr int A4 = D / 4;   // float4 columns of a row
+  constexpr int AC = 8;       // float4 columns staged at a time (32 of the a)
+  // one float4 of row padding: the 16 rows a wave reads fall on distinct banks.
+  // (Staging 32 of the a at a time keeps the LDS per workgroup at 18 KB, so
+  // eight workgroups share a compute unit; the order of the fused
+  // multiply-adds, a = 0 .. D - 1, is the same.)
+  __shared__ f32x4 qs[64][AC + 1];
+  __shared__ f32x4 ks[64][AC + 1];
   const int bh = blockIdx.z;
   const int i0 = blockIdx.y * 64, j0 = blockIdx.x * 64;
   const f32x4* qh = reinterpret_cast<const f32x4*>(qbar + static_cast<size_t>(bh) * T * D);
   const f32x4* kh = reinterpret_cast<const f32x4*>(kbar + static_cast<size_t>(bh) * T * D);
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-  for (int e = threadIdx.x; e < 64 * A4; e += 256) {
-    const int r = e / A4, a4 = e % A4;
-    qs[r][a4] = (i0 + r < T) ? qh[static_cast<size_t>(i0 + r) * A4 + a4] : zero;
-    ks[r][a4] = (j0 + r < T) ? kh[static_cast<size_t>(j0 + r) * A4 + a4] : zero;
-  }
-  __syncthreads();
   const int ty = threadIdx.x / 16, tx = threadIdx.x % 16;
   float acc[4][4] = {};
+  for (int c0 = 0; c0 < A4; c0 += AC) {
+    __syncthreads();   // the previous columns are consumed
+    for (int e = threadIdx.x; e < 64 * AC; e += 256) {
+      const int r = e / AC, a4 = e % AC;
+      qs[r][a4] = (i0 + r < T) ? qh[static_cast<size_t>(i0 + r) * A4 + c0 + a4] : zero;
+      ks[r][a4] = (j0 + r < T) ? kh[static_cast<size_t>(j0 + r) * A4 + c0 + a4] : zero;
+    }
+    __syncthreads();
 #pragma unroll 2
-  for (int a4 = 0; a4 < A4; ++a4) {
-    f32x4 qv[4], kv[4];
+    for (int a4 = 0; a4 < AC; ++a4) {
+      f32x4 qv[4], kv[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) qv[r] = qs[ty + 16 * r][a4];
+      for (int r = 0; r < 4; ++r) qv[r] = qs[ty + 16 * r][a4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) kv[c] = ks[tx + 16 * c][a4];
+      for (int c = 0; c < 4; ++c) kv[c] = ks[tx + 16 * c][a4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+      for (int r = 0; r < 4; ++r)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {   // a = 4 a4 + 0 .. 3, in order
-        acc[r][c] = __fmaf_rn(qv[r][0], kv[c][0], acc[r][c]);
-        acc[r][c] = __fmaf_rn(qv[r][1], kv[c][1], acc[r][c]);
-        acc[r][c] = __fmaf_rn(qv[r][2], kv[c][2], acc[r][c]);
-        acc[r][c] = __fmaf_rn(qv[r][3], kv[c][3], acc[r][c]);
-      }
+        for (int c = 0; c < 4; ++c) {   // a = 4 (c0 + a4) + 0 .. 3, in order
+          acc[r][c] = __fmaf_rn(qv[r][0], kv[c][0], acc[r][c]);
+          acc[r][c] = __fmaf_rn(qv[r][1], kv[c][1], acc[r][c]);
+          acc[r][c] = __fmaf_rn(qv[r][2], kv[c][2], acc[r][c]);
+          acc[r][c] = __fmaf_rn(qv[r][3], kv[c][3], acc[r][c]);
+        }
+    }
   }
 #pragma unroll
   for (int r = 0; r < 4; ++r)
