@@ -699,6 +699,57 @@ __global__ __launch_bounds__(64) void mask_lists_kernel(const int8_t* __restrict
   if (lane == 0) cnts[bh * T + x] = cnt;
 }
 
+// The column pass when T is a multiple of 4: one wave per four adjacent
+// columns, each row's four mask bytes read with one aligned 32-bit load (the
+// byte-per-row column reads touch 64 cache lines per instruction; this reads
+// each line once for four columns).  Same lists, counts and bits as the
+// column half of mask_lists_kernel.
+__global__ __launch_bounds__(64) void mask_cols4_kernel(const int8_t* __restrict__ mask,
+                                                        int32_t* __restrict__ col,
+                                                        int32_t* __restrict__ col_cnt,
+                                                        uint32_t* __restrict__ cbits, int T,
+                                                        int Tp) {
+  const int x0 = 4 * blockIdx.x;
+  const long long bh = blockIdx.y;
+  const int lane = threadIdx.x;
+  const int words = Tp / 32;
+  const int8_t* m = mask + bh * T * T;
+  // columns x0 .. x0 + 3 < Tp; those at or past T only get cleared bits
+  const int ncols = x0 + 4 <= T ? 4 : (x0 < T ? T - x0 : 0);
+  int cnt[4] = {0, 0, 0, 0};
+  for (int base = 0; base < Tp; base += 64) {
+    const int y = base + lane;
+    // x0 + 3 < T whenever ncols > 0 (T is a multiple of 4), so the word is
+    // inside row y; rows past T read as all-negligible
+    const uint32_t v4 = (y < T && ncols > 0)
+                            ? *reinterpret_cast<const uint32_t*>(m + static_cast<long long>(y) * T + x0)
+                            : 0xFFFFFFFFu;
+#pragma unroll
+    for (int xi = 0; xi < 4; ++xi) {
+      const int x = x0 + xi;
+      const int8_t val = static_cast<int8_t>((v4 >> (8 * xi)) & 0xffu);
+      const bool crit = xi < ncols && val == 1;
+      const bool marg = xi < ncols && val == 0;
+      const unsigned long long bc = __ballot(crit);
+      if (crit) col[(bh * T + x) * T + cnt[xi] + __popcll(bc & ((1ull << lane) - 1ull))] = y;
+      cnt[xi] += __popcll(bc);
+      const unsigned long long bm = __ballot(marg);
+      if (cbits && lane == 0 && x < Tp) {
+        uint32_t* brow = cbits + bh * words * Tp + x;   // word w at brow[w * Tp]
+        brow[(base / 32) * Tp] = static_cast<uint32_t>(bm);
+        if (base / 32 + 1 < words) brow[(base / 32 + 1) * Tp] = static_cast<uint32_t>(bm >> 32);
+      }
+    }
+  }
+  if (lane < ncols) {
+    int c = cnt[0];
+    c = lane == 1 ? cnt[1] : c;
+    c = lane == 2 ? cnt[2] : c;
+    c = lane == 3 ? cnt[3] : c;
+    col_cnt[bh * T + x0 + lane] = c;
+  }
+}
+
 __global__ void fill_mask_kernel(int8_t* __restrict__ mask, long long n, int8_t value) {
   for (long long e = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x; e < n;
        e += static_cast<long long>(gridDim.x) * blockDim.x)
@@ -803,9 +854,17 @@ hipError_t launch_classify_hier(const Dims& d, const float* qbar, const float* k
 hipError_t launch_mask_lists(const Dims& d, const int8_t* mask, int32_t* lut, int32_t* lut_cnt,
                              uint32_t* rbits, int32_t* col, int32_t* col_cnt, uint32_t* cbits,
                              hipStream_t s) {
-  const unsigned z = col ? 2u : 1u;
+  // rows (and, unless T is a multiple of 4, columns) by mask_lists_kernel
+  const bool cols4 = col != nullptr && d.T % 4 == 0;
+  const unsigned z = (col && !cols4) ? 2u : 1u;
   hipLaunchKernelGGL(mask_lists_kernel, dim3(d.Tp, static_cast<unsigned>(d.BH()), z), dim3(64), 0,
                      s, mask, lut, lut_cnt, rbits, col, col_cnt, cbits, d.T, d.Tp);
+  if (cols4) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(mask_cols4_kernel, dim3(d.Tp / 4, static_cast<unsigned>(d.BH())), dim3(64),
+                       0, s, mask, col, col_cnt, cbits, d.T, d.Tp);
+  }
   return hipGetLastError();
 }
 
