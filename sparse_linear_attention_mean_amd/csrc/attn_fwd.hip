@@ -99,8 +99,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs args) {
 
   const int cnt = DENSE ? T : args.lut_cnt[bh * T + i];
   const int32_t* lrow = DENSE ? nullptr : args.lut + (bh * T + i) * static_cast<long long>(T);
-  // the list is held in a register, entry 64 g + l in lane l (g = n / 64): the
-  // loop takes its block indices with readlane instead of a memory load
+  // the list is held in a register, entry 64 g + l in lane l for the current
+  // group g = n / 64 (reloaded when the loop enters the next group): the loop
+  // takes its block indices with readlane instead of a memory load
   int lutv = 0;
   if (!DENSE && lane < cnt) lutv = lrow[lane];
   auto block_at = [&](int n) { return DENSE ? n : __builtin_amdgcn_readlane(lutv, n & 63); };
@@ -219,8 +220,15 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs args) {
   // then D / 32 for the V tile, one after each of the D / 16 MFMAs)
   auto iter = [&](int n, const uint16_t* kc, uint16_t* kn, uint16_t* vn,
                   const uint16_t* vp) __attribute__((always_inline)) {
+    const int jv = block_at(n);
+    // entry n + 1 starts a new group of 64: the register takes the next 64
+    // entries of the list (after entry n was read above)
+    if (!DENSE && ((n + 1) & 63) == 0 && n + 1 < cnt) {
+      const int e = n + 1 + lane;
+      lutv = e < cnt ? lrow[e] : 0;
+    }
     const bool kmore = n + 1 < cnt;
-    const int jk = kmore ? block_at(n + 1) : 0, jv = block_at(n);
+    const int jk = kmore ? block_at(n + 1) : 0;
     const f32x16 sn = s_tile(kc, [&](int cc) __attribute__((always_inline)) {
       if (cc < D / 32) {
         if (kmore) copy_swz_buf_one<D, 4>(krs, jk * kBlock, kn, wave, lane, cc);

@@ -679,7 +679,6 @@ __global__ __launch_bounds__(512, 1) void bwd_kv_kernel(
   // one query block from (qt: Q_i then dO_i, lt); the next one is copied into (qn, ln)
   auto step = [&](int n, const uint16_t* qt, const float* lt, uint16_t* qn,
                   float* ln) __attribute__((always_inline)) {
-    const uint16_t* dt = qt + C::kTile;
     if (((n + 1) & 63) == 0 && n + 1 < cnt) {
       const int e = n + 1 + lane;   // the next 64 entries of the list
       colv = e < cnt ? crow[e] : 0;

@@ -127,6 +127,22 @@ def test_backward_multi_block_runs(case):
     _check_grads(f"runs_d{d}", got, ref)
 
 
+def test_dw_runs_of_24_query_blocks():
+    """dW with 12,288 query blocks, so that each of the preparation kernel's
+    512 runs holds 24 blocks, as in the benchmark's layout (B = 2, H = 12,
+    T = 512); here B = 1, H = 24 at d = 64 keeps the oracle to seconds.  Runs
+    cross head boundaries and the ragged tail of every head; every gradient,
+    dW in particular, against the oracle."""
+    b, h, n, d, vl = 1, 24, 32768, 64, 32760
+    log(f"dW runs of 24 blocks: B={b} H={h} N={n} d={d} L={vl} ({b * h * (n // 64)} blocks)")
+    inp = make_inputs(b, h, n, d, (21, 30, 52), vl, seed=37)
+    x = decoded(inp)
+    mask = _oracle_mask(x, 0.02, 0.9, vl)
+    got = _gpu_fwd_bwd(inp, 0.0, 0.0, mask)
+    ref = orc.backward(x["q"], x["k"], x["v"], x["w"], x["do"], mask, valid_len=vl)
+    _check_grads("runs24_d64", got, ref)
+
+
 def test_backward_is_deterministic():
     inp = make_inputs(1, 2, 1024, 128, (4, 16, 16), 1000, seed=21)
     x = decoded(inp)

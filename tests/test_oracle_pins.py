@@ -29,6 +29,39 @@ def _random_mask(bsz, nh, t, seed, p=(0.3, 0.5, 0.2)):
 
 
 # ---------------------------------------------------------------------------
+# bf16 decoding: known bit patterns (every other pin decodes through it)
+# ---------------------------------------------------------------------------
+def test_decode_bf16_known_bit_patterns():
+    """A bf16 value is the upper half of the fp32 with the same bits: sign,
+    8 exponent bits (bias 127), 7 mantissa bits; exponent 0 is subnormal,
+    exponent 255 is infinity / NaN.  Values written from that definition."""
+    cases = [
+        (0x3F80, 1.0),
+        (0xC000, -2.0),
+        (0x3FC0, 1.5),                           # mantissa 1000000b
+        (0x4049, 3.140625),                      # 2 * (1 + 73 / 128)
+        (0x0080, 2.0 ** -126),                   # smallest normal
+        (0x0001, 2.0 ** -133),                   # smallest subnormal: 2^-126 * 2^-7
+        (0x007F, 127 * 2.0 ** -133),             # largest subnormal
+        (0x7F7F, (2.0 - 2.0 ** -7) * 2.0 ** 127),  # largest finite
+        (0x7F80, math.inf),
+        (0xFF80, -math.inf),
+        (0x0000, 0.0),
+    ]
+    bits = np.array([c[0] for c in cases], np.uint16)
+    got = orc.decode_bf16(bits)
+    assert got.dtype == np.float64
+    for (b, want), g in zip(cases, got):
+        assert g == want, (hex(b), g, want)
+    neg0 = orc.decode_bf16(np.array([0x8000], np.uint16))[0]
+    assert neg0 == 0.0 and math.copysign(1.0, neg0) == -1.0
+    assert math.copysign(1.0, got[-1]) == 1.0
+    assert np.isnan(orc.decode_bf16(np.array([0x7FC0, 0xFFC1], np.uint16))).all()
+    # shape is kept
+    assert orc.decode_bf16(np.full((2, 3), 0x3F80, np.uint16)).shape == (2, 3)
+
+
+# ---------------------------------------------------------------------------
 # token-level brute force (independent of block states and of the oracle)
 # ---------------------------------------------------------------------------
 def brute_force_head(q, k, v, w, mask, valid_len, scale):
