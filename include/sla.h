@@ -71,7 +71,8 @@
  *    returns SLA_ERR_DEVICE; device faults surface at the caller's next
  *    synchronisation.
  *  - Outputs are overwritten, never accumulated; inputs are never written.
- *  - Calls are reentrant: no mutable global state.  Two calls that share a
+ *  - Calls are reentrant: no mutable global state apart from the static
+ *    scratch of sla_forward_static (below).  Two calls that share a
  *    workspace or saved buffer must be ordered on one stream.
  */
 #ifndef SLA_H_
@@ -186,6 +187,30 @@ sla_status sla_backward(const sla_config* cfg, const void* q, const void* k, con
                         const void* w, const void* o, const void* d_o, const int8_t* mask,
                         const void* saved, float* dq, float* dk, float* dv, float* dw,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Allocation-free forward, for callers that cannot allocate device memory or
+ * hand the library a workspace: code under HIP graph capture, tight serving
+ * loops (a denoising loop that calls the layer every step), harnesses that
+ * forbid hipMalloc.  Same arguments and results as sla_forward without the
+ * workspace: the scratch is a fixed device array of SLA_STATIC_SCRATCH_BYTES
+ * inside the library, one per GPU, which each GPU the library runs on holds
+ * until the process ends.  The call allocates nothing and uses the array of
+ * the current device (``stream`` must belong to it).  The B*H (batch, head)
+ * problems run in passes of as many problems as the array holds, so outputs
+ * are bit-identical to sla_forward's; a configuration whose single (batch,
+ * head) problem needs more scratch than the array returns SLA_ERR_WORKSPACE
+ * before anything is enqueued (at d = 128 above T = 1440, i.e. N = 92160; every
+ * supported size fits at d = 64).
+ * cfg->stage_events is ignored.  Every call on one GPU shares that GPU's
+ * array, whose contents persist between calls: two calls that can overlap on
+ * one GPU (different streams, or threads without ordering) race on it and
+ * must be serialised by the caller.
+ */
+#define SLA_STATIC_SCRATCH_BYTES (64ull << 20)
+sla_status sla_forward_static(const sla_config* cfg, const void* q, const void* k,
+                              const void* v, const void* w, void* o, int8_t* mask, void* saved,
+                              void* stream);
 
 /* The compressed score map alone: scores fp32 [B,H,T,T] (out), bit-identical
    to the map sla_forward classifies in SLA_MASK_COMPUTE mode. */

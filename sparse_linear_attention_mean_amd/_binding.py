@@ -30,8 +30,9 @@ STAGES = ("kv_state", "pool_q", "classify", "aggregate", "attention", "bwd_pre",
 EXPORTED = (
     "sla_block_counts", "sla_workspace_size", "sla_saved_size", "sla_saved_offsets",
     "sla_forward", "sla_backward", "sla_pool_scores", "sla_classify", "sla_coarse_scores",
-    "sla_classify_hier", "sla_status_string", "sla_last_error",
+    "sla_classify_hier", "sla_status_string", "sla_last_error", "sla_forward_static",
 )
+SLA_STATIC_SCRATCH_BYTES = 64 << 20
 
 
 class SlaConfig(ctypes.Structure):
@@ -73,6 +74,7 @@ def _load() -> ctypes.CDLL:
         "sla_saved_size": (sz, [cfgp]),
         "sla_saved_offsets": (ctypes.c_int, [cfgp, szp, szp, szp, szp, szp]),
         "sla_forward": (ctypes.c_int, [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "sla_forward_static": (ctypes.c_int, [cfgp, vp, vp, vp, vp, vp, vp, vp, vp]),
         "sla_backward": (ctypes.c_int, [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                         sz, vp]),
         "sla_pool_scores": (ctypes.c_int, [cfgp, vp, vp, vp, vp, sz, vp]),
@@ -141,6 +143,11 @@ def sla_forward(cfg, q, k, v, w, o, mask, saved, workspace, stream=None) -> None
     _check(lib.sla_forward(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v), _ptr(w), _ptr(o),
                            _ptr(mask), _ptr(saved), _ptr(workspace),
                            workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def sla_forward_static(cfg, q, k, v, w, o, mask, saved, stream=None) -> None:
+    _check(lib.sla_forward_static(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v), _ptr(w), _ptr(o),
+                                  _ptr(mask), _ptr(saved), _stream(stream)))
 
 
 def sla_backward(cfg, q, k, v, w, o, d_o, mask, saved, dq, dk, dv, dw, workspace,

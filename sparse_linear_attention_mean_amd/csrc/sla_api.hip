@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "sla_device.h"
 #include "sla_internal.h"
@@ -199,6 +200,179 @@ SavedLayout saved_layout(const Dims& d) {
   return s;
 }
 
+namespace {
+
+sla_status check_forward_ptrs(const void* q, const void* k, const void* v, const void* w,
+                              const void* o, const void* mask, const void* saved) {
+  SLA_CHECK(check_ptr(q, "q"));
+  SLA_CHECK(check_ptr(k, "k"));
+  SLA_CHECK(check_ptr(v, "v"));
+  SLA_CHECK(check_ptr(w, "w"));
+  SLA_CHECK(check_ptr(o, "o"));
+  SLA_CHECK(check_ptr(mask, "mask"));
+  SLA_CHECK(check_ptr(saved, "saved"));
+  return SLA_OK;
+}
+
+// The forward's scratch regions (a subset of the workspace).
+struct FwdScratch {
+  float* qbar;
+  float* kbar;
+  float* kgbar;
+  float* scores;
+  int32_t* lut;
+  int32_t* lut_cnt;
+  uint32_t* rbits;
+  uint16_t* states;
+};
+
+// The forward's outputs: O, the mask and the regions of the saved state.
+struct FwdOut {
+  uint16_t* o;
+  int8_t* mask;
+  float* lse;
+  float* den;
+  uint16_t* y;
+  uint16_t* hst;
+  float* zst;
+};
+
+// Enqueue the whole forward for the B*H problems of d on s.
+sla_status forward_run(const Dims& d, const uint16_t* q16, const uint16_t* k16,
+                       const uint16_t* v16, const uint16_t* w16, const FwdOut& out,
+                       const FwdScratch& fs, Stages stg, hipStream_t s) {
+  int8_t* mask = out.mask;
+  const bool given = d.mask_mode == SLA_MASK_GIVEN;
+  // all blocks critical: plain dense attention, no classification, no linear branch
+  const bool dense = !given && d.kc == d.T && !d.global;
+  // (the two-level split can leave marginal blocks even when the flat one has none)
+  const bool linear = d.global || given || ((d.km > 0 || d.G > 0) && d.kc < d.T);
+  uint32_t* bits = d.global ? nullptr : fs.rbits;   // the global branch needs no marginal bits
+
+  if (dense) {
+    SLA_CHECK(launched(launch_fill_mask(d, mask, 1, s), "fill_mask"));
+  } else {
+    if (linear || !given) {
+      SLA_CHECK(stg.begin(SLA_STAGE_KV_STATE));
+      SLA_CHECK(launched(launch_kv_state(d, k16, v16, fs.kbar, fs.states, s), "kv_state"));
+      SLA_CHECK(stg.end(SLA_STAGE_KV_STATE));
+    }
+    if (!given) {
+      SLA_CHECK(stg.begin(SLA_STAGE_POOL_Q));
+      SLA_CHECK(launched(launch_pool(d, q16, fs.qbar, s), "pool_q"));
+      SLA_CHECK(stg.end(SLA_STAGE_POOL_Q));
+      SLA_CHECK(stg.begin(SLA_STAGE_CLASSIFY));
+      if (d.G > 0) {
+        // two-level: group means of K, then coarse and candidate scores inside the classifier
+        SLA_CHECK(launched(launch_group_means(d, fs.kbar, fs.kgbar, s), "group_means"));
+        SLA_CHECK(launched(launch_classify_hier(d, fs.qbar, fs.kgbar, fs.kbar, nullptr, nullptr,
+                                                mask, fs.lut, fs.lut_cnt, bits, s),
+                           "classify_hier"));
+      } else {
+        SLA_CHECK(launched(launch_scores(d, fs.qbar, fs.kbar, fs.scores, s), "scores"));
+        SLA_CHECK(launched(launch_classify(d, fs.scores, mask, fs.lut, fs.lut_cnt, bits, s),
+                           "classify"));
+      }
+      SLA_CHECK(stg.end(SLA_STAGE_CLASSIFY));
+    } else {
+      SLA_CHECK(stg.begin(SLA_STAGE_CLASSIFY));
+      SLA_CHECK(launched(launch_mask_lists(d, mask, fs.lut, fs.lut_cnt, bits, nullptr, nullptr,
+                                           nullptr, s),
+                         "mask_lists"));
+      SLA_CHECK(stg.end(SLA_STAGE_CLASSIFY));
+    }
+    if (linear) {
+      SLA_CHECK(stg.begin(SLA_STAGE_AGGREGATE));
+      if (d.global)
+        SLA_CHECK(launched(launch_state_total(d, fs.states, out.hst, out.zst, s), "state_total"));
+      else
+        SLA_CHECK(launched(launch_aggregate(d, fs.rbits, fs.states, out.hst, out.zst, s), "aggregate"));
+      SLA_CHECK(stg.end(SLA_STAGE_AGGREGATE));
+    }
+  }
+  SLA_CHECK(stg.begin(SLA_STAGE_ATTENTION));
+  SLA_CHECK(launched(launch_attn_fwd(d, q16, k16, v16, w16, fs.lut, fs.lut_cnt, dense, linear,
+                                     out.hst, out.zst, out.o, out.lse, out.den, out.y, s),
+                     "attention"));
+  SLA_CHECK(stg.end(SLA_STAGE_ATTENTION));
+  return SLA_OK;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Allocation-free forward.  The forward's scratch lives in one fixed device
+// array per GPU instead of a caller workspace; the B*H problems run in passes
+// of as many (batch, head) problems as the array holds.  In host code the
+// array's name only stands in for the symbol: kernels and copies get the
+// device address that hipGetSymbolAddress returns for the current device,
+// looked up once per device and kept in g_scratch.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[SLA_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+struct ScratchSlot {
+  std::once_flag once;
+  void* ptr = nullptr;
+  hipError_t err = hipSuccess;
+};
+ScratchSlot g_scratch[kMaxDevices];
+
+// Device address of the current device's copy of ``scratch``.
+sla_status static_scratch(char** base) {
+  int dev = -1;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SLA_ERR_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(SLA_ERR_UNSUPPORTED, "device %d is beyond the %d the library supports", dev,
+                kMaxDevices);
+  ScratchSlot& slot = g_scratch[dev];
+  std::call_once(slot.once, [&slot]() {
+    slot.err = hipGetSymbolAddress(&slot.ptr, HIP_SYMBOL(scratch));
+  });
+  if (slot.err != hipSuccess || slot.ptr == nullptr)
+    return fail(SLA_ERR_DEVICE, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(slot.err));
+  *base = static_cast<char*>(slot.ptr);
+  return SLA_OK;
+}
+
+// The forward's regions for the B*H problems of d, packed (256-byte aligned).
+struct FwdLayout {
+  size_t qbar, kbar, kgbar, scores, lut, lut_cnt, rbits, states, total;
+};
+FwdLayout forward_layout(const Dims& d) {
+  FwdLayout f{};
+  const size_t BH = static_cast<size_t>(d.BH());
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  f.qbar = take(BH * d.T * d.D * 4);
+  f.kbar = take(BH * d.T * d.D * 4);
+  f.kgbar = take(BH * (d.G > 0 ? d.Tg : 1) * d.D * 4);
+  f.scores = take(BH * d.T * d.T * 4);
+  f.lut = take(BH * d.T * d.T * 4);
+  f.lut_cnt = take(BH * d.T * 4);
+  f.rbits = take(BH * d.Tp * (d.Tp / 32) * 4);
+  f.states = take(BH * d.Tp * d.NB * 2);
+  f.total = off;
+  return f;
+}
+
+Dims with_problems(const Dims& d, int n) {
+  Dims c = d;
+  c.B = 1;
+  c.H = n;
+  return c;
+}
+
+}  // namespace
+
 }  // namespace sla
 
 using namespace sla;
@@ -244,96 +418,76 @@ sla_status sla_forward(const sla_config* cfg, const void* q, const void* k, cons
                        size_t workspace_bytes, void* stream) {
   Dims d;
   SLA_CHECK(make_dims(cfg, &d));
-  SLA_CHECK(check_ptr(q, "q"));
-  SLA_CHECK(check_ptr(k, "k"));
-  SLA_CHECK(check_ptr(v, "v"));
-  SLA_CHECK(check_ptr(w, "w"));
-  SLA_CHECK(check_ptr(o, "o"));
-  SLA_CHECK(check_ptr(mask, "mask"));
-  SLA_CHECK(check_ptr(saved, "saved"));
+  SLA_CHECK(check_forward_ptrs(q, k, v, w, o, mask, saved));
   SLA_CHECK(check_ptr(workspace, "workspace"));
   const WorkspaceLayout wl = workspace_layout(d);
   if (workspace_bytes < wl.total)
     return fail(SLA_ERR_WORKSPACE, "workspace of %zu bytes is below the required %zu",
                 workspace_bytes, wl.total);
-  const SavedLayout sl = saved_layout(d);
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  Stages stg{static_cast<hipEvent_t*>(cfg->stage_events), s};
   char* ws = static_cast<char*>(workspace);
+  const FwdScratch fs{reinterpret_cast<float*>(ws + wl.qbar), reinterpret_cast<float*>(ws + wl.kbar),
+                      reinterpret_cast<float*>(ws + wl.kgbar), reinterpret_cast<float*>(ws + wl.scores),
+                      reinterpret_cast<int32_t*>(ws + wl.lut), reinterpret_cast<int32_t*>(ws + wl.lut_cnt),
+                      reinterpret_cast<uint32_t*>(ws + wl.rbits), reinterpret_cast<uint16_t*>(ws + wl.states)};
+  const SavedLayout sl = saved_layout(d);
   char* sv = static_cast<char*>(saved);
-  auto* lut = reinterpret_cast<int32_t*>(ws + wl.lut);
-  auto* lut_cnt = reinterpret_cast<int32_t*>(ws + wl.lut_cnt);
-  auto* rbits = reinterpret_cast<uint32_t*>(ws + wl.rbits);
-  auto* states = reinterpret_cast<uint16_t*>(ws + wl.states);
-  auto* hst = reinterpret_cast<uint16_t*>(sv + sl.hst);
-  auto* zst = reinterpret_cast<float*>(sv + sl.zst);
-  const auto* q16 = static_cast<const uint16_t*>(q);
-  const auto* k16 = static_cast<const uint16_t*>(k);
-  const auto* v16 = static_cast<const uint16_t*>(v);
+  const FwdOut out{static_cast<uint16_t*>(o), mask, reinterpret_cast<float*>(sv + sl.lse),
+                   reinterpret_cast<float*>(sv + sl.den), reinterpret_cast<uint16_t*>(sv + sl.y),
+                   reinterpret_cast<uint16_t*>(sv + sl.hst), reinterpret_cast<float*>(sv + sl.zst)};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return forward_run(d, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                     static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(w), out, fs,
+                     Stages{static_cast<hipEvent_t*>(cfg->stage_events), s}, s);
+}
 
-  const bool given = d.mask_mode == SLA_MASK_GIVEN;
-  // all blocks critical: plain dense attention, no classification, no linear branch
-  const bool dense = !given && d.kc == d.T && !d.global;
-  // (the two-level split can leave marginal blocks even when the flat one has none)
-  const bool linear = d.global || given || ((d.km > 0 || d.G > 0) && d.kc < d.T);
-  uint32_t* bits = d.global ? nullptr : rbits;   // the global branch needs no marginal bits
-
-  if (dense) {
-    SLA_CHECK(launched(launch_fill_mask(d, mask, 1, s), "fill_mask"));
-  } else {
-    if (linear || !given) {
-      SLA_CHECK(stg.begin(SLA_STAGE_KV_STATE));
-      SLA_CHECK(launched(launch_kv_state(d, k16, v16, reinterpret_cast<float*>(ws + wl.kbar), states, s),
-                         "kv_state"));
-      SLA_CHECK(stg.end(SLA_STAGE_KV_STATE));
-    }
-    if (!given) {
-      SLA_CHECK(stg.begin(SLA_STAGE_POOL_Q));
-      SLA_CHECK(launched(launch_pool(d, q16, reinterpret_cast<float*>(ws + wl.qbar), s), "pool_q"));
-      SLA_CHECK(stg.end(SLA_STAGE_POOL_Q));
-      SLA_CHECK(stg.begin(SLA_STAGE_CLASSIFY));
-      if (d.G > 0) {
-        // two-level: group means of K, then coarse and candidate scores inside the classifier
-        auto* kgbar = reinterpret_cast<float*>(ws + wl.kgbar);
-        SLA_CHECK(launched(launch_group_means(d, reinterpret_cast<float*>(ws + wl.kbar), kgbar, s),
-                           "group_means"));
-        SLA_CHECK(launched(launch_classify_hier(d, reinterpret_cast<float*>(ws + wl.qbar), kgbar,
-                                                reinterpret_cast<float*>(ws + wl.kbar), nullptr,
-                                                nullptr, mask, lut, lut_cnt, bits, s),
-                           "classify_hier"));
-      } else {
-        SLA_CHECK(launched(launch_scores(d, reinterpret_cast<float*>(ws + wl.qbar),
-                                         reinterpret_cast<float*>(ws + wl.kbar),
-                                         reinterpret_cast<float*>(ws + wl.scores), s),
-                           "scores"));
-        SLA_CHECK(launched(launch_classify(d, reinterpret_cast<float*>(ws + wl.scores), mask, lut,
-                                           lut_cnt, bits, s),
-                           "classify"));
-      }
-      SLA_CHECK(stg.end(SLA_STAGE_CLASSIFY));
-    } else {
-      SLA_CHECK(stg.begin(SLA_STAGE_CLASSIFY));
-      SLA_CHECK(launched(launch_mask_lists(d, mask, lut, lut_cnt, bits, nullptr, nullptr, nullptr, s),
-                         "mask_lists"));
-      SLA_CHECK(stg.end(SLA_STAGE_CLASSIFY));
-    }
-    if (linear) {
-      SLA_CHECK(stg.begin(SLA_STAGE_AGGREGATE));
-      if (d.global)
-        SLA_CHECK(launched(launch_state_total(d, states, hst, zst, s), "state_total"));
-      else
-        SLA_CHECK(launched(launch_aggregate(d, rbits, states, hst, zst, s), "aggregate"));
-      SLA_CHECK(stg.end(SLA_STAGE_AGGREGATE));
-    }
+sla_status sla_forward_static(const sla_config* cfg, const void* q, const void* k,
+                              const void* v, const void* w, void* o, int8_t* mask, void* saved,
+                              void* stream) {
+  Dims d;
+  SLA_CHECK(make_dims(cfg, &d));
+  SLA_CHECK(check_forward_ptrs(q, k, v, w, o, mask, saved));
+  const long long BH = d.BH();
+  const size_t one = forward_layout(with_problems(d, 1)).total;
+  if (one > SLA_STATIC_SCRATCH_BYTES)
+    return fail(SLA_ERR_WORKSPACE,
+                "one (batch, head) problem needs %zu bytes of scratch, above the %llu of the "
+                "static scratch; use sla_forward with a workspace",
+                one, static_cast<unsigned long long>(SLA_STATIC_SCRATCH_BYTES));
+  // problems per pass: the most whose packed regions fit the array
+  long long per = std::min<long long>(BH, SLA_STATIC_SCRATCH_BYTES / one);
+  while (per > 1 && forward_layout(with_problems(d, static_cast<int>(per))).total >
+                        SLA_STATIC_SCRATCH_BYTES)
+    --per;
+  char* base = nullptr;
+  SLA_CHECK(static_scratch(&base));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const SavedLayout sl = saved_layout(d);
+  char* sv = static_cast<char*>(saved);
+  const size_t N = d.N, D = d.D, T = d.T;
+  for (long long p0 = 0; p0 < BH; p0 += per) {
+    const int n = static_cast<int>(std::min(per, BH - p0));
+    const Dims dc = with_problems(d, n);
+    const FwdLayout fl = forward_layout(dc);
+    const FwdScratch fs{reinterpret_cast<float*>(base + fl.qbar),
+                        reinterpret_cast<float*>(base + fl.kbar),
+                        reinterpret_cast<float*>(base + fl.kgbar),
+                        reinterpret_cast<float*>(base + fl.scores),
+                        reinterpret_cast<int32_t*>(base + fl.lut),
+                        reinterpret_cast<int32_t*>(base + fl.lut_cnt),
+                        reinterpret_cast<uint32_t*>(base + fl.rbits),
+                        reinterpret_cast<uint16_t*>(base + fl.states)};
+    const size_t p = static_cast<size_t>(p0);
+    const FwdOut out{static_cast<uint16_t*>(o) + p * N * D, mask + p * T * T,
+                     reinterpret_cast<float*>(sv + sl.lse) + p * N,
+                     reinterpret_cast<float*>(sv + sl.den) + p * N,
+                     reinterpret_cast<uint16_t*>(sv + sl.y) + p * N * D,
+                     reinterpret_cast<uint16_t*>(sv + sl.hst) + p * T * D * D,
+                     reinterpret_cast<float*>(sv + sl.zst) + p * T * 2 * D};
+    SLA_CHECK(forward_run(dc, static_cast<const uint16_t*>(q) + p * N * D,
+                          static_cast<const uint16_t*>(k) + p * N * D,
+                          static_cast<const uint16_t*>(v) + p * N * D,
+                          static_cast<const uint16_t*>(w), out, fs, Stages{nullptr, s}, s));
   }
-  SLA_CHECK(stg.begin(SLA_STAGE_ATTENTION));
-  SLA_CHECK(launched(launch_attn_fwd(d, q16, k16, v16, static_cast<const uint16_t*>(w), lut, lut_cnt,
-                                     dense, linear, hst, zst, static_cast<uint16_t*>(o),
-                                     reinterpret_cast<float*>(sv + sl.lse),
-                                     reinterpret_cast<float*>(sv + sl.den),
-                                     reinterpret_cast<uint16_t*>(sv + sl.y), s),
-                     "attention"));
-  SLA_CHECK(stg.end(SLA_STAGE_ATTENTION));
   return SLA_OK;
 }
 

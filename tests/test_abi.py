@@ -90,6 +90,29 @@ def test_forward_rejects_bad_pointers_before_any_launch(B):
     assert st == B.SLA_ERR_INVALID_ARGUMENT
 
 
+def test_static_forward_rejects_on_the_host(B):
+    """The allocation-free forward validates like sla_forward and refuses a
+    problem whose one (batch, head) share of scratch exceeds its static array,
+    all before any device call."""
+    buf = ctypes.create_string_buffer(64)
+    good = (ctypes.addressof(buf) + 15) & ~15
+    cfg = B.make_config(1, 2, 256, 64, 0.25, 0.25)
+    st = B.lib.sla_forward_static(ctypes.byref(cfg), good, None, *([good] * 6), None)
+    assert st == B.SLA_ERR_INVALID_ARGUMENT and "k" in B.sla_last_error()
+    st = B.lib.sla_forward_static(ctypes.byref(cfg), *([good] * 6), good + 4, good, None)
+    assert st == B.SLA_ERR_INVALID_ARGUMENT and "aligned" in B.sla_last_error()
+    bad = B.make_config(0, 2, 256, 64, 0.25, 0.25)
+    assert B.lib.sla_forward_static(ctypes.byref(bad), *([good] * 7), None) == \
+        B.SLA_ERR_INVALID_ARGUMENT
+    # T = 1441 blocks at d = 128: one head needs more than the 64 MiB array
+    big = B.make_config(1, 1, 64 * 1441, 128, 0.05, 0.1)
+    st = B.lib.sla_forward_static(ctypes.byref(big), *([good] * 7), None)
+    assert st == B.SLA_ERR_WORKSPACE and "static scratch" in B.sla_last_error()
+    assert B.SLA_STATIC_SCRATCH_BYTES == 64 << 20
+    header = open(os.path.join(ROOT, "include", "sla.h")).read()
+    assert "#define SLA_STATIC_SCRATCH_BYTES (64ull << 20)" in header
+
+
 def test_status_strings_and_sizes(B):
     for s in range(5):
         assert B.sla_status_string(s)
