@@ -9,6 +9,12 @@ Prints one JSON line.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--mode fwd|fwdbwd] [--no-cpu-baseline] [--no-side-runs]
                     [--traffic-probe]
+    python bench.py --trace-summary KERNEL_TRACE_CSV --warmup W --steps K
+
+`ms_per_step` / `value` come from the K timed steps bracketed by
+synchronisations; `step_ms` gives median / min / p90 / mean per step and
+`stages_ms` the median per stage.  The roofline of a kernel uses the median
+of the HIP events around its stage's single launch.
 """
 from __future__ import annotations
 
@@ -28,6 +34,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
+PEAK_CLOCK_MHZ = 2400.0     # engine clock the published MFMA peak is quoted at
 DEFAULT_WORKLOAD = "video_dit_b2_h12_n32768_d128"
 DOMINANT = {"fwd": "attention", "fwdbwd": "bwd_kv"}
 
@@ -48,6 +55,13 @@ def parse():
                          "to calibrate hardware traffic counters")
     ap.add_argument("--dense", action="store_true",
                     help="time the same library as dense attention (all blocks critical)")
+    ap.add_argument("--counter-summary", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "GRBM_CSV"),
+                    help="summarise three rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE, "
+                         "GRBM_COUNT GRBM_GUI_ACTIVE) and write the traffic records under profiles/")
+    ap.add_argument("--trace-summary", metavar="KERNEL_TRACE_CSV",
+                    help="no GPU run: summarise a rocprofv3 kernel trace of a run of this script "
+                         "(--warmup / --steps as in that run): per kernel, the launches of the "
+                         "timed steps only (warm-up launches dropped), median / min / p90 / mean")
     return ap.parse_args()
 
 
@@ -112,6 +126,7 @@ def cpu_baseline(inp, wl, k_c, k_n):
     v = orc.decode_bf16(inp["v"][0, 0])
     w = orc.decode_bf16(inp["w"])
     t = wl.num_blocks
+    cpu0 = time.process_time()
     t0 = time.perf_counter()
     scores = orc.compressed_scores(q, k, wl.valid_len, scale)
     mask = orc.classify(scores, k_c, k_n)
@@ -127,37 +142,161 @@ def cpu_baseline(inp, wl, k_c, k_n):
     orc.backward_head(q, k, v, w, do, mq, wl.valid_len, scale)
     t_bwd = time.perf_counter() - t1
     flops_bwd = 10.0 * 64 * 64 * wl.head_dim * k_c * t
-    tflops = (flops_fwd + flops_bwd) / (t_fwd + t_bwd) / 1e12
+    cpu_s = time.process_time() - cpu0
+    wall_s = t_fwd + t_bwd
+    tflops = (flops_fwd + flops_bwd) / wall_s / 1e12
     try:
         cores = len(os.sched_getaffinity(0))
     except AttributeError:
         cores = os.cpu_count()
-    threads = int(os.environ.get("OMP_NUM_THREADS", cores))
     return {
         "value": tflops,
         "unit": "TFLOP/s (critical-block FLOPs, fp64 oracle)",
-        "cores": min(cores, threads),
+        # threads actually busy: process CPU time over wall time of the sample
+        "cores": round(cpu_s / wall_s, 1),
+        "cores_available": cores,
+        "cpu_model": _cpu_model(),
         "kind": "oracle",
         "sample": (f"head (0,0) of {wl.batch * wl.heads}: scores, classification, states and "
                    f"forward of all {len(blocks)} query blocks ({t_fwd:.1f} s); backward of the "
                    f"same head ({t_bwd:.1f} s)"),
+        "one_thread": _oracle_one_thread(wl, k_c, k_n),
     }
 
 
-def _timed(fn, warmup, steps):
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+_ONE_THREAD_SNIPPET = """
+import sys, time, json
+sys.path.insert(0, {root!r})
+import oracle as orc
+from sparse_linear_attention_mean_amd.inputs import make_workload_inputs
+wl_name, k_c, k_n, nblk = {name!r}, {k_c}, {k_n}, {nblk}
+from sparse_linear_attention_mean_amd.inputs import WORKLOADS
+wl = WORKLOADS[wl_name]
+inp = make_workload_inputs(wl_name, seed=0, with_grad=False)
+scale = orc.default_scale(wl.head_dim)
+q, k, v = (orc.decode_bf16(inp[x][0, 0]) for x in ("q", "k", "v"))
+w = orc.decode_bf16(inp["w"])
+t0 = time.perf_counter()
+mask = orc.classify(orc.compressed_scores(q, k, wl.valid_len, scale), k_c, k_n)
+orc.forward_head(q, k, v, w, mask, wl.valid_len, scale, blocks=list(range(nblk)))
+print(json.dumps({{"s": time.perf_counter() - t0}}))
+"""
+
+
+def _oracle_one_thread(wl, k_c, k_n, nblk=64):
+    """The oracle forward of the first nblk query blocks of head (0, 0) (plus
+    the scores and classification of the head) in a child process whose BLAS
+    and OpenMP pools are limited to one thread."""
+    import subprocess
+
+    env = dict(os.environ)
+    for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS", "BLIS_NUM_THREADS"):
+        env[var] = "1"
+    code = _ONE_THREAD_SNIPPET.format(root=ROOT, name=wl.name, k_c=k_c, k_n=k_n, nblk=nblk)
+    try:
+        res = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
+                             timeout=600)
+        sec = json.loads(res.stdout.strip().splitlines()[-1])["s"]
+    except Exception as exc:   # reported, not fatal: the baseline is context
+        return {"error": str(exc)[:200]}
+    flops = 4.0 * 64 * 64 * wl.head_dim * k_c * nblk
+    return {"value": flops / sec / 1e12, "unit": "TFLOP/s (critical-block FLOPs, fp64 oracle)",
+            "cores": 1, "seconds": round(sec, 2),
+            "sample": f"scores and classification of head (0,0), forward of its first {nblk} "
+                      f"query blocks, one thread"}
+
+
+def _timed(fn, warmup, steps, per_step=False):
+    """Mean ms per call over `steps` calls after `warmup` (one event pair
+    around all of them); with per_step, also the list of per-call times from
+    an event at every call boundary."""
     import torch
 
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    a = torch.cuda.Event(enable_timing=True)
-    b = torch.cuda.Event(enable_timing=True)
-    a.record()
-    for _ in range(steps):
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    evs[0].record()
+    for i in range(steps):
         fn()
-    b.record()
+        evs[i + 1].record()
     torch.cuda.synchronize()
-    return a.elapsed_time(b) / steps
+    mean = evs[0].elapsed_time(evs[-1]) / steps
+    if per_step:
+        return mean, [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
+    return mean
+
+
+def sustained_clock(step, max_s=4.0):
+    """GFX (shader) clock while ``step`` runs back to back.
+
+    amdsmi's GPU metrics table holds per-XCD clocks averaged over a window and
+    is refreshed about once a second (its ``system_clock_counter`` moves on at
+    each refresh), far longer than the timed steps.  So the step is repeated,
+    untimed, until two refreshes whose whole window lies inside the repeated
+    run have been read (the first refresh after the start also covers the idle
+    time before it).  None where amdsmi is unavailable."""
+    import torch
+
+    try:
+        import amdsmi
+
+        amdsmi.amdsmi_init()
+        h = amdsmi.amdsmi_get_processor_handles()[0]
+    except Exception as exc:
+        return {"gfx_mhz": None, "error": str(exc)[:200]}
+
+    def read():
+        m = amdsmi.amdsmi_get_gpu_metrics_info(h)
+        clks = m.get("current_gfxclks")
+        vals = [float(c) for c in clks if isinstance(c, (int, float)) and 0 < c < 0xFFFF] \
+            if isinstance(clks, (list, tuple)) else []
+        return m.get("system_clock_counter"), vals, m.get("current_socket_power")
+
+    try:
+        prev, _, _ = read()
+        refreshes, windows = 0, []
+        t0 = time.time()
+        while time.time() - t0 < max_s and len(windows) < 2:
+            for _ in range(10):
+                step()
+            torch.cuda.synchronize()
+            cnt, vals, power = read()
+            if cnt != prev:
+                refreshes += 1
+                prev = cnt
+                if refreshes >= 2 and vals:
+                    windows.append((vals, power))
+    except Exception as exc:
+        return {"gfx_mhz": None, "error": str(exc)[:200]}
+    finally:
+        try:
+            amdsmi.amdsmi_shut_down()
+        except Exception:
+            pass
+    if not windows:
+        return {"gfx_mhz": None, "error": "no metrics refresh inside the repeated run"}
+    means = [sum(v) / len(v) for v, _ in windows]
+    return {
+        "gfx_mhz": round(sum(means) / len(means), 1),
+        "gfx_mhz_per_xcd": windows[-1][0],
+        "socket_power_w": windows[-1][1],
+        "windows": len(windows),
+        "source": "amdsmi GPU metrics, current GFX clock averaged over the XCDs, from "
+                  "about-1-s refresh windows lying wholly inside an untimed run of the "
+                  "same step back to back after the timed steps",
+    }
 
 
 def linear_branch_rate(wl, inp, q, k, v, w, dev):
@@ -205,10 +344,18 @@ def dense_ratio(wl, q, k, v, w, do, dev, with_bwd, sla_ms):
         if with_bwd:
             prob.backward(q, k, v, w, o, do, mask, grads=grads)
 
-    ms = _timed(step, 1, 2)
-    return {"dense_ms_per_step": round(ms, 3), "sla_ms_per_step": round(sla_ms, 4),
-            "speedup": round(ms / sla_ms, 2),
-            "note": "frac_critical = 1, frac_negligible = 0 through the same entry points"}
+    mean, per = _timed(step, 2, 5, per_step=True)
+    st = step_stats(per)
+    t = wl.num_blocks
+    bh = wl.batch * wl.heads
+    dense_flops = (4.0 + (10.0 if with_bwd else 0.0)) * 64 * 64 * wl.head_dim * bh * t * t
+    tf = dense_flops / (st["median"] * 1e-3) / 1e12
+    return {"dense_ms_per_step": st["median"], "dense_step_ms": st, "sla_ms_per_step": round(sla_ms, 4),
+            "speedup": round(st["median"] / sla_ms, 2),
+            "dense_tflops": round(tf, 1), "dense_frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            "note": "frac_critical = 1, frac_negligible = 0 through the same entry points; "
+                    "median of 5 steps after 2 warm-up steps; speedup = dense median / SLA "
+                    "median step time"}
 
 
 def mask_reuse_rate(wl, q, k, v, w, dev, mask):
@@ -307,8 +454,176 @@ def two_level_selection(dev, hip, group=8, keep=8, steps=5):
     return out
 
 
+def _percentile(sorted_vals, q):
+    """Nearest-rank percentile of an ascending list."""
+    if not sorted_vals:
+        return None
+    k = max(0, min(len(sorted_vals) - 1, math.ceil(q / 100.0 * len(sorted_vals)) - 1))
+    return sorted_vals[k]
+
+
+def step_stats(ms_list):
+    """median / min / p90 / mean of per-step (or per-launch) times, ms."""
+    v = sorted(x for x in ms_list if x is not None)
+    if not v:
+        return None
+    return {"median": round(_percentile(v, 50), 4), "min": round(v[0], 4),
+            "p90": round(_percentile(v, 90), 4), "mean": round(sum(v) / len(v), 4), "n": len(v)}
+
+
+def trace_summary(path, warmup, steps):
+    """Per-kernel launch durations of a rocprofv3 --kernel-trace CSV of one run
+    of this script.  Every kernel of the hot path is launched the same number
+    of times per step, in step order, so the first warmup / (warmup + steps)
+    of each kernel's launches are the warm-up steps and are dropped."""
+    import csv
+
+    by_name = {}
+    with open(path, newline="") as f:
+        for rec in csv.DictReader(f):
+            name = rec.get("Kernel_Name") or rec.get("KernelName") or rec.get("Name")
+            t0 = int(rec.get("Start_Timestamp") or rec.get("BeginNs"))
+            t1 = int(rec.get("End_Timestamp") or rec.get("EndNs"))
+            by_name.setdefault(name, []).append((t0, (t1 - t0) / 1000.0))
+    rows = []
+    for name, launches in by_name.items():
+        launches.sort()
+        total = len(launches)
+        per_step = total / float(warmup + steps)
+        skip = int(round(warmup * per_step)) if per_step.is_integer() else 0
+        us = sorted(d for _, d in launches[skip:])
+        rows.append((sum(us), name, total, len(us), _percentile(us, 50), us[0],
+                     _percentile(us, 90), sum(us) / len(us)))
+    rows.sort(reverse=True)
+    busy = sum(r[0] for r in rows)
+    out = ["| kernel | launches | timed | median µs | min µs | p90 µs | mean µs | % of timed GPU time |",
+           "|---|---:|---:|---:|---:|---:|---:|---:|"]
+    for tot, name, total, n, med, mn, p90, mean in rows:
+        out.append(f"| `{name}` | {total} | {n} | {med:.1f} | {mn:.1f} | {p90:.1f} | {mean:.1f} | "
+                   f"{100.0 * tot / busy:.1f} |")
+    out.append("")
+    out.append(f"Kernel time over the timed steps: {busy / 1000.0 / steps:.3f} ms per step "
+               f"({steps} steps, {warmup} warm-up steps dropped).")
+    return "\n".join(out)
+
+
+# kernels whose roofline reports traffic: tag -> (kernel name stem, sources)
+TRAFFIC_KERNELS = {
+    "attn_fwd": ("attn_fwd_kernel", ["attn_fwd.hip", "sla_device.h"]),
+    "bwd_kv": ("bwd_kv_kernel", ["bwd.hip", "sla_device.h"]),
+}
+COUNTER_COMMAND = ("rocprofv3 --pmc {c} --output-format csv -d gpurun_out/pmc/{t} -o {t} -- "
+                   "python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline --no-side-runs "
+                   "--traffic-probe")
+
+
+def _counter_rows(path):
+    """(dispatch id, kernel name, value) of a rocprofv3 --pmc CSV with one counter."""
+    import csv
+
+    out = []
+    with open(path, newline="") as f:
+        for rec in csv.DictReader(f):
+            out.append((int(rec["Dispatch_Id"]), rec["Kernel_Name"], float(rec["Counter_Value"]),
+                        int(rec["End_Timestamp"]) - int(rec["Start_Timestamp"])))
+    out.sort()
+    return out
+
+
+def counter_summary(fetch_csv, write_csv, grbm_csv, workload, xcc=8, write_json=True):
+    """HBM traffic and engine clock per kernel from three rocprofv3 --pmc runs
+    of ``bench.py --steps 1 --warmup 1 --traffic-probe`` (FETCH_SIZE;
+    WRITE_SIZE; GRBM_COUNT with GRBM_GUI_ACTIVE).
+
+    The run ends with one device copy of 256 MiB (the last dispatch); what the
+    counters read for it against the bytes it moves gives the scale factor of
+    each counter.  GRBM_COUNT counts engine clocks summed over the ``xcc``
+    XCDs; per XCD over the dispatch's duration it gives the clock (biased high
+    for short kernels, whose counting window is longer than the kernel).
+    Writes profiles/traffic_<tag>_<workload>.json for the kernels in
+    TRAFFIC_KERNELS, stamped with the digest of their current sources, and
+    returns the markdown table."""
+    fetch, write = _counter_rows(fetch_csv), _counter_rows(write_csv)
+    grbm = _counter_rows(grbm_csv) if grbm_csv else []
+    probe_bytes = 256 << 20
+    f_probe, w_probe = fetch[-1], write[-1]
+    f_fac = f_probe[2] * 1024.0 / probe_bytes
+    w_fac = w_probe[2] * 1024.0 / probe_bytes
+
+    def per_kernel(rows):
+        d = {}
+        for _, name, val, dur in rows[:-1]:
+            if "sla::" in name:          # the library's kernels, not the probe's fill
+                d.setdefault(name, []).append((val, dur))
+        return d
+
+    fk, wk = per_kernel(fetch), per_kernel(write)
+    gk = {}
+    for _, name, val, dur in grbm:
+        gk.setdefault(name, []).append((val, dur))
+    lines = [
+        f"Calibration: the copy at the end of each run moves 262144 KiB each way; FETCH_SIZE reads "
+        f"{f_probe[2]:.0f} KiB for it (factor {f_fac:.4f}), WRITE_SIZE {w_probe[2]:.0f} KiB "
+        f"(factor {w_fac:.4f}).  Bytes below are counter / factor, mean per launch.",
+        "",
+        "| kernel | launches | read MB | written MB | engine cycles per XCD (M) | duration under counters µs | implied clock MHz |",
+        "|---|---:|---:|---:|---:|---:|---:|",
+    ]
+    summary = {}
+    for name, vals in fk.items():
+        n = len(vals)
+        rd = sum(v for v, _ in vals) / n * 1024.0 / f_fac
+        wr = sum(v for v, _ in wk.get(name, [(0.0, 0)])) / max(1, len(wk.get(name, []))) * 1024.0 / w_fac
+        g = [x for x in gk.get(name, []) if x[1] > 0]
+        # GRBM_COUNT and GRBM_GUI_ACTIVE rows alternate per dispatch: keep one
+        # value per dispatch (they agree for a kernel that keeps the GPU busy)
+        g = g[::2] if len(g) == 2 * n else g
+        cyc = sum(v for v, _ in g) / len(g) / xcc if g else None
+        dur = sum(du for _, du in g) / len(g) / 1000.0 if g else None
+        mhz = cyc / dur if cyc and dur else None
+        stem = name.replace("void ", "").split("(")[0]
+        summary[stem] = {"read_bytes": rd, "written_bytes": wr, "cycles_per_xcd": cyc,
+                         "duration_us": dur, "mhz": mhz, "launches": n,
+                         "fetch_kib": sum(v for v, _ in vals) / n,
+                         "write_kib": sum(v for v, _ in wk.get(name, [(0.0, 0)])) / max(1, len(wk.get(name, [])))}
+        show_clk = mhz is not None and dur >= 100.0
+        lines.append(f"| `{stem}` | {n} | {rd / 1e6:.1f} | {wr / 1e6:.1f} | "
+                     f"{(cyc / 1e6) if cyc else float('nan'):.3f} | {dur if dur else float('nan'):.1f} | "
+                     f"{(f'{mhz:.0f}' if show_clk else '(short)')} |")
+    if write_json:
+        for tag, (kname, sources) in TRAFFIC_KERNELS.items():
+            hit = [v for k, v in summary.items() if kname in k]
+            if not hit:
+                continue
+            r = hit[0]
+            rec = {
+                "kernel": kname, "workload": workload,
+                "source_digest": kernel_sources_digest(sources), "sources": sources,
+                "fetch_kib_per_launch": round(r["fetch_kib"], 1),
+                "write_kib_per_launch": round(r["write_kib"], 1),
+                "copy_probe": {"bytes_read": probe_bytes, "bytes_written": probe_bytes,
+                               "fetch_kib": f_probe[2], "write_kib": w_probe[2]},
+                "fetch_factor": round(f_fac, 4), "write_factor": round(w_fac, 4),
+                "hbm_bytes_per_launch": int(round(r["read_bytes"] + r["written_bytes"])),
+                "engine_cycles_per_xcd": round(r["cycles_per_xcd"]) if r["cycles_per_xcd"] else None,
+                "clock_mhz_under_counters": round(r["mhz"], 1) if r["mhz"] else None,
+                "commands": [COUNTER_COMMAND.format(c=c, t=c.replace(" ", "_"))
+                             for c in ("FETCH_SIZE", "WRITE_SIZE", "GRBM_COUNT GRBM_GUI_ACTIVE")],
+            }
+            with open(os.path.join(ROOT, "profiles", f"traffic_{tag}_{workload}.json"), "w") as f:
+                json.dump(rec, f, indent=1)
+                f.write("\n")
+    return "\n".join(lines)
+
+
 def main():
     args = parse()
+    if args.trace_summary:
+        print(trace_summary(args.trace_summary, args.warmup, args.steps))
+        return
+    if args.counter_summary:
+        print(counter_summary(*args.counter_summary, workload=args.workload))
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "the library runs on one GPU; it has no multi-GPU path, "
                                    "so --gpus must be 1",
@@ -352,23 +667,28 @@ def main():
     for _ in range(args.warmup):
         step(warm_ev)
     torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
-    start.record()
+    # timed region: one event at every step boundary (the library runs on
+    # torch's current stream), the whole region bracketed by synchronisations
+    bounds = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    bounds[0].record()
     for s in range(args.steps):
         step(ev_sets[s])
-    stop.record()
+        bounds[s + 1].record()
     torch.cuda.synchronize()
-    ms = start.elapsed_time(stop) / args.steps
+    ms = bounds[0].elapsed_time(bounds[-1]) / args.steps
+    step_ms = step_stats([bounds[s].elapsed_time(bounds[s + 1]) for s in range(args.steps)])
 
-    stage_ms = {}
+    # per stage: the median over the timed steps (each stage's events bracket
+    # its launches on the stream); min / p90 / mean alongside
+    stage_ms, stage_stats = {}, {}
     for si, name in enumerate(B.STAGES):
         if not with_bwd and si >= 5:   # backward stages are not recorded in forward-only runs
             continue
         vals = [hip.elapsed_ms(ev_sets[s][2 * si], ev_sets[s][2 * si + 1]) for s in range(args.steps)]
-        vals = [x for x in vals if x is not None]
-        if vals:
-            stage_ms[name] = sum(vals) / len(vals)
+        st = step_stats(vals)
+        if st:
+            stage_ms[name] = st["median"]
+            stage_stats[name] = st
 
     bh = wl.batch * wl.heads
     t = wl.num_blocks
@@ -401,7 +721,19 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(ach / PEAK_BF16_TFLOPS, 4) if ach else None,
             "traffic": traffic_from_profile(tag, wl.name, kernel_sources_digest(sources)),
+            "frac_of_peak_at_measured_clock": (round(ach / (PEAK_BF16_TFLOPS * mhz / PEAK_CLOCK_MHZ), 4)
+                                               if ach and mhz else None),
+            "flop_per_launch": flops_k,
+            "launch_ms": round(kms, 4) if kms else None,
+            "time_basis": "median over the timed steps of the HIP events around the stage's "
+                          "single launch (the kernel's median duration in a rocprofv3 kernel "
+                          "trace of the same command is the check)",
         }
+
+    # shader clock under this load: the published peaks assume 2.4 GHz
+    clock = (sustained_clock(lambda: step(warm_ev)) if not args.no_side_runs
+             else {"gfx_mhz": None, "skipped": "--no-side-runs"})
+    mhz = clock.get("gfx_mhz")
 
     rl_fwd = roofline("attention", flops_fwd_crit + lin_blk,
                       "attn_fwd_kernel (fused sparse + linear + projection)", "attn_fwd",
@@ -432,7 +764,10 @@ def main():
         },
         "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "tflops_dense_equivalent": round(dense_flops / (ms * 1e-3) / 1e12, 1),
+        "step_ms": step_ms,
         "stages_ms": {kk: round(vv, 4) for kk, vv in stage_ms.items()},
+        "stages_ms_stats": stage_stats,
+        "clock": clock,
         "roofline": rl_kv if DOMINANT[args.mode] == "bwd_kv" else rl_fwd,
     }
     if DOMINANT[args.mode] == "bwd_kv":
@@ -446,7 +781,7 @@ def main():
             rec["bwd_tflops"] = round(flops_bwd_crit / (bwd_ms * 1e-3) / 1e12, 2)
     if not args.no_side_runs and not args.dense:
         rec["linear_branch"] = linear_branch_rate(wl, inp, q, k, v, w, dev)
-        rec["vs_dense"] = dense_ratio(wl, q, k, v, w, do, dev, with_bwd, ms)
+        rec["vs_dense"] = dense_ratio(wl, q, k, v, w, do, dev, with_bwd, step_ms["median"])
         rec["mask_reuse"] = mask_reuse_rate(wl, q, k, v, w, dev, mask)
         rec["global_linear"] = global_linear_rate(wl, q, k, v, w, do, dev, with_bwd)
         rec["two_level_selection"] = two_level_selection(dev, hip)

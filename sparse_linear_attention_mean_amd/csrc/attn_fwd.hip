@@ -120,6 +120,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs args) {
   auto copy_v = [&](int n, uint16_t* dst) __attribute__((always_inline)) {
     copy_swz_buf<D, 4>(vrs, block_at(n) * kBlock, dst, wave, lane);
   };
+  // in the loop, each copy instruction takes a per-lane constant offset and a
+  // resource that starts at the block's first row
+  uint32_t cvoff[D / 32];
+#pragma unroll
+  for (int u = 0; u < D / 32; ++u) cvoff[u] = swz_copy_voff<D, 4>(wave, lane, u);
   // H_i^T (swizzled, rows 0..63 into kb0 and 64..127 into kb1) and Z_i, once
   // the K buffers are no longer read
   float* zsw = extra;   // 2 D floats
@@ -171,15 +176,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs args) {
         if (key >= L) st[e] = -INFINITY;
       }
     }
-    float mraw = fmaxf(st[0], st[1]);
-#pragma unroll
-    for (int e = 2; e < 16; e += 2) mraw = fmaxf(mraw, fmaxf(st[e], st[e + 1]));
+    float mraw = max16(st);
     {
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mraw), __float_as_uint(mraw),
                                                        false, false);
-      mraw = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));   // max over both lane halves
+      mraw = fmax_p(__uint_as_float(sw[0]), __uint_as_float(sw[1]));   // max over both lane halves
     }
-    const float m_new = fmaxf(m_run, mraw * sl2);
+    const float m_new = fmax_p(m_run, mraw * sl2);
     const bool need = m_new > m_run + 8.0f;
     if (__any(need)) {
       const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
@@ -229,11 +232,13 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs args) {
     }
     const bool kmore = n + 1 < cnt;
     const int jk = kmore ? block_at(n + 1) : 0;
+    const __amdgpu_buffer_rsrc_t kr = rows_rsrc<D>(args.k + head, jk * kBlock, L);
+    const __amdgpu_buffer_rsrc_t vr = rows_rsrc<D>(args.v + head, jv * kBlock, L);
     const f32x16 sn = s_tile(kc, [&](int cc) __attribute__((always_inline)) {
       if (cc < D / 32) {
-        if (kmore) copy_swz_buf_one<D, 4>(krs, jk * kBlock, kn, wave, lane, cc);
+        if (kmore) copy_swz_rows_one<D, 4>(kr, cvoff[cc], kn, wave, cc);
       } else {
-        copy_swz_buf_one<D, 4>(vrs, jv * kBlock, vn, wave, lane, cc - D / 32);
+        copy_swz_rows_one<D, 4>(vr, cvoff[cc - D / 32], vn, wave, cc - D / 32);
       }
     });
     soft_pv(sp, vp, false);

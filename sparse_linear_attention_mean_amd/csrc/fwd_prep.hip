@@ -315,8 +315,6 @@ __global__ __launch_bounds__(256) void scores_kernel(const float* __restrict__ q
 // optionally the ascending critical list and the marginal bit row.  Rows i
 // in [T, Tp) only clear their bit row.
 // ---------------------------------------------------------------------------
-constexpr int kMaxT = 2048;
-
 __device__ __forceinline__ uint32_t descending_code(float s) {
   uint32_t u = __float_as_uint(s + 0.0f);   // -0 -> +0
   const uint32_t asc = (u & 0x80000000u) ? ~u : (u | 0x80000000u);

@@ -29,6 +29,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kBlock = 64;
+constexpr int kMaxT = 2048;   // most 64-token blocks per sequence (N <= 131072)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -242,6 +243,44 @@ __device__ __forceinline__ void copy_swz_buf_one(__amdgpu_buffer_rsrc_t rs, int 
   const int voff = ((row0 + r) * D + 8 * (sl ^ swz<D>(r))) * 2;
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + it * 512),
                                            16, voff, 0, 0, 0);
+}
+// Buffer resource over rows [row0, L) of a row-major bf16 matrix with D
+// columns: copies through it read the padded rows at or past L as zero, and
+// the row offset lives in the resource (scalar) instead of every lane's
+// offset.
+template <int D>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t* base, int row0, int L) {
+  return make_rsrc(base + static_cast<size_t>(row0) * D,
+                   static_cast<uint32_t>(L > row0 ? L - row0 : 0) * D * 2);
+}
+// Byte offset, within a 64-row tile, of this lane's 16 bytes in the u-th of
+// the kCopies / NW copy instructions of wave w (the copy_swz_buf split); a
+// per-lane constant.
+template <int D, int NW>
+__device__ __forceinline__ uint32_t swz_copy_voff(int w, int lane, int u) {
+  const int it = w + NW * u;
+  const int p = it * 64 + lane;
+  const int r = p / (D / 8), sl = p % (D / 8);
+  return static_cast<uint32_t>((r * D + 8 * (sl ^ swz<D>(r))) * 2);
+}
+// Copy instruction u of wave w into the swizzled LDS tile dst, from the
+// rows of rs (built by rows_rsrc), with the lane offset voff from swz_copy_voff.
+template <int D, int NW>
+__device__ __forceinline__ void copy_swz_rows_one(__amdgpu_buffer_rsrc_t rs, uint32_t voff,
+                                                  uint16_t* dst, int w, int u) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + (w + NW * u) * 512),
+                                           16, voff, 0, 0, 0);
+}
+
+// NaN-propagating maximum (IEEE 754-2019 maximum): v_maximum3_f32 on gfx950,
+// with no canonicalisation of the inputs (fmaxf adds one per input)
+__device__ __forceinline__ float fmax_p(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+// maximum of the 16 elements of a result tile, three at a time
+__device__ __forceinline__ float max16(const f32x16& v) {
+  float m = fmax_p(fmax_p(v[0], v[1]), v[2]);
+#pragma unroll
+  for (int e = 3; e < 15; e += 2) m = fmax_p(fmax_p(m, v[e]), v[e + 1]);
+  return fmax_p(m, v[15]);
 }
 // four consecutive rows of one column: lane gets M[kb + 4 (l/32) + s][n0 + l%32], s < 4
 template <int D>

@@ -42,3 +42,71 @@ def test_traffic_only_for_the_profiled_sources(tmp_path, monkeypatch):
     assert b.traffic_from_profile("k", "wl", "abc123") == 12345
     assert b.traffic_from_profile("k", "wl", "stale") is None          # kernel changed since
     assert b.traffic_from_profile("other", "wl", "abc123") is None     # never profiled
+
+
+def test_step_stats_nearest_rank():
+    b = _bench()
+    st = b.step_stats([5.0, 1.0, 3.0, 2.0, 4.0, None])
+    assert st == {"median": 3.0, "min": 1.0, "p90": 5.0, "mean": 3.0, "n": 5}
+    assert b.step_stats([None]) is None
+    assert b.step_stats(list(map(float, range(1, 21))))["p90"] == 18.0
+
+
+def test_trace_summary_drops_warmup_launches(tmp_path):
+    """Every kernel runs the same number of times per step: the first
+    warmup / (warmup + steps) of each kernel's launches (by start time) are
+    dropped, whatever order the trace lists them in."""
+    b = _bench()
+    rows = ['"Kind","Kernel_Name","Start_Timestamp","End_Timestamp"']
+    # kernel a: once per step, warm-up launch 100 us, timed 10, 20 us
+    for t0, dur in ((0, 100_000), (1_000_000, 10_000), (2_000_000, 20_000)):
+        rows.append(f'"KERNEL_DISPATCH","a",{t0},{t0 + dur}')
+    # kernel b: twice per step, listed out of order
+    for t0, dur in ((2_500_000, 3_000), (500, 90_000), (1_500_000, 1_000), (600, 80_000),
+                    (1_600_000, 2_000), (2_600_000, 4_000)):
+        rows.append(f'"KERNEL_DISPATCH","b",{t0},{t0 + dur}')
+    path = tmp_path / "trace.csv"
+    path.write_text("\n".join(rows) + "\n")
+    out = b.trace_summary(str(path), warmup=1, steps=2)
+    line_a = next(ln for ln in out.splitlines() if "`a`" in ln)
+    line_b = next(ln for ln in out.splitlines() if "`b`" in ln)
+    # a: timed 10 and 20 us -> nearest-rank median 10, min 10, p90 20, mean 15
+    assert "| 3 | 2 | 10.0 | 10.0 | 20.0 | 15.0 |" in line_a
+    # b: the two warm-up launches (90 and 80 us) dropped; timed 1, 2, 3, 4 us
+    assert "| 6 | 4 | 2.0 | 1.0 | 4.0 | 2.5 |" in line_b
+    assert "(2 steps, 1 warm-up steps dropped)" in out
+
+
+def test_counter_summary_scales_by_the_copy_probe(tmp_path, monkeypatch):
+    """Counter values are divided by what the same counter reads for the
+    closing 256 MiB copy; engine cycles are per XCD over the duration."""
+    b = _bench()
+    hdr = '"Dispatch_Id","Kernel_Name","Counter_Name","Counter_Value","Start_Timestamp","End_Timestamp"'
+
+    def write(name, rows):
+        p = tmp_path / name
+        p.write_text("\n".join([hdr] + [",".join(map(str, r)) for r in rows]) + "\n")
+        return str(p)
+
+    k = '"void sla::bwd_kv_kernel<128>(int)"'
+    fetch = write("f.csv", [(1, k, '"FETCH_SIZE"', 1000.0, 0, 1_000_000),
+                            (2, k, '"FETCH_SIZE"', 3000.0, 0, 1_000_000),
+                            (3, '"__amd_rocclr_copyBuffer"', '"FETCH_SIZE"', 131072.0, 0, 100)])
+    wr = write("w.csv", [(1, k, '"WRITE_SIZE"', 500.0, 0, 1_000_000),
+                         (2, k, '"WRITE_SIZE"', 500.0, 0, 1_000_000),
+                         (3, '"__amd_rocclr_copyBuffer"', '"WRITE_SIZE"', 262144.0, 0, 100)])
+    # 8 XCDs x 2.0e6 cycles in 1 ms -> 2000 MHz
+    gr = write("g.csv", [(1, k, '"GRBM_COUNT"', 16e6, 0, 1_000_000),
+                         (1, k, '"GRBM_GUI_ACTIVE"', 16e6, 0, 1_000_000),
+                         (2, k, '"GRBM_COUNT"', 16e6, 0, 1_000_000),
+                         (2, k, '"GRBM_GUI_ACTIVE"', 16e6, 0, 1_000_000)])
+    (tmp_path / "profiles").mkdir()
+    monkeypatch.setattr(b, "ROOT", str(tmp_path))
+    monkeypatch.setattr(b, "kernel_sources_digest", lambda names: "d1")
+    out = b.counter_summary(fetch, wr, gr, "wl")
+    rec = json.loads((tmp_path / "profiles" / "traffic_bwd_kv_wl.json").read_text())
+    assert rec["fetch_factor"] == 0.5 and rec["write_factor"] == 1.0
+    # mean fetch 2000 KiB / 0.5 + write 500 KiB / 1.0
+    assert rec["hbm_bytes_per_launch"] == (4000 + 500) * 1024
+    assert rec["clock_mhz_under_counters"] == 2000.0 and rec["source_digest"] == "d1"
+    assert "| `sla::bwd_kv_kernel<128>` | 2 |" in out
