@@ -10,11 +10,18 @@ Prints one JSON line.
                     [--mode fwd|fwdbwd] [--no-cpu-baseline] [--no-side-runs]
                     [--traffic-probe]
     python bench.py --trace-summary KERNEL_TRACE_CSV --warmup W --steps K
+    python bench.py --counter-summary FETCH_CSV WRITE_CSV GRBM_CSV
 
 `ms_per_step` / `value` come from the K timed steps bracketed by
 synchronisations; `step_ms` gives median / min / p90 / mean per step and
 `stages_ms` the median per stage.  The roofline of a kernel uses the median
-of the HIP events around its stage's single launch.
+of the HIP events around its stage's single launch; `clock` is the engine
+clock while the step repeats (amdsmi), and the roofline also states the
+fraction of the peak rescaled to it.  --trace-summary turns a rocprofv3
+kernel trace of this script into per-kernel median / min / p90 with the
+warm-up launches dropped; --counter-summary turns three rocprofv3 --pmc runs
+into HBM bytes and engine clock per kernel and writes the traffic records
+under profiles/.
 """
 from __future__ import annotations
 
@@ -238,7 +245,7 @@ def _timed(fn, warmup, steps, per_step=False):
     return mean
 
 
-def sustained_clock(step, max_s=4.0):
+def sustained_clock(step, max_s=4.0, sync=None):
     """GFX (shader) clock while ``step`` runs back to back.
 
     amdsmi's GPU metrics table holds per-XCD clocks averaged over a window and
@@ -246,9 +253,12 @@ def sustained_clock(step, max_s=4.0):
     each refresh), far longer than the timed steps.  So the step is repeated,
     untimed, until two refreshes whose whole window lies inside the repeated
     run have been read (the first refresh after the start also covers the idle
-    time before it).  None where amdsmi is unavailable."""
-    import torch
+    time before it).  None where amdsmi is unavailable.  ``sync`` waits for
+    the queued steps (torch.cuda.synchronize by default)."""
+    if sync is None:
+        import torch
 
+        sync = torch.cuda.synchronize
     try:
         import amdsmi
 
@@ -271,7 +281,7 @@ def sustained_clock(step, max_s=4.0):
         while time.time() - t0 < max_s and len(windows) < 2:
             for _ in range(10):
                 step()
-            torch.cuda.synchronize()
+            sync()
             cnt, vals, power = read()
             if cnt != prev:
                 refreshes += 1

@@ -110,3 +110,43 @@ def test_counter_summary_scales_by_the_copy_probe(tmp_path, monkeypatch):
     assert rec["hbm_bytes_per_launch"] == (4000 + 500) * 1024
     assert rec["clock_mhz_under_counters"] == 2000.0 and rec["source_digest"] == "d1"
     assert "| `sla::bwd_kv_kernel<128>` | 2 |" in out
+
+
+def test_sustained_clock_skips_the_first_refresh(monkeypatch):
+    """The metrics table refreshes about once a second; the first refresh
+    after the start also covers idle time, so only later windows count."""
+    import sys
+    import types
+
+    b = _bench()
+    # refresh counter moves on every third read; clocks per window
+    state = {"reads": 0}
+    windows = [[100, 100], [2000, 2200], [2100, 2300], [2150, 2250]]
+
+    def metrics(_h):
+        state["reads"] += 1
+        w = min(state["reads"] // 3, len(windows) - 1)
+        return {"system_clock_counter": w, "current_gfxclks": windows[w] + [0xFFFF],
+                "current_socket_power": 1000 + w}
+
+    fake = types.SimpleNamespace(
+        amdsmi_init=lambda: None, amdsmi_shut_down=lambda: None,
+        amdsmi_get_processor_handles=lambda: ["gpu0"],
+        amdsmi_get_gpu_metrics_info=metrics)
+    monkeypatch.setitem(sys.modules, "amdsmi", fake)
+    steps = []
+    rec = b.sustained_clock(lambda: steps.append(1), max_s=5.0, sync=lambda: None)
+    # windows 2 and 3 (the first refresh, window 1, is skipped; 0xFFFF entries ignored)
+    assert rec["windows"] == 2
+    assert rec["gfx_mhz"] == round(((2100 + 2300) / 2 + (2150 + 2250) / 2) / 2, 1)
+    assert rec["gfx_mhz_per_xcd"] == [2150.0, 2250.0] and rec["socket_power_w"] == 1003
+    assert steps   # the step ran while the clock was read
+
+
+def test_sustained_clock_without_amdsmi(monkeypatch):
+    import sys
+
+    b = _bench()
+    monkeypatch.setitem(sys.modules, "amdsmi", None)   # import fails
+    rec = b.sustained_clock(lambda: None, sync=lambda: None)
+    assert rec["gfx_mhz"] is None and "error" in rec
