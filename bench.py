@@ -62,6 +62,10 @@ def parse():
                          "to calibrate hardware traffic counters")
     ap.add_argument("--dense", action="store_true",
                     help="time the same library as dense attention (all blocks critical)")
+    ap.add_argument("--sq-summary", nargs=2, metavar=("PASS_A_CSV", "PASS_B_CSV"),
+                    help="summarise two rocprofv3 --pmc runs of the SQ_PASSES counters")
+    ap.add_argument("--pairs", type=int, default=319488,
+                    help="critical pairs per launch for --sq-summary (default: the bench workload)")
     ap.add_argument("--counter-summary", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "GRBM_CSV"),
                     help="summarise three rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE, "
                          "GRBM_COUNT GRBM_GUI_ACTIVE) and write the traffic records under profiles/")
@@ -626,10 +630,61 @@ def counter_summary(fetch_csv, write_csv, grbm_csv, workload, xcc=8, write_json=
     return "\n".join(lines)
 
 
+SQ_PASSES = (
+    "SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_ACTIVE_INST_VALU "
+    "SQ_ACTIVE_INST_LDS SQ_VALU_MFMA_BUSY_CYCLES SQ_LDS_BANK_CONFLICT",
+    "SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_WAIT_INST_LDS SQ_ACTIVE_INST_ANY "
+    "SQ_INSTS_SALU SQ_ACTIVE_INST_MISC SQ_INSTS_VMEM",
+)
+
+
+def sq_summary(csv_a, csv_b, pairs, simds=1024, engines=32):
+    """Per kernel, from two rocprofv3 --pmc runs with the SQ_PASSES counters:
+    the matrix-core busy fraction per SIMD (SQ_VALU_MFMA_BUSY_CYCLES over
+    ``simds`` SIMDs x the kernel's cycles, the cycles being SQ_BUSY_CYCLES per
+    shader engine, ``engines`` of them), the share of wave time spent waiting
+    at s_waitcnt (SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES), and the instructions per
+    critical pair (``pairs`` per launch) issued by all waves."""
+    import csv
+
+    data = {}
+    for path in (csv_a, csv_b):
+        with open(path, newline="") as f:
+            for rec in csv.DictReader(f):
+                name = rec["Kernel_Name"].replace("void ", "").split("(")[0]
+                d = data.setdefault(name, {})
+                d.setdefault(rec["Counter_Name"], []).append(float(rec["Counter_Value"]))
+                if rec["Counter_Name"] == "SQ_BUSY_CYCLES":
+                    d.setdefault("_us", []).append(
+                        (int(rec["End_Timestamp"]) - int(rec["Start_Timestamp"])) / 1000.0)
+
+    def mean(d, c):
+        v = d.get(c)
+        return sum(v) / len(v) if v else float("nan")
+
+    lines = ["| kernel | µs under counters | clock MHz | MFMA busy % | waiting at s_waitcnt % | "
+             "MFMA / VALU / LDS / VMEM / SALU instructions per critical pair |",
+             "|---|---:|---:|---:|---:|---|"]
+    for name, d in data.items():
+        if not name.startswith("sla::"):
+            continue
+        cyc = mean(d, "SQ_BUSY_CYCLES") / engines
+        us = mean(d, "_us")
+        mfma = mean(d, "SQ_VALU_MFMA_BUSY_CYCLES") / (simds * cyc)
+        wait = mean(d, "SQ_WAIT_INST_ANY") / mean(d, "SQ_WAVE_CYCLES")
+        mix = " / ".join(f"{mean(d, 'SQ_INSTS_' + k) / pairs:.0f}"
+                         for k in ("MFMA", "VALU", "LDS", "VMEM", "SALU"))
+        lines.append(f"| `{name}` | {us:.1f} | {cyc / us:.0f} | {100 * mfma:.1f} | {100 * wait:.1f} | {mix} |")
+    return "\n".join(lines)
+
+
 def main():
     args = parse()
     if args.trace_summary:
         print(trace_summary(args.trace_summary, args.warmup, args.steps))
+        return
+    if args.sq_summary:
+        print(sq_summary(*args.sq_summary, pairs=args.pairs))
         return
     if args.counter_summary:
         print(counter_summary(*args.counter_summary, workload=args.workload))

@@ -150,3 +150,23 @@ def test_sustained_clock_without_amdsmi(monkeypatch):
     monkeypatch.setitem(sys.modules, "amdsmi", None)   # import fails
     rec = b.sustained_clock(lambda: None, sync=lambda: None)
     assert rec["gfx_mhz"] is None and "error" in rec
+
+
+def test_sq_summary_normalisation(tmp_path):
+    """MFMA busy is per SIMD over the kernel's cycles (SQ_BUSY_CYCLES per
+    engine); instruction counts are per critical pair."""
+    b = _bench()
+    hdr = '"Kernel_Name","Counter_Name","Counter_Value","Start_Timestamp","End_Timestamp"'
+    k = '"void sla::bwd_kv_kernel<128>(int)"'
+    a = tmp_path / "a.csv"
+    # 2 engines busy 2000 cycles each over 1 us -> 2000 MHz; 4 SIMDs, MFMA busy 2000 of 8000
+    a.write_text("\n".join([hdr, f'{k},"SQ_BUSY_CYCLES",4000,0,1000',
+                            f'{k},"SQ_VALU_MFMA_BUSY_CYCLES",2000,0,1000',
+                            f'{k},"SQ_WAVE_CYCLES",1000,0,1000',
+                            f'{k},"SQ_WAIT_INST_ANY",250,0,1000']) + "\n")
+    bb = tmp_path / "b.csv"
+    bb.write_text("\n".join([hdr] + [f'{k},"SQ_INSTS_{c}",{v},0,1000' for c, v in
+                                     (("MFMA", 40), ("VALU", 80), ("LDS", 20), ("VMEM", 4), ("SALU", 8))]) + "\n")
+    out = b.sq_summary(str(a), str(bb), pairs=4, simds=4, engines=2)
+    row = next(ln for ln in out.splitlines() if "bwd_kv_kernel" in ln)
+    assert "| 1.0 | 2000 | 25.0 | 25.0 | 10 / 20 / 5 / 1 / 2 |" in row
