@@ -526,7 +526,7 @@ TRAFFIC_KERNELS = {
     "attn_fwd": ("attn_fwd_kernel", ["attn_fwd.hip", "sla_device.h"]),
     "bwd_kv": ("bwd_kv_kernel", ["bwd.hip", "sla_device.h"]),
 }
-COUNTER_COMMAND = ("rocprofv3 --pmc {c} --output-format csv -d gpurun_out/pmc/{t} -o {t} -- "
+COUNTER_COMMAND = ("rocprofv3 --pmc {c} --output-format csv -d OUT/{t} -o {t} -- "
                    "python3 bench.py --steps 1 --warmup 1 --no-cpu-baseline --no-side-runs "
                    "--traffic-probe")
 
