@@ -49,8 +49,8 @@ DOMINANT = {"fwd": "attention", "fwdbwd": "bwd_kv"}
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--mode", choices=("fwd", "fwdbwd"), default="fwdbwd")
     ap.add_argument("--seed", type=int, default=0)
@@ -331,9 +331,14 @@ def linear_branch_rate(wl, inp, q, k, v, w, dev):
     states = bh * t * (d * d + 2 * d) * 2        # h (d x d) and z (two bf16 parts) per block
     nbytes = 2 * tok + 2 * states + tok + tok
     gbs = nbytes / (ms * 1e-3) / 1e9
+    # the same accounting with fp32 states (h d x d, z d per block)
+    nbytes32 = 2 * tok + 2 * (bh * t * (d * d + d) * 4) + tok + tok
     return {"ms": round(ms, 4), "bytes": nbytes, "GB/s": round(gbs, 1),
             "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
-            "note": "sla_forward with frac_critical = 0 and the same frac_negligible"}
+            "bytes_fp32_states": nbytes32,
+            "GB/s_fp32_states": round(nbytes32 / (ms * 1e-3) / 1e9, 1),
+            "note": "sla_forward with frac_critical = 0 and the same frac_negligible; states "
+                    "are stored in bf16, the fp32 figure counts them as fp32"}
 
 
 def dense_ratio(wl, q, k, v, w, do, dev, with_bwd, sla_ms):
