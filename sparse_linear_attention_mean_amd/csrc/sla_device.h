@@ -81,11 +81,6 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const uint2& lo, const uint2& hi) {
   uint4 v = make_uint4(lo.x, lo.y, hi.x, hi.y);
   return as_bf16x8(v);
 }
-__device__ __forceinline__ uint4 as_uint4(const bf16x8& v) {
-  uint4 r;
-  __builtin_memcpy(&r, &v, 16);
-  return r;
-}
 
 // 16-bit element s (0..7) of a 16-byte register vector.
 __device__ __forceinline__ uint32_t u4_elem(const u32x4& v, int s) {
@@ -231,18 +226,6 @@ __device__ __forceinline__ void copy_swz_buf(__amdgpu_buffer_rsrc_t rs, int row0
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + it * 512),
                                              16, voff, 0, 0, 0);
   }
-}
-// the u-th of this wave's kCopies / NW copy instructions of copy_swz_buf
-// (callers spread them between independent work)
-template <int D, int NW>
-__device__ __forceinline__ void copy_swz_buf_one(__amdgpu_buffer_rsrc_t rs, int row0, uint16_t* dst,
-                                                 int w, int lane, int u) {
-  const int it = w + NW * u;
-  const int p = it * 64 + lane;
-  const int r = p / (D / 8), sl = p % (D / 8);
-  const int voff = ((row0 + r) * D + 8 * (sl ^ swz<D>(r))) * 2;
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + it * 512),
-                                           16, voff, 0, 0, 0);
 }
 // Buffer resource over rows [row0, L) of a row-major bf16 matrix with D
 // columns: copies through it read the padded rows at or past L as zero, and
