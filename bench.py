@@ -377,6 +377,47 @@ def dense_ratio(wl, q, k, v, w, do, dev, with_bwd, sla_ms):
                     "median step time"}
 
 
+def sdpa_ratio(wl, q, k, v, do, dev, with_bwd, sla_ms):
+    """A dense baseline from outside this library: PyTorch's fused
+    scaled-dot-product attention (flash backend, else memory-efficient; never
+    the unfused math path) on the same bf16 Q, K, V, forward and, with the
+    backward, the gradients of Q, K, V for the same output gradient.  Plain
+    softmax attention only (no linear branch, no projection)."""
+    import torch
+    import torch.nn.functional as F
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+
+    qq, kk, vv = (x.detach().clone().requires_grad_(with_bwd) for x in (q, k, v))
+    scale = wl.head_dim ** -0.5
+    err = {}
+    for name, backend in (("flash", SDPBackend.FLASH_ATTENTION),
+                          ("efficient", SDPBackend.EFFICIENT_ATTENTION)):
+        def step():
+            with sdpa_kernel([backend]):
+                out = F.scaled_dot_product_attention(qq, kk, vv, scale=scale)
+            if with_bwd:
+                qq.grad = kk.grad = vv.grad = None
+                out.backward(do)
+
+        try:
+            _, per = _timed(step, 2, 5, per_step=True)
+        except RuntimeError as e:   # backend not available for this device or shape
+            err[name] = str(e).splitlines()[0][:160]
+            continue
+        st = step_stats(per)
+        bh, n = wl.batch * wl.heads, wl.seq_len
+        flops = (4.0 + (10.0 if with_bwd else 0.0)) * bh * n * n * wl.head_dim
+        tf = flops / (st["median"] * 1e-3) / 1e12
+        return {"backend": name, "sdpa_ms_per_step": st["median"], "sdpa_step_ms": st,
+                "sla_ms_per_step": round(sla_ms, 4), "speedup": round(st["median"] / sla_ms, 2),
+                "sdpa_tflops": round(tf, 1), "sdpa_frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                "skipped_backends": err,
+                "note": "torch.nn.functional.scaled_dot_product_attention at the same shape, "
+                        "median of 5 steps after 2 warm-up steps; speedup = SDPA median / SLA "
+                        "median step time"}
+    return {"unavailable": err}
+
+
 def mask_reuse_rate(wl, q, k, v, w, dev, mask):
     """Forward with the mask of the timed run passed back in (given-mask mode:
     no pooling, scores or classification) against the computed-mask forward."""
@@ -852,6 +893,7 @@ def main():
     if not args.no_side_runs and not args.dense:
         rec["linear_branch"] = linear_branch_rate(wl, inp, q, k, v, w, dev)
         rec["vs_dense"] = dense_ratio(wl, q, k, v, w, do, dev, with_bwd, step_ms["median"])
+        rec["vs_torch_sdpa"] = sdpa_ratio(wl, q, k, v, do, dev, with_bwd, step_ms["median"])
         rec["mask_reuse"] = mask_reuse_rate(wl, q, k, v, w, dev, mask)
         rec["global_linear"] = global_linear_rate(wl, q, k, v, w, do, dev, with_bwd)
         rec["two_level_selection"] = two_level_selection(dev, hip)
