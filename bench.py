@@ -401,7 +401,7 @@ def sdpa_ratio(wl, q, k, v, do, dev, with_bwd, sla_ms):
 
         try:
             _, per = _timed(step, 2, 5, per_step=True)
-        except RuntimeError as e:   # backend not available for this device or shape
+        except Exception as e:   # backend not available for this device or shape
             err[name] = str(e).splitlines()[0][:160]
             continue
         st = step_stats(per)
